@@ -1,0 +1,159 @@
+"""ResidualAttention by its plain definition, fp64 (oracle side; test infrastructure).
+
+ForkKV study note, "2. Q1 / Q2 / Q3" (Q2) and the "Reconstruction" equation of
+"4. 作者证明": the cached projection of agent i is the shared base ``xW`` plus
+the agent's residual ``xA_i`` times ``B_i``.  For keys the base is stored after
+RoPE and the residual before it ("3. 架构 / 方法图", Figure 8), so the agent's
+key is ``RoPE(xW_k + s * xA_k B_k)`` where ``xW_k`` is the stored base key with
+its rotation undone.  Values carry no RoPE: ``V = xW_v + s * xA_v B_v``.
+Attention is ``softmax(sm_scale * q K^T) V`` over every cached key of the
+agent; query head g reads KV head ``g // (Hq / Hkv)``.
+
+The oracle builds these merged K and V explicitly -- the eager form that the
+note's reproduction check 4 compares the fused kernel against -- and applies a
+textbook softmax.  No blocking, no online softmax, no split-K.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .rope import rope_rotate, rope_unrotate
+from .storage import (base_key_rows, base_value_rows, decode_values, res_key_rows,
+                      res_value_rows)
+
+
+class Geometry:
+    def __init__(self, *, page_size, num_q_heads, num_kv_heads, head_dim, rank, dtype):
+        self.P, self.Hq, self.Hkv = page_size, num_q_heads, num_kv_heads
+        self.d, self.r, self.dtype = head_dim, rank, dtype
+        self.G = num_q_heads // num_kv_heads
+
+    @classmethod
+    def of(cls, cfg):
+        return cls(page_size=cfg.page_size, num_q_heads=cfg.num_q_heads,
+                   num_kv_heads=cfg.num_kv_heads, head_dim=cfg.head_dim, rank=cfg.rank,
+                   dtype=cfg.dtype)
+
+
+def _cached_rows(geo, bpool, rpool, btab, rtab, a, h, positions):
+    bk = base_key_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype)
+    bv = base_value_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype)
+    rk = res_key_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype)
+    rv = res_value_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype)
+    return bk, bv, rk, rv
+
+
+def merged_kv(geo, bk, bv, rk, rv, Bk_a, Bv_a, h, positions, lora_scale, theta):
+    """Merged key and value rows of one agent and KV head.
+
+    bk: stored post-RoPE base keys [L, d]; bv: base values [L, d];
+    rk, rv: rank-r residuals [L, r]; Bk_a, Bv_a: the agent's up-projections
+    [r, Hkv*d] (fp64).  Returns (K, V), each [L, d].
+    """
+    cols = slice(h * geo.d, (h + 1) * geo.d)
+    xw_k = rope_unrotate(bk, positions, theta)
+    k = rope_rotate(xw_k + lora_scale * (rk @ Bk_a[:, cols]), positions, theta)
+    v = bv + lora_scale * (rv @ Bv_a[:, cols])
+    return k, v
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_scale,
+                     sm_scale, theta, agents=None, kv_heads=None):
+    """One decode query per agent over its cached keys 0 .. seq_len-1.
+
+    q: [N, Hq, d] (post-RoPE, stored encoding).  Returns fp64 [N, Hq, d]; rows
+    not requested through ``agents`` / ``kv_heads`` are NaN.  An agent with no
+    cached keys gets a zero output.
+    """
+    N = q.shape[0]
+    qv = decode_values(q, geo.dtype)
+    Bkv = decode_values(Bk, geo.dtype)
+    Bvv = decode_values(Bv, geo.dtype)
+    out = np.full((N, geo.Hq, geo.d), np.nan)
+    for a in (range(N) if agents is None else agents):
+        L = int(seq_lens[a])
+        pos = np.arange(L, dtype=np.int64)
+        for h in (range(geo.Hkv) if kv_heads is None else kv_heads):
+            gs = range(h * geo.G, (h + 1) * geo.G)
+            if L == 0:
+                out[a, list(gs)] = 0.0
+                continue
+            bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, pos)
+            k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
+            for g in gs:
+                p = _softmax_rows(sm_scale * (k @ qv[a, g]))
+                out[a, g] = p @ v
+    return out
+
+
+def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk_new, rv_new):
+    """Pool contents after the prefill chunk rows are stored (copies; inputs untouched).
+
+    Row i of agent a goes to position ``start_pos[a] + i``: page
+    ``table[a][pos // P]``, row ``pos % P``, laid out as the pool layout says.
+    """
+    bp, rp = bpool.copy(), rpool.copy()
+    N, C = k_new.shape[0], k_new.shape[1]
+    P, d, r = geo.P, geo.d, geo.r
+    for a in range(N):
+        for i in range(C):
+            t = int(start_pos[a]) + i
+            page, row = int(btab[a][t // P]), t % P
+            for h in range(geo.Hkv):
+                bp[page, 0, h, row * d:(row + 1) * d] = k_new[a, i, h]
+                bp[page, 1, h, np.arange(d) * P + row] = v_new[a, i, h]
+            page = int(rtab[a][t // P])
+            rp[page, 0, row * r:(row + 1) * r] = rk_new[a, i]
+            rp[page, 1, np.arange(r) * P + row] = rv_new[a, i]
+    return bp, rp
+
+
+def prefill_attention(geo, bpool, rpool, btab, rtab, start_pos, q, k_new, v_new, rk_new,
+                      rv_new, Bk, Bv, lora_scale, sm_scale, theta, samples=None):
+    """Chunked prefill: the chunk rows are written first, then every query attends causally.
+
+    ``bpool``/``rpool`` are the pools *before* the write; keys at positions below
+    ``start_pos[a]`` come from them and the chunk's own keys from
+    ``k_new``/``v_new``/``rk_new``/``rv_new`` -- the same as reading the pools
+    after the write (Penelope review, 部件二: each layer writes the batch's K/V,
+    then attends).  Query i of agent a sits at position ``start_pos[a] + i`` and
+    sees keys ``0 .. start_pos[a] + i`` (self included).
+
+    Returns fp64 [N, C, Hq, d]; with ``samples`` (a list of (a, i, g)) only those
+    rows are computed and the rest are NaN.
+    """
+    N, C = q.shape[0], q.shape[1]
+    qv = decode_values(q, geo.dtype)
+    Bkv, Bvv = decode_values(Bk, geo.dtype), decode_values(Bv, geo.dtype)
+    out = np.full((N, C, geo.Hq, geo.d), np.nan)
+    want = {}
+    if samples is None:
+        for a in range(N):
+            for g in range(geo.Hq):
+                want.setdefault((a, g // geo.G), []).extend((i, g) for i in range(C))
+    else:
+        for a, i, g in samples:
+            want.setdefault((int(a), int(g) // geo.G), []).append((int(i), int(g)))
+    for (a, h), rows in sorted(want.items()):
+        start = int(start_pos[a])
+        last = start + max(i for i, _ in rows)
+        pos = np.arange(last + 1, dtype=np.int64)
+        old = pos[pos < start]
+        bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, old)
+        n_new = last + 1 - start
+        bk = np.concatenate([bk, decode_values(k_new[a, :n_new, h], geo.dtype)])
+        bv = np.concatenate([bv, decode_values(v_new[a, :n_new, h], geo.dtype)])
+        rk = np.concatenate([rk, decode_values(rk_new[a, :n_new], geo.dtype)])
+        rv = np.concatenate([rv, decode_values(rv_new[a, :n_new], geo.dtype)])
+        k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
+        for i, g in rows:
+            n_keys = start + i + 1
+            p = _softmax_rows(sm_scale * (k[:n_keys] @ qv[a, i, g]))
+            out[a, i, g] = p @ v[:n_keys]
+    return out

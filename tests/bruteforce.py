@@ -1,0 +1,114 @@
+"""Pure-Python scalar brute force of ResidualAttention (independent of ``oracle/``).
+
+Written from the ForkKV study note's definitions with plain loops and the
+``math`` module only: read the stored bytes, undo the base key's rotation,
+add the up-projected residual, rotate again, and take a softmax-weighted sum of
+base value + up-projected value residual.  Used on tiny inputs only.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _bf16(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def _val(x, dtype):
+    return float(x) if dtype == "f32" else _bf16(x)
+
+
+def _lists(a):
+    return a.tolist() if hasattr(a, "tolist") else a
+
+
+def _key_value(P, d, r, dtype, bpool, rpool, btab_a, rtab_a, Bk_a, Bv_a, h, t, s, theta,
+               row_override=None):
+    """Merged key and value of one agent/head at position t (lists of d floats)."""
+    if row_override is not None:
+        bk, bv, rk, rv = row_override
+    else:
+        lp, row = divmod(t, P)
+        bp, rp = btab_a[lp], rtab_a[lp]
+        bk = [_val(bpool[bp][0][h][row * d + j], dtype) for j in range(d)]
+        bv = [_val(bpool[bp][1][h][j * P + row], dtype) for j in range(d)]
+        rk = [_val(rpool[rp][0][row * r + k], dtype) for k in range(r)]
+        rv = [_val(rpool[rp][1][k * P + row], dtype) for k in range(r)]
+    half = d // 2
+    key = [0.0] * d
+    for j in range(half):
+        w = theta ** (-(2.0 * j) / d)
+        c, sn = math.cos(t * w), math.sin(t * w)
+        # pre-RoPE base: rotate back by -t*w
+        x1 = bk[j] * c + bk[j + half] * sn
+        x2 = bk[j + half] * c - bk[j] * sn
+        u1 = s * sum(rk[k] * _val(Bk_a[k][h * d + j], dtype) for k in range(r))
+        u2 = s * sum(rk[k] * _val(Bk_a[k][h * d + j + half], dtype) for k in range(r))
+        y1, y2 = x1 + u1, x2 + u2
+        key[j] = y1 * c - y2 * sn
+        key[j + half] = y2 * c + y1 * sn
+    val = [bv[j] + s * sum(rv[k] * _val(Bv_a[k][h * d + j], dtype) for k in range(r))
+           for j in range(d)]
+    return key, val
+
+
+def _attend(qrow, kv, sm_scale, d):
+    if not kv:
+        return [0.0] * d
+    scores = [sm_scale * sum(qrow[j] * k[j] for j in range(d)) for k, _ in kv]
+    m = max(scores)
+    e = [math.exp(x - m) for x in scores]
+    z = math.fsum(e)
+    return [math.fsum(e[t] * kv[t][1][j] for t in range(len(kv))) / z for j in range(d)]
+
+
+def brute_decode(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv,
+                 s, sm_scale, theta):
+    bpool, rpool, btab, rtab = map(_lists, (bpool, rpool, btab, rtab))
+    q, Bk, Bv = map(_lists, (q, Bk, Bv))
+    G = Hq // Hkv
+    out = []
+    for a in range(len(q)):
+        rows = []
+        for g in range(Hq):
+            h = g // G
+            kv = [_key_value(P, d, r, dtype, bpool, rpool, btab[a], rtab[a], Bk[a], Bv[a], h, t,
+                             s, theta) for t in range(int(seq_lens[a]))]
+            qrow = [_val(x, dtype) for x in q[a][g]]
+            rows.append(_attend(qrow, kv, sm_scale, d))
+        out.append(rows)
+    return out
+
+
+def brute_prefill(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, start_pos, q, k_new,
+                  v_new, rk_new, rv_new, Bk, Bv, s, sm_scale, theta):
+    """Chunk rows are written at start_pos[a] + i, then query i attends to keys 0..start+i."""
+    bpool, rpool, btab, rtab = map(_lists, (bpool, rpool, btab, rtab))
+    q, k_new, v_new, rk_new, rv_new, Bk, Bv = map(_lists, (q, k_new, v_new, rk_new, rv_new, Bk, Bv))
+    G = Hq // Hkv
+    out = []
+    for a in range(len(q)):
+        start = int(start_pos[a])
+        C = len(q[a])
+        per_q = []
+        for i in range(C):
+            rows = []
+            for g in range(Hq):
+                h = g // G
+                kv = []
+                for t in range(start + i + 1):
+                    ov = None
+                    if t >= start:
+                        j = t - start
+                        ov = ([_val(x, dtype) for x in k_new[a][j][h]],
+                              [_val(x, dtype) for x in v_new[a][j][h]],
+                              [_val(x, dtype) for x in rk_new[a][j]],
+                              [_val(x, dtype) for x in rv_new[a][j]])
+                    kv.append(_key_value(P, d, r, dtype, bpool, rpool, btab[a], rtab[a], Bk[a],
+                                         Bv[a], h, t, s, theta, row_override=ov))
+                qrow = [_val(x, dtype) for x in q[a][i][g]]
+                rows.append(_attend(qrow, kv, sm_scale, d))
+            per_q.append(rows)
+        out.append(per_q)
+    return out

@@ -1,0 +1,53 @@
+"""Small seeded cases with ragged lengths, unaligned forks and partial pages."""
+from __future__ import annotations
+
+import numpy as np
+
+from workloads import bf16_bits_from_f32
+
+
+def encode(x, dtype):
+    x = np.asarray(x, dtype=np.float32)
+    return x.copy() if dtype == "f32" else bf16_bits_from_f32(x)
+
+
+def random_ops(rng, n_agents, P=16, max_prefix=40, max_suffix=24):
+    """Root with a ragged prefix; agents fork at (often unaligned) points and append."""
+    L0 = int(rng.integers(1, max_prefix + 1))
+    ops = [("create", "root", 0), ("append", "root", L0)]
+    agents = []
+    for j in range(n_agents):
+        alias = int(rng.integers(0, L0 + 1))
+        ops.append(("fork", "root", alias, f"a{j}"))
+        agents.append(f"a{j}")
+    for a in agents:
+        n = int(rng.integers(1, max_suffix + 1))
+        ops.append(("append", a, n))
+    return ops, agents
+
+
+def tiny_case(seed, dtype="f32", Hq=4, Hkv=2, d=8, r=3, n_agents=3, P=16, max_prefix=40,
+              max_suffix=24, b_std=0.3, num_pages=64, chunk=0):
+    rng = np.random.default_rng(seed)
+    ops, agents = random_ops(rng, n_agents, P, max_prefix, max_suffix)
+    perm_b = rng.permutation(num_pages).astype(np.int32)
+    perm_r = rng.permutation(num_pages).astype(np.int32)
+    case = dict(
+        P=P, Hq=Hq, Hkv=Hkv, d=d, r=r, dtype=dtype, ops=ops, agents=agents,
+        perm_b=perm_b, perm_r=perm_r, num_bpages=num_pages, num_rpages=num_pages,
+        bpool=encode(rng.standard_normal((num_pages, 2, Hkv, P * d)), dtype),
+        rpool=encode(rng.standard_normal((num_pages, 2, P * r)), dtype),
+        Bk=encode(b_std * rng.standard_normal((n_agents, r, Hkv * d)), dtype),
+        Bv=encode(b_std * rng.standard_normal((n_agents, r, Hkv * d)), dtype),
+        lora_scale=float(rng.choice([0.5, 1.0, 2.0])), theta=float(rng.choice([1e4, 5e5])),
+    )
+    case["sm_scale"] = 1.0 / np.sqrt(d)
+    if chunk:
+        case["q"] = encode(rng.standard_normal((n_agents, chunk, Hq, d)), dtype)
+        case["k_new"] = encode(rng.standard_normal((n_agents, chunk, Hkv, d)), dtype)
+        case["v_new"] = encode(rng.standard_normal((n_agents, chunk, Hkv, d)), dtype)
+        case["rk_new"] = encode(rng.standard_normal((n_agents, chunk, r)), dtype)
+        case["rv_new"] = encode(rng.standard_normal((n_agents, chunk, r)), dtype)
+    else:
+        case["q"] = encode(rng.standard_normal((n_agents, Hq, d)), dtype)
+    return case
