@@ -1,0 +1,232 @@
+"""Benchmark: ResidualAttention decode on one MI355X.
+
+Workload: Llama3-8B attention shape (32 q heads, 8 KV heads, d=128, LoRA rank 16, bf16),
+8 agents sharing a 32768-token prefix with 1024 private tokens each (MapReduce fan-out),
+one decode query per agent.  A step is one decode call (split-K kernel + LSE/B_v
+combine) over the whole batch; inputs are resident in HBM.  Input copies are rotated
+so the step streams from HBM rather than the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_pmc_llama3_8b_mapreduce.json")
+KERNEL_SOURCES = {
+    "generic": "lora_shared_prefix_amd/csrc/kernels_generic.hip",
+    "mfma": "lora_shared_prefix_amd/csrc/kernels_mfma.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, n_unique_tokens):
+    """Unique base-cache bytes once + per-agent residual, q, o and B bytes."""
+    e = cfg.elem_bytes
+    n = cfg.kv_width
+    N = cfg.n_agents
+    base = n_unique_tokens * n * 2 * e
+    res = N * cfg.seq_len * 2 * cfg.rank * e
+    q = N * cfg.num_q_heads * cfg.head_dim * e
+    bk = N * cfg.rank * n * e
+    split = base + res + q + bk          # what the split kernel must read
+    step = split + q + bk                # + o written and B_v read by the combine
+    return split, step
+
+
+def source_sha(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, ops, agents, n_sample):
+    """The fp64 oracle, as it is, on a sample of the agents (all heads)."""
+    import numpy as np
+    from oracle import PoolModel
+    from oracle.attention import Geometry, decode_attention
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    pm = PoolModel(cfg.num_bpages, cfg.num_rpages, 16, x["perm_b"], x["perm_r"])
+    names = pm.replay(ops)
+    bt, rt, lens = pm.tables([names[a] for a in agents], -(-cfg.seq_len // 16))
+    sample = list(range(n_sample))
+    t0 = time.perf_counter()
+    decode_attention(Geometry.of(cfg), x["bpool"], x["rpool"], np.array(bt), np.array(rt), lens,
+                     x["q"], x["Bk"], x["Bv"], cfg.lora_scale, 1 / np.sqrt(cfg.head_dim),
+                     cfg.rope_theta, agents=sample)
+    dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "agent-tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{n_sample} of {cfg.n_agents} agents, all {cfg.num_q_heads} q heads, "
+                      f"fp64 numpy, {dt:.1f} s; host cpus={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="index of the decode workload")
+    ap.add_argument("--kernel", choices=["auto", "generic", "mfma"], default="auto")
+    ap.add_argument("--pages-per-item", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--cpu-sample", type=int, default=2, help="agents timed on the oracle (0 = skip)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="only run a plain device copy of this many MiB (PMC scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lora_shared_prefix_amd import forkkv as fk
+    from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
+    from workloads import CONFIGS, draw_inputs, pool_ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 2 ** 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} bytes read and written per copy, 3 copies")
+        return
+
+    cfg = CONFIGS[args.workload]
+    assert cfg.kind == "decode"
+    kernel = {"auto": fk.KERNEL_AUTO, "generic": fk.KERNEL_GENERIC, "mfma": fk.KERNEL_MFMA}[args.kernel]
+    log(f"drawing inputs of {cfg.name}")
+    x = draw_inputs(cfg)
+    ops, agents = pool_ops(cfg)
+    geom = workload_geom(cfg)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    unique = cfg.sessions * cfg.prefix_len + cfg.n_agents * cfg.suffix_len
+    split_bytes, step_bytes = algorithmic_bytes(cfg, unique)
+    ws_mb = step_bytes / 1e6
+    copies = args.copies or max(1, int(np.ceil(3 * 256e6 / (split_bytes))))
+    log(f"uploading {copies} input copies (working set {ws_mb:.1f} MB each)")
+    first = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel,
+                        pages_per_item=args.pages_per_item)
+    batches = [first]
+    for _ in range(copies - 1):
+        arrays = {}
+        b = DeviceBatch.__new__(DeviceBatch)
+        b.__dict__.update(first.__dict__)
+        b.bcache = first.bcache.clone()
+        b.rcache = first.rcache.clone()
+        b.q, b.Bk, b.Bv = first.q.clone(), first.Bk.clone(), first.Bv.clone()
+        b.out = torch.empty_like(first.out)
+        b.pool = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim,
+                         cfg.rank, cfg.dtype, x["perm_b"], x["perm_r"], b.bcache, b.rcache)
+        b.pool.replay(ops)
+        batches.append(b)
+    plan = first.plan
+    kname = "mfma" if plan.info["kernel"] == fk.KERNEL_MFMA else "generic"
+    log(f"plan: kernel={kname} items={plan.info['n_items']} slots={plan.info['n_slots']} "
+        f"workspace={plan.info['workspace_bytes'] / 1e6:.1f} MB")
+
+    def step(i):
+        b = batches[i % copies]
+        fk.residual_attn_decode(b.pool, plan, b.q, b.Bk, b.Bv, first.btab, first.rtab, b.out,
+                                first.workspace, cfg.lora_scale, sm, cfg.rope_theta)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan.timing()  # drop anything recorded so far
+    plan.set_timing(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    total_ms = t0.elapsed_time(t1)
+    split_ms, comb_ms, launches = plan.timing()
+    ms_step = total_ms / args.steps
+    split_avg = split_ms / max(launches, 1)
+    comb_avg = comb_ms / max(launches, 1)
+    log(f"step {ms_step * 1e3:.1f} us; split {split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us")
+
+    # warm (cache-resident) figure for context: the same copy every step
+    plan.set_timing(True)
+    for _ in range(args.steps):
+        fk.residual_attn_decode(first.pool, plan, first.q, first.Bk, first.Bv, first.btab,
+                                first.rtab, first.out, first.workspace, cfg.lora_scale, sm,
+                                cfg.rope_theta)
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    wsplit, _, wl = plan.timing()
+
+    achieved = split_bytes / (split_avg * 1e-3) / 1e9
+    traffic = load_traffic(kname)
+    result = {
+        "metric": "ResidualAttention decode agent-tokens/s + achieved HBM GB/s (% roofline), 1 GPU",
+        "value": cfg.n_agents / (ms_step * 1e-3),
+        "unit": "agent-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) caches and queries, B ~ N(0, 0.02^2))",
+        "config": {"workload": cfg.name, "agents": cfg.n_agents, "shared_prefix": cfg.prefix_len,
+                   "private_suffix": cfg.suffix_len, "q_heads": cfg.num_q_heads,
+                   "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "rank": cfg.rank,
+                   "page_size": 16, "kernel": kname, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": f"residual_attn_{kname} (split-K decode)",
+                     "algorithmic_bytes_per_launch": split_bytes,
+                     "avg_launch_us": split_avg * 1e3},
+        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "combine_avg_us": comb_avg * 1e3,
+        "warm_split_avg_us": wsplit / max(wl, 1) * 1e3,
+    }
+    if args.cpu_sample > 0:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(cfg, x, ops, agents, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,261 @@
+/*
+ * forkkv.h -- C ABI of the ResidualAttention library for AMD MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Many LoRA agents that share a long prefix share ONE base KV cache ("bCache":
+ * the base projections xW_k after RoPE and xW_v), aliased page by page through
+ * copy-on-write forks, and each agent keeps a private rank-r residual cache
+ * ("rCache": xA_k and xA_v, no RoPE).  For agent a with up-projections B_k,a and
+ * B_v,a (ForkKV study note, "2. Q1 / Q2 / Q3" Q2; "4. 作者证明", the
+ * "Reconstruction" and "Attention fusion" equations):
+ *
+ *   K_a[t] = bK[t] + RoPE_t( s * rK_a[t] * B_k,a )          (deferred RoPE)
+ *   V_a[t] = bV[t] + s * rV_a[t] * B_v,a
+ *   o      = softmax(sm_scale * q K_a^T) V_a
+ *          = [ sum_t p_t bV[t] + s * (sum_t p_t rV_a[t]) B_v,a ] / sum_t p_t
+ *
+ * The second form (associativity, the note's Eq.(4)) is what the kernels use:
+ * B_v is applied once, after the online softmax.  RoPE is the rotate-half form
+ * (dimension j paired with j + d/2, angle t * theta^(-2j/d)); query head g
+ * reads KV head g / (Hq/Hkv).
+ *
+ * Storage (caller-owned device memory; the pages leave the layout open)
+ * -----------------------------------------------------------------------
+ *   bcache: [num_bpages][2][Hkv][P*d] elements.  Plane 0 = key tile, row-major
+ *           [row][dim] (post-RoPE).  Plane 1 = value tile, transposed [dim][row].
+ *   rcache: [num_rpages][2][P*r] elements.  Plane 0 = key residual [row][k];
+ *           plane 1 = value residual, transposed [k][row].
+ *   Element type: FORKKV_DTYPE_BF16 (bfloat16) or FORKKV_DTYPE_F32.  P = 16.
+ *   A slot is page * P + row; position t of a sequence lives in page
+ *   table[t / P], row t % P.
+ *
+ * Fork bookkeeping (host side, bit-exact deterministic)
+ * -----------------------------------------------------
+ * ForkKV note "3. 架构 / 方法图" (Figure 6): a forked agent maps the parent's
+ * read-only base pages (Step 1) and gets its own residual pages (Step 2).
+ * ForkServe README "Design vs APC" / "Methods": fork aliases the parent's frames
+ * in O(pages); a write allocates private pages only; an unaligned trunk tail is
+ * packed into a private page by copying its n_valid rows; "Status": a freed
+ * parent does not drop the trunk (every base page is reference counted).
+ * Free lists are FIFO queues seeded with the pool's page order; allocation takes
+ * from the head, release appends to the tail (base pages, then residual pages,
+ * each in table order).  Sequence handles are 0, 1, 2, ... and never reused.
+ * Every call is all-or-nothing: on an error nothing changes.
+ *
+ * Conventions
+ * -----------
+ * All functions return FORKKV_OK (0) or a negative error code; no exception
+ * crosses the ABI.  "host" pointers are CPU memory, "device" pointers are HIP
+ * device memory.  Arguments are validated before any launch; launches are
+ * asynchronous on the given stream and the caller keeps every buffer alive until
+ * the stream has finished.  A pool or plan handle must not be used from two
+ * threads at once.
+ */
+#ifndef FORKKV_H
+#define FORKKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FORKKV_OK = 0,
+  FORKKV_EINVAL = -1,      /* bad argument or handle */
+  FORKKV_ENOMEM = -2,      /* page pool exhausted (state unchanged) */
+  FORKKV_EHIP = -3,        /* a HIP call or kernel launch failed */
+  FORKKV_ESTATE = -4,      /* call not valid in the current state (e.g. plan not uploaded) */
+  FORKKV_EUNSUPPORTED = -5 /* shape or dtype outside what the kernels implement */
+};
+
+enum { FORKKV_DTYPE_F32 = 0, FORKKV_DTYPE_BF16 = 1 };
+
+/* Decode kernel selection (forkkv_plan_opts.kernel). */
+enum { FORKKV_KERNEL_AUTO = 0, FORKKV_KERNEL_GENERIC = 1, FORKKV_KERNEL_MFMA = 2 };
+
+typedef struct forkkv_pool forkkv_pool;
+typedef struct forkkv_plan forkkv_plan;
+typedef int32_t forkkv_seq;
+
+typedef struct {
+  int32_t num_bpages;   /* pages in the base pool */
+  int32_t num_rpages;   /* pages in the residual pool */
+  int32_t page_size;    /* P; must be 16 */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d; even, 2..256 */
+  int32_t rank;         /* r; 1..64 */
+  int32_t dtype;        /* FORKKV_DTYPE_* */
+  const int32_t* bpage_order; /* host, nullable: initial base free-list order, a permutation */
+  const int32_t* rpage_order; /* host, nullable: initial residual free-list order */
+} forkkv_pool_desc;
+
+/* A copy of the first n_rows rows of base page src into base page dst (all KV heads, K and V). */
+typedef struct {
+  int32_t src_bpage;
+  int32_t dst_bpage;
+  int32_t n_rows; /* 0 = no copy needed */
+} forkkv_cow_op;
+
+typedef struct {
+  int32_t live_bpages, live_rpages;
+  int32_t free_bpages, free_rpages;
+  int32_t shared_bpages;           /* base pages with reference count > 1 */
+  int64_t bpage_refs, rpage_refs;  /* sums of reference counts */
+  int64_t live_bytes_b, live_bytes_r;
+} forkkv_stats;
+
+/* Human-readable text of an error code (static storage). */
+const char* forkkv_strerror(int code);
+
+/* Bytes the caller must allocate for the two device pools of a descriptor. */
+int forkkv_pool_bytes(const forkkv_pool_desc* desc, size_t* bcache_bytes, size_t* rcache_bytes);
+
+/* Create the host bookkeeping of a pool.  bcache / rcache (device, nullable) are the
+ * caller's pool buffers; with NULL the pool does bookkeeping only and device calls on
+ * it return FORKKV_ESTATE.  The handle owns host metadata only. */
+int forkkv_pool_create(const forkkv_pool_desc* desc, void* bcache, void* rcache,
+                       forkkv_pool** out);
+int forkkv_pool_destroy(forkkv_pool* pool);
+
+/* New empty sequence; with_residual = 0 makes a base-only snapshot (no rCache pages). */
+int forkkv_seq_create(forkkv_pool* pool, int32_t with_residual, forkkv_seq* out);
+
+/* Reserve n rows at the end of seq.  bslots / rslots (host, nullable, n entries) receive
+ * the slot of each new row (rslots = -1 for a base-only sequence).  cow (host, nullable)
+ * receives the copy-on-write row copy the append needed (n_rows = 0 if none); the caller
+ * runs it with forkkv_cow_copy before writing the new rows. */
+int forkkv_seq_append(forkkv_pool* pool, forkkv_seq seq, int32_t n, int32_t* bslots,
+                      int32_t* rslots, forkkv_cow_op* cow);
+
+/* Fork a new agent sharing the parent's first alias_len rows (0 <= alias_len <= len).
+ * Full base pages are aliased (reference count + 1); a partial tail is packed into a
+ * private page (cow receives the row copy).  The child gets fresh residual pages for
+ * [0, alias_len), which the caller fills. */
+int forkkv_fork(forkkv_pool* pool, forkkv_seq parent, int32_t alias_len, forkkv_seq* child,
+                forkkv_cow_op* cow);
+
+/* Release a sequence: each page's reference count drops; pages reaching 0 return to the
+ * tail of their free list. */
+int forkkv_seq_free(forkkv_pool* pool, forkkv_seq seq);
+int forkkv_seq_len(const forkkv_pool* pool, forkkv_seq seq, int32_t* len);
+
+/* Block tables of n sequences (host outputs): btab, rtab [n][max_pages] page ids padded
+ * with -1 (rtab all -1 for base-only sequences); seq_lens [n] (nullable). */
+int forkkv_export_tables(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
+                         int32_t max_pages, int32_t* btab, int32_t* rtab, int32_t* seq_lens);
+
+int forkkv_pool_stats(const forkkv_pool* pool, forkkv_stats* out);
+
+/* Free-list contents in queue order (which = 0 base, 1 residual); host out[cap]; *n = size. */
+int forkkv_free_list(const forkkv_pool* pool, int32_t which, int32_t* out, int32_t cap,
+                     int32_t* n);
+
+/* Reference counts of every page (which = 0 base, 1 residual); host out[num pages]. */
+int forkkv_refcounts(const forkkv_pool* pool, int32_t which, int32_t* out);
+
+/* Run copy-on-write row copies on the device pool (ForkServe README "Status": n_valid
+ * rows, not P).  Needs the pool's device buffers. */
+int forkkv_cow_copy(forkkv_pool* pool, const forkkv_cow_op* ops, int32_t n_ops,
+                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode plan.  Groups (logical page, physical base page) entries that several agents
+ * alias into work items, so that each shared base page is read once for all its
+ * agents, and cuts long runs into split-K items whose partial softmax states are
+ * merged afterwards.  Integer only, deterministic; built on the host from the pool's
+ * tables and lengths, which it captures.
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t kernel;             /* FORKKV_KERNEL_*; 0 = auto */
+  int32_t max_agents_per_item;/* 0 = the kernel's maximum */
+  int32_t pages_per_item;     /* split-K length in pages; 0 = auto */
+} forkkv_plan_opts;
+
+typedef struct {
+  int32_t n_agents, n_items, n_slots, kernel, item_ints, num_q_heads;
+  size_t plan_bytes;      /* device bytes forkkv_plan_upload needs */
+  size_t workspace_bytes; /* device workspace forkkv_residual_attn_decode needs */
+} forkkv_plan_info;
+
+/* Build the decode plan of the n sequences seqs (agent a = seqs[a]) for num_q_heads
+ * query heads.  opts is nullable. */
+int forkkv_plan_decode(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
+                       int32_t num_q_heads, const forkkv_plan_opts* opts, forkkv_plan** out);
+int forkkv_plan_get_info(const forkkv_plan* plan, forkkv_plan_info* out);
+/* Copy the plan's integer blob (plan_bytes / 4 int32) to host memory, for inspection. */
+int forkkv_plan_export(const forkkv_plan* plan, int32_t* host_blob);
+/* Copy the plan blob to a caller-owned device buffer of plan_bytes (async on stream);
+ * the plan remembers the buffer. */
+int forkkv_plan_upload(forkkv_plan* plan, void* dev_buf, hipStream_t stream);
+int forkkv_plan_destroy(forkkv_plan* plan);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each launch
+ * of the plan's split kernel and combine kernel (enable = 1).  forkkv_plan_timing
+ * waits for the recorded events and returns the summed milliseconds and the number
+ * of timed launches, then clears the sums. */
+int forkkv_plan_set_timing(forkkv_plan* plan, int32_t enable);
+int forkkv_plan_timing(forkkv_plan* plan, double* split_ms, double* combine_ms,
+                       int32_t* launches);
+
+/* ---------------------------------------------------------------------------------
+ * Decode: one query per agent over its cached keys 0 .. len-1 (len captured by the
+ * plan).  ForkKV note "7. 实现 cross-reference" (kernel; core barriers (1) deferred
+ * RoPE and (2) B_v lifted out of the loop with a rescaled residual accumulator).
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  const forkkv_pool* pool;  /* geometry, dtype and device pools */
+  const forkkv_plan* plan;  /* built for this batch and uploaded */
+  const void* q;            /* device [N][Hq][d], post-RoPE, pool dtype */
+  const void* Bk;           /* device [N][r][Hkv*d], pool dtype */
+  const void* Bv;           /* device [N][r][Hkv*d], pool dtype */
+  const int32_t* btab;      /* device [N][max_pages], as exported from the pool */
+  const int32_t* rtab;      /* device [N][max_pages] */
+  int32_t max_pages;        /* row stride of btab / rtab */
+  float lora_scale;         /* s */
+  float sm_scale;           /* softmax scale, e.g. 1/sqrt(d) */
+  float rope_theta;         /* theta */
+  void* out;                /* device [N][Hq][d], pool dtype; an agent with len 0 gets 0 */
+  void* workspace;          /* device, workspace_bytes of the plan */
+  size_t workspace_bytes;
+} forkkv_decode_args;
+
+int forkkv_residual_attn_decode(const forkkv_decode_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Chunked prefill: agent a appends C rows at positions start_pos[a] .. start_pos[a]+C-1
+ * (the caller has already reserved them with forkkv_seq_append and uploaded the tables).
+ * The kernel first stores the chunk rows into the pools, then every chunk query
+ * attends causally to keys 0 .. its own position (Penelope review, 部件二: each layer
+ * writes the batch's K/V first, then attends).
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  const forkkv_pool* pool;
+  int32_t n_agents;         /* N */
+  int32_t chunk_len;        /* C >= 1 */
+  int32_t num_q_heads;      /* Hq, a multiple of Hkv */
+  const void* q;            /* device [N][C][Hq][d], post-RoPE */
+  const void* k_new;        /* device [N][C][Hkv][d], post-RoPE base keys of the chunk */
+  const void* v_new;        /* device [N][C][Hkv][d] */
+  const void* rk_new;       /* device [N][C][r] */
+  const void* rv_new;       /* device [N][C][r] */
+  const void* Bk;           /* device [N][r][Hkv*d] */
+  const void* Bv;           /* device [N][r][Hkv*d] */
+  const int32_t* btab;      /* device [N][max_pages], covering start_pos + C */
+  const int32_t* rtab;      /* device [N][max_pages] */
+  int32_t max_pages;
+  const int32_t* start_pos;      /* device [N] */
+  const int32_t* start_pos_host; /* host [N], same values (validation and launch shape) */
+  float lora_scale, sm_scale, rope_theta;
+  void* out;                /* device [N][C][Hq][d] */
+} forkkv_prefill_args;
+
+int forkkv_residual_attn_prefill(const forkkv_prefill_args* args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FORKKV_H */

@@ -1,0 +1,207 @@
+// C-ABI entry points of the attention calls: argument validation, launch, timing.
+#include <cmath>
+
+#include "forkkv_internal.h"
+
+using forkkv::kPage;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool same_geometry(const forkkv_pool_desc& a, const forkkv_pool_desc& b) {
+  return a.num_bpages == b.num_bpages && a.num_rpages == b.num_rpages &&
+         a.num_kv_heads == b.num_kv_heads && a.head_dim == b.head_dim && a.rank == b.rank &&
+         a.dtype == b.dtype && a.page_size == b.page_size;
+}
+
+hipEvent_t get_event(forkkv_plan* pl) {
+  if (!pl->spare.empty()) {
+    hipEvent_t e = pl->spare.back();
+    pl->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+}  // namespace
+
+extern "C" {
+
+int forkkv_plan_set_timing(forkkv_plan* pl, int32_t enable) {
+  if (!pl) return FORKKV_EINVAL;
+  pl->timing = enable != 0;
+  return FORKKV_OK;
+}
+
+int forkkv_plan_timing(forkkv_plan* pl, double* split_ms, double* combine_ms, int32_t* launches) {
+  if (!pl) return FORKKV_EINVAL;
+  double sms = 0.0, cms = 0.0;
+  int32_t count = 0;
+  int rc = FORKKV_OK;
+  for (auto& t : pl->pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.e) != hipSuccess || hipEventElapsedTime(&ms, t.b, t.e) != hipSuccess)
+      rc = FORKKV_EHIP;
+    if (t.kind == 0) {
+      sms += ms;
+      ++count;
+    } else {
+      cms += ms;
+    }
+    pl->spare.push_back(t.b);
+    pl->spare.push_back(t.e);
+  }
+  pl->pending.clear();
+  if (split_ms) *split_ms = sms;
+  if (combine_ms) *combine_ms = cms;
+  if (launches) *launches = count;
+  return rc;
+}
+
+int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream) {
+  if (!a || !a->pool || !a->plan) return FORKKV_EINVAL;
+  const forkkv_pool* pool = a->pool;
+  forkkv_plan* pl = const_cast<forkkv_plan*>(a->plan);
+  if (!same_geometry(pool->desc, pl->geo)) return FORKKV_EINVAL;
+  if (!pool->bcache) return FORKKV_ESTATE;
+  if (pl->n_agents == 0) return FORKKV_OK;
+  if (!pl->dev) return FORKKV_ESTATE;
+  if (!a->q || !a->Bk || !a->Bv || !a->btab || !a->rtab || !a->out) return FORKKV_EINVAL;
+  if (a->max_pages < pl->max_pages_needed) return FORKKV_EINVAL;
+  if (pl->n_slots > 0 && (!a->workspace || a->workspace_bytes < pl->workspace_bytes))
+    return FORKKV_EINVAL;
+  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->rope_theta > 0.f) ||
+      !finite(a->rope_theta))
+    return FORKKV_EINVAL;
+
+  const forkkv_pool_desc& g = pool->desc;
+  forkkv::DecodeParams p{};
+  p.q = a->q;
+  p.Bk = a->Bk;
+  p.Bv = a->Bv;
+  p.bcache = pool->bcache;
+  p.rcache = pool->rcache;
+  p.btab = a->btab;
+  p.rtab = a->rtab;
+  p.plan = static_cast<const int32_t*>(pl->dev);
+  char* ws = static_cast<char*>(a->workspace);
+  p.ws_ml = reinterpret_cast<float*>(ws);
+  p.ws_acc = reinterpret_cast<float*>(ws + pl->ws_off_acc);
+  p.ws_accr = reinterpret_cast<float*>(ws + pl->ws_off_accr);
+  p.out = a->out;
+  p.n_agents = pl->n_agents;
+  p.n_items = pl->n_items;
+  p.num_q_heads = pl->num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.head_dim = g.head_dim;
+  p.rank = g.rank;
+  p.group = pl->num_q_heads / g.num_kv_heads;
+  p.max_pages = a->max_pages;
+  p.num_bpages = g.num_bpages;
+  p.num_rpages = g.num_rpages;
+  p.off_items = pl->blob[forkkv::kHdrOffItems];
+  p.off_lens = pl->blob[forkkv::kHdrOffLens];
+  p.off_slot_ptr = pl->blob[forkkv::kHdrOffSlotPtr];
+  p.off_slot_list = pl->blob[forkkv::kHdrOffSlotList];
+  p.lora_scale = a->lora_scale;
+  p.sm_scale_log2 = a->sm_scale * kLog2e;
+  p.rope_theta = a->rope_theta;
+
+  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (pl->timing) {
+    for (auto& e : ev) {
+      e = get_event(pl);
+      if (!e) return FORKKV_EHIP;
+    }
+  }
+  if (pl->n_items > 0) {
+    if (ev[0] && hipEventRecord(ev[0], stream) != hipSuccess) return FORKKV_EHIP;
+    hipError_t err = pl->kernel == FORKKV_KERNEL_MFMA
+                         ? forkkv::launch_decode_mfma(p, stream)
+                         : forkkv::launch_decode_generic(p, g.dtype, pl->group, stream);
+    if (err != hipSuccess) return FORKKV_EHIP;
+    if (ev[1] && hipEventRecord(ev[1], stream) != hipSuccess) return FORKKV_EHIP;
+  }
+  if (ev[2] && hipEventRecord(ev[2], stream) != hipSuccess) return FORKKV_EHIP;
+  if (forkkv::launch_combine(p, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  if (ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return FORKKV_EHIP;
+  if (pl->timing) {
+    if (pl->n_items > 0) {
+      pl->pending.push_back({0, ev[0], ev[1]});
+    } else {
+      pl->spare.push_back(ev[0]);
+      pl->spare.push_back(ev[1]);
+    }
+    pl->pending.push_back({1, ev[2], ev[3]});
+  }
+  if (hipGetLastError() != hipSuccess) return FORKKV_EHIP;
+  return FORKKV_OK;
+}
+
+int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t stream) {
+  if (!a || !a->pool) return FORKKV_EINVAL;
+  const forkkv_pool* pool = a->pool;
+  const forkkv_pool_desc& g = pool->desc;
+  if (!pool->bcache) return FORKKV_ESTATE;
+  if (a->n_agents < 0 || a->chunk_len < 1) return FORKKV_EINVAL;
+  if (a->num_q_heads < g.num_kv_heads || a->num_q_heads % g.num_kv_heads) return FORKKV_EINVAL;
+  if (a->n_agents == 0) return FORKKV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->rk_new || !a->rv_new || !a->Bk || !a->Bv ||
+      !a->btab || !a->rtab || !a->start_pos || !a->start_pos_host || !a->out)
+    return FORKKV_EINVAL;
+  if (a->max_pages < 1) return FORKKV_EINVAL;
+  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->rope_theta > 0.f) ||
+      !finite(a->rope_theta))
+    return FORKKV_EINVAL;
+  for (int32_t i = 0; i < a->n_agents; ++i) {
+    const int64_t s = a->start_pos_host[i];
+    if (s < 0 || s + a->chunk_len > int64_t(a->max_pages) * kPage) return FORKKV_EINVAL;
+  }
+  forkkv::PrefillParams p{};
+  p.q = a->q;
+  p.k_new = a->k_new;
+  p.v_new = a->v_new;
+  p.rk_new = a->rk_new;
+  p.rv_new = a->rv_new;
+  p.Bk = a->Bk;
+  p.Bv = a->Bv;
+  p.bcache = pool->bcache;
+  p.rcache = pool->rcache;
+  p.btab = a->btab;
+  p.rtab = a->rtab;
+  p.start_pos = a->start_pos;
+  p.out = a->out;
+  p.n_agents = a->n_agents;
+  p.chunk_len = a->chunk_len;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = g.num_kv_heads;
+  p.head_dim = g.head_dim;
+  p.rank = g.rank;
+  p.group = a->num_q_heads / g.num_kv_heads;
+  p.max_pages = a->max_pages;
+  p.num_bpages = g.num_bpages;
+  p.num_rpages = g.num_rpages;
+  p.lora_scale = a->lora_scale;
+  p.sm_scale_log2 = a->sm_scale * kLog2e;
+  p.rope_theta = a->rope_theta;
+  if (p.group > forkkv::kGenericMaxRows || forkkv::generic_max_agents(p.group, p.head_dim, p.rank) < 1)
+    return FORKKV_EUNSUPPORTED;
+
+  (void)hipGetLastError();
+  if (forkkv::launch_prefill_write(p, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  const bool mfma = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, p.group) &&
+                    forkkv::prefill_mfma_enabled();
+  hipError_t err = mfma ? forkkv::launch_prefill_mfma(p, a->start_pos_host, stream)
+                        : forkkv::launch_prefill_generic(p, g.dtype, stream);
+  if (err != hipSuccess) return FORKKV_EHIP;
+  if (hipGetLastError() != hipSuccess) return FORKKV_EHIP;
+  return FORKKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <deque>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "forkkv.h"
+
+namespace forkkv {
+
+constexpr int kPage = 16;
+
+// One decode work item: a run of logical pages that every listed agent maps to the same
+// physical base pages, processed by one workgroup per KV head.
+//   [0] first logical page   [1] number of pages   [2] number of agents
+//   [3] first partial slot (agent j of the item writes slot first + j)
+//   [4 .. 4+kItemAgents) agent indices
+constexpr int kItemAgents = 8;
+constexpr int kItemInts = 4 + kItemAgents;
+
+// Plan blob header (int32 words), followed by the sections at the given offsets.
+enum : int {
+  kHdrMagic = 0, kHdrAgents, kHdrItems, kHdrSlots, kHdrItemInts, kHdrQHeads,
+  kHdrOffItems, kHdrOffLens, kHdrOffSlotPtr, kHdrOffSlotList, kHdrKernel, kHdrGroup,
+  kHdrWords = 16
+};
+constexpr int32_t kPlanMagic = 0x464b5631;  // "FKV1"
+
+struct Seq {
+  bool alive = true;
+  bool has_res = false;
+  int32_t len = 0;
+  std::vector<int32_t> bpages, rpages;
+};
+
+}  // namespace forkkv
+
+struct forkkv_pool {
+  forkkv_pool_desc desc{};
+  void* bcache = nullptr;
+  void* rcache = nullptr;
+  std::deque<int32_t> free_b, free_r;
+  std::vector<int32_t> ref_b, ref_r;
+  std::vector<forkkv::Seq> seqs;
+};
+
+struct forkkv_plan {
+  forkkv_pool_desc geo{};   // geometry copy (orders cleared)
+  void* bcache = nullptr;
+  void* rcache = nullptr;
+  int32_t n_agents = 0, n_items = 0, n_slots = 0, num_q_heads = 0, kernel = 0;
+  int32_t group = 0;        // agents per item the kernel was planned for
+  std::vector<int32_t> blob;
+  void* dev = nullptr;      // caller's device copy
+  size_t workspace_bytes = 0;
+  size_t ws_off_acc = 0, ws_off_accr = 0;
+  int32_t max_pages_needed = 0;
+  // timing: (kind, begin, end) per timed launch, kind 0 = split, 1 = combine
+  bool timing = false;
+  struct Timed { int kind; hipEvent_t b, e; };
+  std::vector<Timed> pending;
+  std::vector<hipEvent_t> spare;
+};
+
+namespace forkkv {
+
+// Launch parameters of the decode kernels (passed by value).
+struct DecodeParams {
+  const void* q;
+  const void* Bk;
+  const void* Bv;
+  const void* bcache;
+  const void* rcache;
+  const int32_t* btab;
+  const int32_t* rtab;
+  const int32_t* plan;      // device blob
+  float* ws_ml;             // [slots][Hq][2]  (running max in log2 units, sum)
+  float* ws_acc;            // [slots][Hq][d]
+  float* ws_accr;           // [slots][Hq][r]
+  void* out;
+  int32_t n_agents, n_items, num_q_heads, num_kv_heads, head_dim, rank, group;
+  int32_t max_pages, num_bpages, num_rpages;
+  int32_t off_items, off_lens, off_slot_ptr, off_slot_list;
+  float lora_scale, sm_scale_log2, rope_theta;
+};
+
+struct PrefillParams {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  const void* rk_new;
+  const void* rv_new;
+  const void* Bk;
+  const void* Bv;
+  void* bcache;
+  void* rcache;
+  const int32_t* btab;
+  const int32_t* rtab;
+  const int32_t* start_pos;
+  void* out;
+  int32_t n_agents, chunk_len, num_q_heads, num_kv_heads, head_dim, rank, group;
+  int32_t max_pages, num_bpages, num_rpages;
+  float lora_scale, sm_scale_log2, rope_theta;
+};
+
+// Kernel launchers (defined in the .hip translation units).  They return hipError_t
+// from the launch.
+hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agents,
+                                 hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
+hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s);
+hipError_t launch_prefill_write(const PrefillParams& p, int dtype, hipStream_t s);
+hipError_t launch_prefill_generic(const PrefillParams& p, int dtype, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t* start_host,
+                               hipStream_t s);
+hipError_t launch_cow_copy(void* bcache, int dtype, int num_kv_heads, int head_dim,
+                           int32_t src_page, int32_t dst_page, int32_t n_rows, hipStream_t s);
+
+// Limits of the generic kernel.
+constexpr int kGenericThreads = 256;
+constexpr int kGenericAccPerThread = 32;   // rows * d <= 256 * 32
+constexpr int kGenericAccrPerThread = 8;   // rows * r <= 256 * 8
+constexpr int kGenericMaxRows = 64;
+int generic_max_agents(int group, int head_dim, int rank);
+int generic_lds_bytes(int na, int rows, int d, int r);
+bool prefill_mfma_enabled();
+bool mfma_supported(int dtype, int head_dim, int rank, int group);
+int mfma_group_agents(int group);
+
+}  // namespace forkkv

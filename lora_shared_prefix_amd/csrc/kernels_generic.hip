@@ -1,0 +1,503 @@
+// Generic (VALU, fp32 arithmetic) ResidualAttention kernels for gfx950, any supported
+// shape and element type, plus the split-K combine, the prefill row write and the
+// copy-on-write row copy.
+//
+// The attention kernel follows the fused form of the ForkKV study note
+// ("7. 实现 cross-reference", core barriers (1) and (2); "4. 作者证明", Eq.(4)):
+// per page, the full key of each agent is rebuilt in on-chip memory as
+// bK + RoPE(s * rK B_k) (RoPE after the up-projection), scores go through an online
+// softmax whose rescale factor multiplies both the base accumulator and the rank-r
+// residual accumulator, and B_v is applied once after the loop (here in the combine
+// kernel, or in the epilogue of the prefill kernel).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "forkkv_internal.h"
+
+namespace forkkv {
+namespace {
+
+// ---- element access ---------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {  // bfloat16 bit patterns
+  static __device__ __forceinline__ float ld(const uint16_t* p, size_t i) {
+    return __uint_as_float(uint32_t(p[i]) << 16);
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, size_t i, float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+      p[i] = 0x7fc0;  // quiet NaN
+      return;
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
+    p[i] = static_cast<uint16_t>(u >> 16);
+  }
+};
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+// Dynamic LDS layout of the generic attention kernel.
+struct GenLds {
+  int inv, cs, bk, bv, kq, rk, rv, s, alpha, m, l, accr, total;  // byte offsets
+};
+
+__host__ __device__ inline GenLds gen_lds(int na, int rows, int d, int r) {
+  GenLds L{};
+  int o = 0;
+  auto take = [&](int bytes) { int at = o; o += (bytes + 15) & ~15; return at; };
+  L.inv = take(8 * (d / 2));
+  L.cs = take(4 * kPage * d);  // [P][d/2][2]
+  L.bk = take(4 * kPage * d);
+  L.bv = take(4 * kPage * d);
+  L.kq = take(4 * kPage * d);
+  L.rk = take(4 * na * kPage * r);
+  L.rv = take(4 * na * kPage * r);
+  L.s = take(4 * rows * kPage);
+  L.alpha = take(4 * rows);
+  L.m = take(4 * rows);
+  L.l = take(4 * rows);
+  L.accr = take(4 * rows * r);
+  L.total = o;
+  return L;
+}
+
+constexpr int kMaxLds = 64 * 1024;
+
+// Rows of the workgroup: decode = (agent j of the item, q head within the group);
+// prefill = (query of the block, q head within the group), one agent.
+template <typename T, bool kPrefill>
+__global__ void __launch_bounds__(kGenericThreads)
+residual_attn_generic(DecodeParams dp, PrefillParams pp) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  using E = Elem<T>;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int d = kPrefill ? pp.head_dim : dp.head_dim;
+  const int r = kPrefill ? pp.rank : dp.rank;
+  const int G = kPrefill ? pp.group : dp.group;
+  const int Hq = kPrefill ? pp.num_q_heads : dp.num_q_heads;
+  const int Hkv = kPrefill ? pp.num_kv_heads : dp.num_kv_heads;
+  const int max_pages = kPrefill ? pp.max_pages : dp.max_pages;
+  const int nbp = kPrefill ? pp.num_bpages : dp.num_bpages;
+  const int nrp = kPrefill ? pp.num_rpages : dp.num_rpages;
+  const float ls = kPrefill ? pp.lora_scale : dp.lora_scale;
+  const float qscale = kPrefill ? pp.sm_scale_log2 : dp.sm_scale_log2;
+  const float theta = kPrefill ? pp.rope_theta : dp.rope_theta;
+  const T* bcache = static_cast<const T*>(kPrefill ? pp.bcache : dp.bcache);
+  const T* rcache = static_cast<const T*>(kPrefill ? pp.rcache : dp.rcache);
+  const int32_t* btab = kPrefill ? pp.btab : dp.btab;
+  const int32_t* rtab = kPrefill ? pp.rtab : dp.rtab;
+  const T* q = static_cast<const T*>(kPrefill ? pp.q : dp.q);
+  const T* Bk = static_cast<const T*>(kPrefill ? pp.Bk : dp.Bk);
+  const int half = d / 2;
+  const int n = Hkv * d;
+
+  // ---- work description -----------------------------------------------------------------
+  int na, lp_begin, lp_end, rows, slot_base = 0;
+  int agents[kItemAgents];
+  int limit[kItemAgents];  // decode: keys t < limit[j]
+  int a_pf = 0, q0 = 0, start = 0, C = 0, QB = 0;
+  if constexpr (kPrefill) {
+    a_pf = blockIdx.z;
+    C = pp.chunk_len;
+    QB = kGenericMaxRows / G;
+    if (QB * G * d > kGenericThreads * kGenericAccPerThread) QB = kGenericThreads * kGenericAccPerThread / (G * d);
+    if (QB * G * r > kGenericThreads * kGenericAccrPerThread) QB = kGenericThreads * kGenericAccrPerThread / (G * r);
+    q0 = blockIdx.x * QB;
+    start = pp.start_pos[a_pf];
+    const int nq = min(QB, C - q0);
+    rows = nq * G;
+    na = 1;
+    agents[0] = a_pf;
+    lp_begin = 0;
+    lp_end = (start + q0 + nq - 1) / kPage + 1;
+  } else {
+    const int32_t* it = dp.plan + dp.off_items + blockIdx.x * kItemInts;
+    lp_begin = it[0];
+    lp_end = it[0] + it[1];
+    na = it[2];
+    slot_base = it[3];
+    for (int j = 0; j < kItemAgents; ++j) {
+      agents[j] = j < na ? it[4 + j] : 0;
+      limit[j] = j < na ? dp.plan[dp.off_lens + agents[j]] : 0;
+    }
+    rows = na * G;
+  }
+  const GenLds L = gen_lds(na, rows, d, r);
+  double* inv = reinterpret_cast<double*>(lds + L.inv);
+  float* cs = reinterpret_cast<float*>(lds + L.cs);
+  float* sbk = reinterpret_cast<float*>(lds + L.bk);
+  float* sbv = reinterpret_cast<float*>(lds + L.bv);
+  float* skq = reinterpret_cast<float*>(lds + L.kq);
+  float* srk = reinterpret_cast<float*>(lds + L.rk);
+  float* srv = reinterpret_cast<float*>(lds + L.rv);
+  float* sS = reinterpret_cast<float*>(lds + L.s);
+  float* salpha = reinterpret_cast<float*>(lds + L.alpha);
+  float* sm = reinterpret_cast<float*>(lds + L.m);
+  float* sl = reinterpret_cast<float*>(lds + L.l);
+  float* saccr = reinterpret_cast<float*>(lds + L.accr);
+
+  for (int j = tid; j < half; j += kGenericThreads)
+    inv[j] = pow(static_cast<double>(theta), -2.0 * j / d);
+  for (int i = tid; i < rows; i += kGenericThreads) {
+    sm[i] = -INFINITY;
+    sl[i] = 0.f;
+  }
+  float acc[kGenericAccPerThread];
+  float accr[kGenericAccrPerThread];
+#pragma unroll
+  for (int i = 0; i < kGenericAccPerThread; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kGenericAccrPerThread; ++i) accr[i] = 0.f;
+  __syncthreads();
+
+  // row -> (agent slot j, query index, head within group)
+  auto row_agent = [&](int row) { return kPrefill ? 0 : row / G; };
+
+  for (int lp = lp_begin; lp < lp_end; ++lp) {
+    const int bpg = btab[size_t(agents[0]) * max_pages + lp];
+    if (bpg < 0 || bpg >= nbp) continue;  // never read outside the pool
+    const size_t kbase = (size_t(bpg) * 2 * Hkv + h) * kPage * d;
+    const size_t vbase = (size_t(bpg) * 2 * Hkv + Hkv + h) * kPage * d;
+    // Rows no query of this workgroup may read are never loaded: their contents are
+    // arbitrary (even NaN) and a zero probability times NaN would still be NaN.
+    int vrows;
+    if constexpr (kPrefill) {
+      vrows = min(kPage, max(0, start + q0 + rows / G - lp * kPage));
+    } else {
+      vrows = 0;
+      for (int j = 0; j < na; ++j) vrows = max(vrows, min(kPage, limit[j] - lp * kPage));
+    }
+    for (int i = tid; i < kPage * d; i += kGenericThreads) {
+      sbk[i] = i / d < vrows ? E::ld(bcache, kbase + i) : 0.f;
+      const int dd = i / kPage, row = i % kPage;
+      sbv[row * d + dd] = row < vrows ? E::ld(bcache, vbase + i) : 0.f;
+    }
+    bool rok[kItemAgents];
+    for (int j = 0; j < na; ++j) {
+      const int rpg = rtab[size_t(agents[j]) * max_pages + lp];
+      rok[j] = rpg >= 0 && rpg < nrp;
+      const size_t rb = size_t(rok[j] ? rpg : 0) * 2 * kPage * r;
+      for (int i = tid; i < kPage * r; i += kGenericThreads) {
+        srk[j * kPage * r + i] = (rok[j] && i / r < vrows) ? E::ld(rcache, rb + i) : 0.f;
+        const int k = i / kPage, row = i % kPage;
+        srv[(j * kPage + row) * r + k] =
+            (rok[j] && row < vrows) ? E::ld(rcache, rb + kPage * r + i) : 0.f;
+      }
+    }
+    for (int i = tid; i < kPage * half; i += kGenericThreads) {
+      const int row = i / half, jj = i % half;
+      double ang = static_cast<double>(lp * kPage + row) * inv[jj];
+      ang -= kTwoPi * floor(ang / kTwoPi);
+      double sv, cv;
+      sincos(ang, &sv, &cv);
+      cs[2 * i] = static_cast<float>(cv);
+      cs[2 * i + 1] = static_cast<float>(sv);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < na; ++j) {
+      const T* bk_a = Bk + size_t(agents[j]) * r * n + size_t(h) * d;
+      for (int i = tid; i < kPage * half; i += kGenericThreads) {
+        const int row = i / half, jj = i % half;
+        float x = 0.f, y = 0.f;
+        for (int k = 0; k < r; ++k) {
+          const float rk = srk[(j * kPage + row) * r + k];
+          x += rk * E::ld(bk_a, size_t(k) * n + jj);
+          y += rk * E::ld(bk_a, size_t(k) * n + jj + half);
+        }
+        const float c = cs[2 * i], s = cs[2 * i + 1];
+        skq[row * d + jj] = sbk[row * d + jj] + ls * (x * c - y * s);
+        skq[row * d + jj + half] = sbk[row * d + jj + half] + ls * (y * c + x * s);
+      }
+      __syncthreads();
+      const int row0 = kPrefill ? 0 : j * G;
+      const int nrows = kPrefill ? rows : G;
+      for (int i = tid; i < nrows * kPage; i += kGenericThreads) {
+        const int row = row0 + i / kPage, t = i % kPage;
+        const int pos = lp * kPage + t;
+        size_t qoff;
+        bool valid;
+        if constexpr (kPrefill) {
+          const int qi = q0 + row / G, g = row % G;
+          qoff = ((size_t(a_pf) * C + qi) * Hq + h * G + g) * d;
+          valid = pos <= start + qi;
+        } else {
+          const int g = row % G;
+          qoff = (size_t(agents[j]) * Hq + h * G + g) * d;
+          valid = pos < limit[j];
+        }
+        valid = valid && rok[j];
+        float sc = -INFINITY;
+        if (valid) {
+          float dot = 0.f;
+          for (int dd = 0; dd < d; ++dd) dot += E::ld(q, qoff + dd) * skq[t * d + dd];
+          sc = dot * qscale;
+        }
+        sS[row * kPage + t] = sc;
+      }
+      __syncthreads();
+    }
+
+    // online softmax (log2 domain): rescale factor alpha applies to acc AND acc_r
+    for (int row = tid; row < rows; row += kGenericThreads) {
+      const float m_old = sm[row];
+      float mx = -INFINITY;
+      for (int t = 0; t < kPage; ++t) mx = fmaxf(mx, sS[row * kPage + t]);
+      const float m_new = fmaxf(m_old, mx);
+      float alpha = 1.f, sum = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_old - m_new);
+        for (int t = 0; t < kPage; ++t) {
+          const float p = exp2f(sS[row * kPage + t] - m_new);
+          sS[row * kPage + t] = p;
+          sum += p;
+        }
+      } else {
+        for (int t = 0; t < kPage; ++t) sS[row * kPage + t] = 0.f;
+      }
+      salpha[row] = alpha;
+      sl[row] = alpha * sl[row] + sum;
+      sm[row] = m_new;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGenericAccPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * d) {
+        const int row = e / d, dd = e % d;
+        float v = 0.f;
+        for (int t = 0; t < kPage; ++t) v += sS[row * kPage + t] * sbv[t * d + dd];
+        acc[i] = salpha[row] * acc[i] + v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGenericAccrPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * r) {
+        const int row = e / r, k = e % r, j = row_agent(row);
+        float v = 0.f;
+        for (int t = 0; t < kPage; ++t) v += sS[row * kPage + t] * srv[(j * kPage + t) * r + k];
+        accr[i] = salpha[row] * accr[i] + v;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (kPrefill) {
+    // epilogue: o = (acc + s * acc_r B_v) / l   (B_v applied once)
+#pragma unroll
+    for (int i = 0; i < kGenericAccrPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * r) saccr[e] = accr[i];
+    }
+    __syncthreads();
+    const T* Bv = static_cast<const T*>(pp.Bv);
+    const T* bv_a = Bv + size_t(a_pf) * r * n + size_t(h) * d;
+    T* out = static_cast<T*>(pp.out);
+#pragma unroll
+    for (int i = 0; i < kGenericAccPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * d) {
+        const int row = e / d, dd = e % d;
+        float v = acc[i];
+        float res = 0.f;
+        for (int k = 0; k < r; ++k) res += saccr[row * r + k] * E::ld(bv_a, size_t(k) * n + dd);
+        v += ls * res;
+        const float l = sl[row];
+        const int qi = q0 + row / G, g = row % G;
+        E::st(out, ((size_t(a_pf) * C + qi) * Hq + h * G + g) * d + dd, l > 0.f ? v / l : 0.f);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kGenericAccPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * d) {
+        const int row = e / d, dd = e % d, j = row / G, g = row % G;
+        dp.ws_acc[((size_t(slot_base) + j) * Hq + h * G + g) * d + dd] = acc[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGenericAccrPerThread; ++i) {
+      const int e = tid + i * kGenericThreads;
+      if (e < rows * r) {
+        const int row = e / r, k = e % r, j = row / G, g = row % G;
+        dp.ws_accr[((size_t(slot_base) + j) * Hq + h * G + g) * r + k] = accr[i];
+      }
+    }
+    for (int row = tid; row < rows; row += kGenericThreads) {
+      const int j = row / G, g = row % G;
+      const size_t o = ((size_t(slot_base) + j) * Hq + h * G + g) * 2;
+      dp.ws_ml[o] = sm[row];
+      dp.ws_ml[o + 1] = sl[row];
+    }
+  }
+}
+
+// Split-K merge with a log-sum-exp rule, then the one-time B_v up-projection:
+// o = (sum_i w_i acc_i + s * (sum_i w_i acc_r,i) B_v) / sum_i w_i l_i, w_i = 2^(m_i - M).
+template <typename T>
+__global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
+  using E = Elem<T>;
+  __shared__ float s_ar[64];
+  const int a = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int d = p.head_dim, r = p.rank, Hq = p.num_q_heads, h = g / p.group;
+  const int n = p.num_kv_heads * d;
+  const int s0 = p.plan[p.off_slot_ptr + a], s1 = p.plan[p.off_slot_ptr + a + 1];
+  const int32_t* slots = p.plan + p.off_slot_list;
+  float M = -INFINITY;
+  for (int i = s0; i < s1; ++i) M = fmaxf(M, p.ws_ml[(size_t(slots[i]) * Hq + g) * 2]);
+  float Lsum = 0.f;
+  float A = 0.f, Ar = 0.f;
+  for (int i = s0; i < s1; ++i) {
+    const size_t row = size_t(slots[i]) * Hq + g;
+    const float m = p.ws_ml[row * 2];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    Lsum += w * p.ws_ml[row * 2 + 1];
+    if (tid < d) A += w * p.ws_acc[row * d + tid];
+    if (tid < r) Ar += w * p.ws_accr[row * r + tid];
+  }
+  if (tid < r) s_ar[tid] = Ar;
+  __syncthreads();
+  if (tid < d) {
+    const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + tid;
+    float res = 0.f;
+    for (int k = 0; k < r; ++k) res += s_ar[k] * E::ld(bv, size_t(k) * n);
+    const float o = Lsum > 0.f ? (A + p.lora_scale * res) / Lsum : 0.f;
+    E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + tid, o);
+  }
+}
+
+// Store the chunk rows at their slots (bit-exact copies in the pool layout).
+template <typename T>
+__global__ void __launch_bounds__(256) prefill_write_kernel(PrefillParams p) {
+  const int i = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
+  const int d = p.head_dim, r = p.rank, Hkv = p.num_kv_heads, C = p.chunk_len;
+  const int t = p.start_pos[a] + i;
+  const int lp = t / kPage, row = t % kPage;
+  const int bpg = p.btab[size_t(a) * p.max_pages + lp];
+  const int rpg = p.rtab[size_t(a) * p.max_pages + lp];
+  T* bc = static_cast<T*>(p.bcache);
+  T* rc = static_cast<T*>(p.rcache);
+  const T* kn = static_cast<const T*>(p.k_new) + (size_t(a) * C + i) * Hkv * d;
+  const T* vn = static_cast<const T*>(p.v_new) + (size_t(a) * C + i) * Hkv * d;
+  if (bpg >= 0 && bpg < p.num_bpages) {
+    for (int idx = tid; idx < Hkv * d; idx += blockDim.x) {
+      const int h = idx / d, dd = idx % d;
+      bc[(size_t(bpg) * 2 * Hkv + h) * kPage * d + row * d + dd] = kn[idx];
+      bc[(size_t(bpg) * 2 * Hkv + Hkv + h) * kPage * d + dd * kPage + row] = vn[idx];
+    }
+  }
+  if (rpg >= 0 && rpg < p.num_rpages) {
+    const T* rkn = static_cast<const T*>(p.rk_new) + (size_t(a) * C + i) * r;
+    const T* rvn = static_cast<const T*>(p.rv_new) + (size_t(a) * C + i) * r;
+    for (int k = tid; k < r; k += blockDim.x) {
+      rc[size_t(rpg) * 2 * kPage * r + row * r + k] = rkn[k];
+      rc[size_t(rpg) * 2 * kPage * r + kPage * r + k * kPage + row] = rvn[k];
+    }
+  }
+}
+
+// Copy the first n rows of base page src into page dst, every KV head, K and V planes.
+template <typename T>
+__global__ void __launch_bounds__(256) cow_copy_kernel(T* bc, int Hkv, int d, int src, int dst,
+                                                       int nrows) {
+  const int total = 2 * Hkv * kPage * d;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int plane = i / (Hkv * kPage * d);
+    const int rem = i % (kPage * d);
+    const int row = plane == 0 ? rem / d : rem % kPage;
+    if (row < nrows) bc[size_t(dst) * total + i] = bc[size_t(src) * total + i];
+  }
+}
+
+int prefill_rows(int G, int d, int r) {
+  int QB = kGenericMaxRows / G;
+  if (QB * G * d > kGenericThreads * kGenericAccPerThread) QB = kGenericThreads * kGenericAccPerThread / (G * d);
+  if (QB * G * r > kGenericThreads * kGenericAccrPerThread) QB = kGenericThreads * kGenericAccrPerThread / (G * r);
+  return QB;
+}
+
+}  // namespace
+
+int generic_lds_bytes(int na, int rows, int d, int r) { return gen_lds(na, rows, d, r).total; }
+
+int generic_max_agents(int group, int head_dim, int rank) {
+  int best = 0;
+  for (int na = 1; na <= kItemAgents; ++na) {
+    const int rows = na * group;
+    if (rows > kGenericMaxRows) break;
+    if (rows * head_dim > kGenericThreads * kGenericAccPerThread) break;
+    if (rows * rank > kGenericThreads * kGenericAccrPerThread) break;
+    if (gen_lds(na, rows, head_dim, rank).total > kMaxLds) break;
+    best = na;
+  }
+  return best;
+}
+
+hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agents, hipStream_t s) {
+  const int rows = max_agents * p.group;
+  const int lds = gen_lds(max_agents, rows, p.head_dim, p.rank).total;
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  dim3 grid(p.n_items, p.num_kv_heads);
+  PrefillParams none{};
+  if (dtype == FORKKV_DTYPE_F32)
+    hipLaunchKernelGGL((residual_attn_generic<float, false>), grid, dim3(kGenericThreads), lds, s, p, none);
+  else
+    hipLaunchKernelGGL((residual_attn_generic<uint16_t, false>), grid, dim3(kGenericThreads), lds, s, p, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s) {
+  if (p.head_dim > 256 || p.rank > 64) return hipErrorInvalidValue;
+  dim3 grid(p.n_agents, p.num_q_heads);
+  if (dtype == FORKKV_DTYPE_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_write(const PrefillParams& p, int dtype, hipStream_t s) {
+  dim3 grid(p.chunk_len, p.n_agents);
+  if (dtype == FORKKV_DTYPE_F32)
+    hipLaunchKernelGGL(prefill_write_kernel<float>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(prefill_write_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_generic(const PrefillParams& p, int dtype, hipStream_t s) {
+  const int QB = prefill_rows(p.group, p.head_dim, p.rank);
+  if (QB < 1) return hipErrorInvalidValue;
+  const int lds = gen_lds(1, QB * p.group, p.head_dim, p.rank).total;
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  dim3 grid((p.chunk_len + QB - 1) / QB, p.num_kv_heads, p.n_agents);
+  DecodeParams none{};
+  if (dtype == FORKKV_DTYPE_F32)
+    hipLaunchKernelGGL((residual_attn_generic<float, true>), grid, dim3(kGenericThreads), lds, s, none, p);
+  else
+    hipLaunchKernelGGL((residual_attn_generic<uint16_t, true>), grid, dim3(kGenericThreads), lds, s, none, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cow_copy(void* bcache, int dtype, int Hkv, int d, int32_t src, int32_t dst,
+                           int32_t n_rows, hipStream_t s) {
+  const int total = 2 * Hkv * kPage * d;
+  const int blocks = (total + 255) / 256;
+  if (dtype == FORKKV_DTYPE_F32)
+    hipLaunchKernelGGL(cow_copy_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<float*>(bcache), Hkv, d, src, dst, n_rows);
+  else
+    hipLaunchKernelGGL(cow_copy_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<uint16_t*>(bcache), Hkv, d, src, dst, n_rows);
+  return hipGetLastError();
+}
+
+}  // namespace forkkv

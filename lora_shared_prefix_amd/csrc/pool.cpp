@@ -1,0 +1,292 @@
+// Host bookkeeping of the forked, disaggregated page pools.
+//
+// ForkKV study note, "3. 架构 / 方法图" (Figure 6): a new agent maps the parent's
+// read-only base pages and allocates only its own residual pages.  ForkServe README,
+// "Design vs APC", "Methods" (CoW tree) and "Status": fork aliases the parent's frames,
+// writes allocate private pages, an unaligned tail is packed by copying its n_valid rows,
+// and reference counts keep a trunk alive after its parent is freed.
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "forkkv_internal.h"
+
+using forkkv::Seq;
+using forkkv::kPage;
+
+namespace {
+
+int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+
+size_t elem_bytes(int dtype) { return dtype == FORKKV_DTYPE_F32 ? 4 : 2; }
+
+bool valid_desc(const forkkv_pool_desc* d) {
+  if (!d) return false;
+  if (d->page_size != kPage) return false;
+  if (d->num_bpages < 1 || d->num_rpages < 1) return false;
+  if (d->num_kv_heads < 1 || d->num_kv_heads > 64) return false;
+  if (d->head_dim < 2 || d->head_dim > 256 || (d->head_dim & 1)) return false;
+  if (d->rank < 1 || d->rank > 64) return false;
+  if (d->dtype != FORKKV_DTYPE_F32 && d->dtype != FORKKV_DTYPE_BF16) return false;
+  return true;
+}
+
+bool valid_order(const int32_t* order, int32_t n) {
+  if (!order) return true;
+  std::vector<char> seen(n, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (order[i] < 0 || order[i] >= n || seen[order[i]]) return false;
+    seen[order[i]] = 1;
+  }
+  return true;
+}
+
+Seq* get_seq(forkkv_pool* p, forkkv_seq h) {
+  if (!p || h < 0 || static_cast<size_t>(h) >= p->seqs.size() || !p->seqs[h].alive) return nullptr;
+  return &p->seqs[h];
+}
+
+const Seq* get_seq(const forkkv_pool* p, forkkv_seq h) {
+  if (!p || h < 0 || static_cast<size_t>(h) >= p->seqs.size() || !p->seqs[h].alive) return nullptr;
+  return &p->seqs[h];
+}
+
+int32_t take(std::deque<int32_t>& fl, std::vector<int32_t>& ref) {
+  int32_t pg = fl.front();
+  fl.pop_front();
+  ref[pg] = 1;
+  return pg;
+}
+
+void clear_cow(forkkv_cow_op* cow) {
+  if (cow) *cow = forkkv_cow_op{-1, -1, 0};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* forkkv_strerror(int code) {
+  switch (code) {
+    case FORKKV_OK: return "ok";
+    case FORKKV_EINVAL: return "invalid argument";
+    case FORKKV_ENOMEM: return "page pool exhausted";
+    case FORKKV_EHIP: return "HIP error";
+    case FORKKV_ESTATE: return "invalid state";
+    case FORKKV_EUNSUPPORTED: return "unsupported shape or dtype";
+    default: return "unknown error";
+  }
+}
+
+int forkkv_pool_bytes(const forkkv_pool_desc* d, size_t* bbytes, size_t* rbytes) {
+  if (!valid_desc(d)) return FORKKV_EINVAL;
+  const size_t e = elem_bytes(d->dtype);
+  if (bbytes) *bbytes = size_t(d->num_bpages) * 2 * d->num_kv_heads * kPage * d->head_dim * e;
+  if (rbytes) *rbytes = size_t(d->num_rpages) * 2 * kPage * d->rank * e;
+  return FORKKV_OK;
+}
+
+int forkkv_pool_create(const forkkv_pool_desc* d, void* bcache, void* rcache,
+                       forkkv_pool** out) {
+  if (!out || !valid_desc(d)) return FORKKV_EINVAL;
+  if (!valid_order(d->bpage_order, d->num_bpages) || !valid_order(d->rpage_order, d->num_rpages))
+    return FORKKV_EINVAL;
+  if ((bcache == nullptr) != (rcache == nullptr)) return FORKKV_EINVAL;
+  forkkv_pool* p = new (std::nothrow) forkkv_pool();
+  if (!p) return FORKKV_ENOMEM;
+  p->desc = *d;
+  p->desc.bpage_order = nullptr;
+  p->desc.rpage_order = nullptr;
+  p->bcache = bcache;
+  p->rcache = rcache;
+  p->ref_b.assign(d->num_bpages, 0);
+  p->ref_r.assign(d->num_rpages, 0);
+  for (int32_t i = 0; i < d->num_bpages; ++i)
+    p->free_b.push_back(d->bpage_order ? d->bpage_order[i] : i);
+  for (int32_t i = 0; i < d->num_rpages; ++i)
+    p->free_r.push_back(d->rpage_order ? d->rpage_order[i] : i);
+  *out = p;
+  return FORKKV_OK;
+}
+
+int forkkv_pool_destroy(forkkv_pool* p) {
+  if (!p) return FORKKV_EINVAL;
+  delete p;
+  return FORKKV_OK;
+}
+
+int forkkv_seq_create(forkkv_pool* p, int32_t with_residual, forkkv_seq* out) {
+  if (!p || !out) return FORKKV_EINVAL;
+  Seq s;
+  s.has_res = with_residual != 0;
+  p->seqs.push_back(std::move(s));
+  *out = static_cast<forkkv_seq>(p->seqs.size() - 1);
+  return FORKKV_OK;
+}
+
+int forkkv_seq_append(forkkv_pool* p, forkkv_seq h, int32_t n, int32_t* bslots,
+                      int32_t* rslots, forkkv_cow_op* cow) {
+  Seq* s = get_seq(p, h);
+  if (!s || n < 0) return FORKKV_EINVAL;
+  const int64_t new_len = int64_t(s->len) + n;
+  if (new_len > INT32_MAX / 2) return FORKKV_EINVAL;
+  const int32_t grow = ceil_div(new_len, kPage) - static_cast<int32_t>(s->bpages.size());
+  // A write into a shared partial last page needs a private copy first.
+  const bool need_cow = n > 0 && (s->len % kPage) != 0 && p->ref_b[s->bpages.back()] > 1;
+  const int32_t need_b = grow + (need_cow ? 1 : 0);
+  const int32_t need_r = s->has_res ? grow : 0;
+  if (need_b > static_cast<int32_t>(p->free_b.size()) ||
+      need_r > static_cast<int32_t>(p->free_r.size()))
+    return FORKKV_ENOMEM;
+  clear_cow(cow);
+  if (need_cow) {
+    const int32_t old = s->bpages.back();
+    const int32_t fresh = take(p->free_b, p->ref_b);
+    p->ref_b[old] -= 1;
+    s->bpages.back() = fresh;
+    if (cow) *cow = forkkv_cow_op{old, fresh, s->len % kPage};
+  }
+  for (int32_t i = 0; i < grow; ++i) {
+    s->bpages.push_back(take(p->free_b, p->ref_b));
+    if (s->has_res) s->rpages.push_back(take(p->free_r, p->ref_r));
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t t = s->len + i;
+    if (bslots) bslots[i] = s->bpages[t / kPage] * kPage + t % kPage;
+    if (rslots) rslots[i] = s->has_res ? s->rpages[t / kPage] * kPage + t % kPage : -1;
+  }
+  s->len = static_cast<int32_t>(new_len);
+  return FORKKV_OK;
+}
+
+int forkkv_fork(forkkv_pool* p, forkkv_seq parent, int32_t alias_len, forkkv_seq* child,
+                forkkv_cow_op* cow) {
+  Seq* ps = get_seq(p, parent);
+  if (!ps || !child || alias_len < 0 || alias_len > ps->len) return FORKKV_EINVAL;
+  const int32_t full = alias_len / kPage;
+  const int32_t tail = alias_len % kPage;
+  const int32_t need_b = tail ? 1 : 0;
+  const int32_t need_r = ceil_div(alias_len, kPage);
+  if (need_b > static_cast<int32_t>(p->free_b.size()) ||
+      need_r > static_cast<int32_t>(p->free_r.size()))
+    return FORKKV_ENOMEM;
+  clear_cow(cow);
+  Seq c;
+  c.has_res = true;
+  c.bpages.assign(ps->bpages.begin(), ps->bpages.begin() + full);
+  for (int32_t pg : c.bpages) p->ref_b[pg] += 1;
+  if (tail) {
+    const int32_t src = ps->bpages[full];
+    const int32_t fresh = take(p->free_b, p->ref_b);
+    c.bpages.push_back(fresh);
+    if (cow) *cow = forkkv_cow_op{src, fresh, tail};
+  }
+  for (int32_t i = 0; i < need_r; ++i) c.rpages.push_back(take(p->free_r, p->ref_r));
+  c.len = alias_len;
+  p->seqs.push_back(std::move(c));  // may reallocate: ps is not used after this
+  *child = static_cast<forkkv_seq>(p->seqs.size() - 1);
+  return FORKKV_OK;
+}
+
+int forkkv_seq_free(forkkv_pool* p, forkkv_seq h) {
+  Seq* s = get_seq(p, h);
+  if (!s) return FORKKV_EINVAL;
+  for (int32_t pg : s->bpages)
+    if (--p->ref_b[pg] == 0) p->free_b.push_back(pg);
+  for (int32_t pg : s->rpages)
+    if (--p->ref_r[pg] == 0) p->free_r.push_back(pg);
+  s->alive = false;
+  s->len = 0;
+  s->bpages.clear();
+  s->rpages.clear();
+  return FORKKV_OK;
+}
+
+int forkkv_seq_len(const forkkv_pool* p, forkkv_seq h, int32_t* len) {
+  const Seq* s = get_seq(p, h);
+  if (!s || !len) return FORKKV_EINVAL;
+  *len = s->len;
+  return FORKKV_OK;
+}
+
+int forkkv_export_tables(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
+                         int32_t max_pages, int32_t* btab, int32_t* rtab, int32_t* seq_lens) {
+  if (!p || n < 0 || (n > 0 && !seqs) || max_pages < 0) return FORKKV_EINVAL;
+  if (n > 0 && (!btab || !rtab)) return FORKKV_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get_seq(p, seqs[i]);
+    if (!s || static_cast<int32_t>(s->bpages.size()) > max_pages) return FORKKV_EINVAL;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get_seq(p, seqs[i]);
+    int32_t* bt = btab + size_t(i) * max_pages;
+    int32_t* rt = rtab + size_t(i) * max_pages;
+    std::fill(bt, bt + max_pages, -1);
+    std::fill(rt, rt + max_pages, -1);
+    std::copy(s->bpages.begin(), s->bpages.end(), bt);
+    std::copy(s->rpages.begin(), s->rpages.end(), rt);
+    if (seq_lens) seq_lens[i] = s->len;
+  }
+  return FORKKV_OK;
+}
+
+int forkkv_pool_stats(const forkkv_pool* p, forkkv_stats* st) {
+  if (!p || !st) return FORKKV_EINVAL;
+  forkkv_stats z{};
+  z.free_bpages = static_cast<int32_t>(p->free_b.size());
+  z.free_rpages = static_cast<int32_t>(p->free_r.size());
+  z.live_bpages = p->desc.num_bpages - z.free_bpages;
+  z.live_rpages = p->desc.num_rpages - z.free_rpages;
+  for (int32_t c : p->ref_b) {
+    z.bpage_refs += c;
+    if (c > 1) ++z.shared_bpages;
+  }
+  for (int32_t c : p->ref_r) z.rpage_refs += c;
+  const size_t e = elem_bytes(p->desc.dtype);
+  z.live_bytes_b = int64_t(z.live_bpages) * 2 * p->desc.num_kv_heads * kPage * p->desc.head_dim * e;
+  z.live_bytes_r = int64_t(z.live_rpages) * 2 * kPage * p->desc.rank * e;
+  *st = z;
+  return FORKKV_OK;
+}
+
+int forkkv_free_list(const forkkv_pool* p, int32_t which, int32_t* out, int32_t cap, int32_t* n) {
+  if (!p || !n || (which != 0 && which != 1) || cap < 0) return FORKKV_EINVAL;
+  const std::deque<int32_t>& fl = which == 0 ? p->free_b : p->free_r;
+  *n = static_cast<int32_t>(fl.size());
+  if (out) {
+    int32_t i = 0;
+    for (auto it = fl.begin(); it != fl.end() && i < cap; ++it) out[i++] = *it;
+  }
+  return FORKKV_OK;
+}
+
+int forkkv_refcounts(const forkkv_pool* p, int32_t which, int32_t* out) {
+  if (!p || !out || (which != 0 && which != 1)) return FORKKV_EINVAL;
+  const std::vector<int32_t>& r = which == 0 ? p->ref_b : p->ref_r;
+  std::copy(r.begin(), r.end(), out);
+  return FORKKV_OK;
+}
+
+int forkkv_cow_copy(forkkv_pool* p, const forkkv_cow_op* ops, int32_t n_ops, hipStream_t stream) {
+  if (!p || n_ops < 0 || (n_ops > 0 && !ops)) return FORKKV_EINVAL;
+  if (!p->bcache) return FORKKV_ESTATE;
+  for (int32_t i = 0; i < n_ops; ++i) {
+    const forkkv_cow_op& o = ops[i];
+    if (o.n_rows == 0) continue;
+    if (o.n_rows < 0 || o.n_rows > kPage || o.src_bpage < 0 || o.dst_bpage < 0 ||
+        o.src_bpage >= p->desc.num_bpages || o.dst_bpage >= p->desc.num_bpages ||
+        o.src_bpage == o.dst_bpage)
+      return FORKKV_EINVAL;
+  }
+  for (int32_t i = 0; i < n_ops; ++i) {
+    const forkkv_cow_op& o = ops[i];
+    if (o.n_rows == 0) continue;
+    if (forkkv::launch_cow_copy(p->bcache, p->desc.dtype, p->desc.num_kv_heads,
+                                p->desc.head_dim, o.src_bpage, o.dst_bpage, o.n_rows,
+                                stream) != hipSuccess)
+      return FORKKV_EHIP;
+  }
+  return FORKKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+"""Helpers of the GPU parity tests: tolerance checks and oracle-side batch builders."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import PoolModel
+from oracle.storage import decode_values
+
+# Tolerance (bf16 inputs, fp32 accumulation): max-abs error <= 1e-2 and the largest
+# absolute error relative to the largest reference magnitude (a normwise relative
+# error) <= 2e-2, per output tensor.  Element-wise relative error is ill-posed here:
+# attention outputs over thousands of keys have many entries near zero.
+MAX_ABS = 1e-2
+MAX_REL = 2e-2
+
+
+def errors(g, r):
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    diff = np.abs(g - r)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    scale = float(np.abs(r).max()) if r.size else 0.0
+    rel = max_abs / scale if scale > 0 else max_abs
+    return max_abs, rel
+
+
+def assert_close(g, r, what="", max_abs=MAX_ABS, max_rel=MAX_REL, scale_abs=False):
+    """scale_abs: synthetic cases whose outputs exceed 1 in magnitude -- bf16 rounding of
+    the output alone is |o| * 2^-9 there -- scale the absolute bar by max(1, max|r|)."""
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    a, rel = errors(g, r)
+    if scale_abs:
+        max_abs = max_abs * max(1.0, float(np.abs(np.asarray(r)).max()))
+    print(f"[parity] {what}: max_abs={a:.3e} normwise_rel={rel:.3e}", flush=True)
+    assert a <= max_abs and rel <= max_rel, f"{what}: max_abs={a:.3e} rel={rel:.3e}"
+
+
+def gpu_values(t, dtype):
+    a = t.detach().cpu().numpy()
+    if dtype == "bf16":
+        a = a.view(np.uint16)
+    return decode_values(a, dtype)
+
+
+def model_tables(num_bpages, num_rpages, perm_b, perm_r, ops, agents, max_pages):
+    pm = PoolModel(num_bpages, num_rpages, 16, perm_b, perm_r)
+    names = pm.replay(ops)
+    hs = [names[a] for a in agents]
+    bt, rt, lens = pm.tables(hs, max_pages)
+    return pm, hs, np.array(bt, dtype=np.int32), np.array(rt, dtype=np.int32), np.array(lens)
+
+
+def apply_cows_host(bpool, cows, Hkv, d):
+    """Row copies of fork packing applied to a host pool (K rows and V^T columns)."""
+    out = bpool.copy()
+    for src, dst, n in cows:
+        for h in range(Hkv):
+            k = out[src, 0, h].reshape(16, d)
+            out[dst, 0, h].reshape(16, d)[:n] = k[:n]
+            v = out[src, 1, h].reshape(d, 16)
+            out[dst, 1, h].reshape(d, 16)[:, :n] = v[:, :n]
+    return out
+
+
+def used_rows(bt, rt, lens):
+    """Sets of (page, row) slots read by the batch."""
+    b, r = set(), set()
+    for a in range(len(lens)):
+        for t in range(int(lens[a])):
+            b.add((int(bt[a][t // 16]), t % 16))
+            r.add((int(rt[a][t // 16]), t % 16))
+    return b, r
+
+
+def poison_unused(bpool, rpool, used_b, used_r, dtype, d, r):
+    """Fill every slot the batch never reads with NaN (bit pattern for bf16)."""
+    nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC0)
+    bp, rp = bpool.copy(), rpool.copy()
+    for page in range(bp.shape[0]):
+        for row in range(16):
+            if (page, row) not in used_b:
+                for h in range(bp.shape[2]):
+                    bp[page, 0, h].reshape(16, d)[row] = nan
+                    bp[page, 1, h].reshape(d, 16)[:, row] = nan
+    for page in range(rp.shape[0]):
+        for row in range(16):
+            if (page, row) not in used_r:
+                rp[page, 0].reshape(16, r)[row] = nan
+                rp[page, 1].reshape(r, 16)[:, row] = nan
+    return bp, rp

@@ -1,0 +1,228 @@
+"""libforkkv's host bookkeeping against the oracle's pool model, bit for bit (CPU only).
+
+Tables, reference counts, free-list order, slots, copy-on-write row copies and
+error behaviour must be identical; the plan's work list must cover every
+(agent, page) exactly once with agents that really share the page.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from lora_shared_prefix_amd import forkkv as fk
+from oracle import PoolError, PoolModel
+from tests.pool_scenarios import fanout_ops, read_table
+from workloads import CONFIGS, chunk_ops, pool_ops
+
+ITEM_INTS = 12
+
+
+def _pair(nb, nr, perm_b=None, perm_r=None, Hkv=1, d=8, r=4):
+    lib_pool = fk.Pool(nb, nr, Hkv, d, r, "f32", perm_b, perm_r)
+    model = PoolModel(nb, nr, 16, perm_b, perm_r)
+    return lib_pool, model
+
+
+def _same_state(lp: fk.Pool, pm: PoolModel, handles):
+    assert lp.free_list(0) == list(pm.free_b)
+    assert lp.free_list(1) == list(pm.free_r)
+    assert lp.refcounts(0) == pm.ref_b
+    assert lp.refcounts(1) == pm.ref_r
+    st = lp.stats()
+    ms = pm.stats()
+    for k, v in ms.items():
+        assert st[k] == v, k
+    if handles:
+        mp = max(1, max(len(pm.seqs[h].bpages) for h in handles))
+        assert lp.tables(handles, mp) == tuple(map(list, pm.tables(handles, mp)))
+
+
+def _replay_both(lp, pm, ops):
+    names_l, cows_l = lp.replay(ops)
+    names_m, cows_m = {}, []
+    for op in ops:
+        if op[0] == "create":
+            names_m[op[1]] = pm.create(bool(op[2]))
+        elif op[0] == "append":
+            _, _, c = pm.append(names_m[op[1]], op[2])
+            if c:
+                cows_m.append(c)
+        else:
+            names_m[op[3]], c = pm.fork(names_m[op[1]], op[2])
+            if c:
+                cows_m.append(c)
+    assert names_l == names_m and cows_l == cows_m
+    return names_l
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_workload_topologies_match_model(idx):
+    cfg = CONFIGS[idx]
+    rng = np.random.default_rng(cfg.seed)
+    pb = rng.permutation(cfg.num_bpages)
+    pr = rng.permutation(cfg.num_rpages)
+    lp, pm = _pair(cfg.num_bpages, cfg.num_rpages, pb, pr)
+    ops, agents = pool_ops(cfg)
+    names = _replay_both(lp, pm, ops + chunk_ops(cfg, agents))
+    _same_state(lp, pm, [names[a] for a in agents])
+
+
+@pytest.mark.parametrize("row", read_table("forkserve_results_table.txt"), ids=lambda r: r[0])
+def test_forkserve_scenarios_match_model(row):
+    L, k, ell, fs = int(row[1]), int(row[2]), int(row[3]), int(row[5])
+    lp, pm = _pair(1 << 15, 1 << 16)
+    names = _replay_both(lp, pm, fanout_ops(L, k, ell))
+    _same_state(lp, pm, list(names.values()))
+    assert lp.stats()["live_bpages"] == fs
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_operations_match_model(seed):
+    rng = np.random.default_rng(1000 + seed)
+    nb, nr = 40, 56
+    lp, pm = _pair(nb, nr, rng.permutation(nb), rng.permutation(nr))
+    live = []
+    for step in range(250):
+        op = int(rng.integers(0, 5))
+        if op == 0 or not live:
+            res = bool(rng.integers(0, 2))
+            h = lp.create(res)
+            assert h == pm.create(res)
+            live.append(h)
+        elif op in (1, 2):
+            h = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 37))
+            try:
+                exp = pm.append(h, n)
+            except PoolError as e:
+                with pytest.raises(fk.ForkKVError) as ei:
+                    lp.append(h, n)
+                assert ei.value.code == fk.ENOMEM and e.kind == "ENOMEM"
+            else:
+                got = lp.append(h, n)
+                assert (got[0], got[1], got[2]) == (exp[0], exp[1], exp[2])
+        elif op == 3:
+            h = live[int(rng.integers(len(live)))]
+            alias = int(rng.integers(0, pm.length(h) + 1))
+            try:
+                exp = pm.fork(h, alias)
+            except PoolError as e:
+                with pytest.raises(fk.ForkKVError) as ei:
+                    lp.fork(h, alias)
+                assert ei.value.code == fk.ENOMEM and e.kind == "ENOMEM"
+            else:
+                assert lp.fork(h, alias) == exp
+                live.append(exp[0])
+        else:
+            h = live.pop(int(rng.integers(len(live))))
+            lp.free(h)
+            pm.free(h)
+        _same_state(lp, pm, live)
+
+
+def test_error_codes():
+    lp = fk.Pool(4, 4, 1, 8, 4, "f32")
+    h = lp.create(True)
+    lp.append(h, 40)
+    with pytest.raises(fk.ForkKVError) as e:
+        lp.append(h, 30)
+    assert e.value.code == fk.ENOMEM
+    with pytest.raises(fk.ForkKVError) as e:
+        lp.fork(h, 41)
+    assert e.value.code == fk.EINVAL
+    with pytest.raises(fk.ForkKVError) as e:
+        lp.append(h, -1)
+    assert e.value.code == fk.EINVAL
+    lp.free(h)
+    with pytest.raises(fk.ForkKVError) as e:
+        lp.free(h)
+    assert e.value.code == fk.EINVAL
+    with pytest.raises(fk.ForkKVError) as e:
+        fk.Pool(4, 4, 1, 8, 4, "f32", bpage_order=[0, 1, 1, 2])
+    assert e.value.code == fk.EINVAL
+    with pytest.raises(fk.ForkKVError):
+        fk.Pool(4, 4, 1, 7, 4, "f32")          # odd head_dim
+    # device call on a host-only pool
+    with pytest.raises(fk.ForkKVError) as e:
+        lp.cow_copy([(0, 1, 3)], stream=type("S", (), {"cuda_stream": 0})())
+    assert e.value.code == fk.ESTATE
+
+
+# ---- decode plan validity ------------------------------------------------------------------
+
+def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
+    blob = plan.blob()
+    n_agents, n_items, n_slots = blob[1], blob[2], blob[3]
+    off_items, off_lens, off_ptr, off_list = blob[6], blob[7], blob[8], blob[9]
+    bt, rt, lens = pm_tables
+    assert n_agents == len(handles)
+    assert blob[off_lens:off_lens + n_agents] == list(lens)
+    covered = {}
+    slots_seen = set()
+    per_agent = {a: [] for a in range(n_agents)}
+    for i in range(n_items):
+        it = blob[off_items + i * ITEM_INTS: off_items + (i + 1) * ITEM_INTS]
+        lp0, npg, na, sb = it[:4]
+        agents = it[4:4 + na]
+        assert 1 <= na <= group_cap and npg >= 1 and agents == sorted(agents)
+        for j, a in enumerate(agents):
+            assert sb + j not in slots_seen
+            slots_seen.add(sb + j)
+            per_agent[a].append(sb + j)
+        for lpg in range(lp0, lp0 + npg):
+            pages = {bt[a][lpg] for a in agents}
+            assert len(pages) == 1 and -1 not in pages
+            for a in agents:
+                assert (a, lpg) not in covered
+                covered[(a, lpg)] = i
+    want = {(a, lpg) for a in range(n_agents) for lpg in range(-(-lens[a] // 16))}
+    assert set(covered) == want
+    # pages aliased by several agents are never split across items of the same agent chunk
+    for a in range(n_agents):
+        ptr0, ptr1 = blob[off_ptr + a], blob[off_ptr + a + 1]
+        assert sorted(blob[off_list + ptr0: off_list + ptr1]) == sorted(per_agent[a])
+    assert slots_seen == set(range(n_slots))
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+@pytest.mark.parametrize("kernel", [fk.KERNEL_GENERIC])
+def test_plan_covers_workloads(idx, kernel):
+    cfg = CONFIGS[idx]
+    lp = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim, cfg.rank,
+                 cfg.dtype)
+    ops, agents = pool_ops(cfg)
+    names, _ = lp.replay(ops)
+    hs = [names[a] for a in agents]
+    plan = fk.Plan(lp, hs, cfg.num_q_heads, kernel=kernel)
+    mp = -(-cfg.seq_len // 16)
+    _check_plan(lp, lp.tables(hs, mp), hs, plan, 8)
+    # shared pages are read once per agent chunk, not once per agent
+    blob = plan.blob()
+    shared_items = [blob[16 + i * ITEM_INTS + 2] for i in range(blob[2])]
+    assert max(shared_items) == min(cfg.agents_per_session, 8 if kernel == fk.KERNEL_GENERIC else 4)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("cap,ppi", [(0, 0), (2, 1), (3, 5)])
+def test_plan_random_topologies(seed, cap, ppi):
+    from tests.cases import random_ops
+    rng = np.random.default_rng(2000 + seed)
+    ops, agents = random_ops(rng, 5, max_prefix=90, max_suffix=50)
+    lp = fk.Pool(128, 128, 2, 8, 4, "f32", rng.permutation(128), rng.permutation(128))
+    names, _ = lp.replay(ops)
+    hs = [names[a] for a in agents]
+    plan = fk.Plan(lp, hs, 4, kernel=fk.KERNEL_GENERIC, max_agents_per_item=cap, pages_per_item=ppi)
+    _check_plan(lp, lp.tables(hs, 16), hs, plan, cap if cap else 8)
+
+
+def test_plan_rejects_base_only_and_bad_heads():
+    lp = fk.Pool(8, 8, 2, 8, 4, "f32")
+    root = lp.create(False)
+    lp.append(root, 20)
+    with pytest.raises(fk.ForkKVError):
+        fk.Plan(lp, [root], 4)
+    c, _ = lp.fork(root, 20)
+    with pytest.raises(fk.ForkKVError):
+        fk.Plan(lp, [c], 3)
+    p = fk.Plan(lp, [], 4)
+    assert p.info["n_items"] == 0

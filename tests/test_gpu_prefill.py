@@ -1,0 +1,102 @@
+"""Chunked-prefill parity on the GPU: rows written bit-exactly, attention vs the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from lora_shared_prefix_amd.session import DeviceBatch, to_device, workload_geom  # noqa: E402
+from oracle.attention import Geometry, apply_chunk_write, prefill_attention  # noqa: E402
+from tests.cases import encode, tiny_case  # noqa: E402
+from tests.gpu_common import assert_close, errors, gpu_values, model_tables  # noqa: E402
+from workloads import CONFIGS, chunk_ops, draw_inputs, pool_ops  # noqa: E402
+
+
+def _host(t, dtype):
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if dtype == "bf16" else a
+
+
+def _run(geom, arrays, ops, agents, perm_b, perm_r, C, s, sm, theta, samples=None):
+    b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
+    pool_before = (arrays["bpool"], arrays["rpool"])
+    start = b.reserve_chunk(C)
+    chunk = {k: to_device(arrays[k]) for k in ("q", "k_new", "v_new", "rk_new", "rv_new")}
+    out = b.prefill(chunk, s, sm, theta)
+    torch.cuda.synchronize()
+    dtype = geom["dtype"]
+    g = Geometry(page_size=16, num_q_heads=geom["num_q_heads"], num_kv_heads=geom["num_kv_heads"],
+                 head_dim=geom["head_dim"], rank=geom["rank"], dtype=dtype)
+    # oracle-side bookkeeping, then the expected pool contents after the write
+    pm, hs, _, _, _ = model_tables(geom["num_bpages"], geom["num_rpages"], perm_b, perm_r, ops,
+                                   agents, b.max_pages)
+    for h in hs:
+        pm.append(h, C)
+    bt, rt, _ = pm.tables(hs, b.max_pages)
+    bt, rt = np.array(bt, dtype=np.int32), np.array(rt, dtype=np.int32)
+    assert np.array_equal(bt, b.btab_host) and np.array_equal(rt, b.rtab_host)
+    ref = prefill_attention(g, pool_before[0], pool_before[1], bt, rt, np.array(start),
+                            arrays["q"], arrays["k_new"], arrays["v_new"], arrays["rk_new"],
+                            arrays["rv_new"], arrays["Bk"], arrays["Bv"], s, sm, theta,
+                            samples=samples)
+    return b, out, ref, bt, rt, start, g
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_tiny_prefill(seed, dtype):
+    C = [5, 16, 23][seed]
+    d, r = [(8, 3), (64, 8), (128, 16)][seed]
+    case = tiny_case(900 + seed, dtype, Hq=8, Hkv=2, d=d, r=r, n_agents=3, chunk=C,
+                     max_prefix=60, max_suffix=20)
+    case["ops"] = [op if op[0] != "fork" else (op[0], op[1], (op[2] // 16) * 16, op[3])
+                   for op in case["ops"]]
+    geom = dict(num_bpages=64, num_rpages=64, num_kv_heads=2, num_q_heads=8, head_dim=d, rank=r,
+                dtype=dtype)
+    print(f"[gpu-prefill] tiny seed={seed} {dtype} C={C} d={d} r={r}", flush=True)
+    b, out, ref, bt, rt, start, g = _run(geom, case, case["ops"], case["agents"], case["perm_b"],
+                                         case["perm_r"], C, case["lora_scale"], case["sm_scale"],
+                                         case["theta"])
+    exp_b, exp_r = apply_chunk_write(g, case["bpool"], case["rpool"], bt, rt, start,
+                                     case["k_new"], case["v_new"], case["rk_new"], case["rv_new"])
+    # written rows are bit-exact and no other pool byte changed
+    assert np.array_equal(_host(b.bcache, dtype).view(np.uint8), exp_b.view(np.uint8))
+    assert np.array_equal(_host(b.rcache, dtype).view(np.uint8), exp_r.view(np.uint8))
+    gv = gpu_values(out, dtype)
+    assert_close(gv, ref, f"prefill tiny seed={seed} {dtype}", scale_abs=True)
+    if dtype == "f32":
+        assert errors(gv, ref)[1] < 1e-5
+
+
+def test_qwen3_shape_scaled_prefill():
+    """Qwen3-8B attention shape (32/8 heads, d=128, r=16, theta 1e6) at a reduced prefix."""
+    rng = np.random.default_rng(44)
+    N, L, C = 3, 1000, 77
+    nb, nr = 512, 512
+    geom = dict(num_bpages=nb, num_rpages=nr, num_kv_heads=8, num_q_heads=32, head_dim=128,
+                rank=16, dtype="bf16")
+    arrays = dict(bpool=encode(rng.standard_normal((nb, 2, 8, 2048)), "bf16"),
+                  rpool=encode(rng.standard_normal((nr, 2, 256)), "bf16"),
+                  q=encode(rng.standard_normal((N, C, 32, 128)), "bf16"),
+                  k_new=encode(rng.standard_normal((N, C, 8, 128)), "bf16"),
+                  v_new=encode(rng.standard_normal((N, C, 8, 128)), "bf16"),
+                  rk_new=encode(rng.standard_normal((N, C, 16)), "bf16"),
+                  rv_new=encode(rng.standard_normal((N, C, 16)), "bf16"),
+                  Bk=encode(0.02 * rng.standard_normal((N, 16, 1024)), "bf16"),
+                  Bv=encode(0.02 * rng.standard_normal((N, 16, 1024)), "bf16"))
+    ops = [("create", "root", 0), ("append", "root", L)]
+    ops += [("fork", "root", 992, f"a{j}") for j in range(N)]
+    ops += [("append", f"a{j}", 8 * j) for j in range(N)]
+    agents = [f"a{j}" for j in range(N)]
+    samples = [(a, i, g) for a in range(N) for i in (0, 1, 40, C - 1) for g in (0, 13, 31)]
+    b, out, ref, *_ = _run(geom, arrays, ops, agents, rng.permutation(nb), rng.permutation(nr),
+                           C, 2.0, 1 / np.sqrt(128), 1e6, samples=samples)
+    gv = gpu_values(out, "bf16")
+    idx = tuple(np.array(samples).T)
+    assert np.all(np.isfinite(gv))
+    assert_close(gv[idx], ref[idx], "qwen3-shape scaled prefill")
