@@ -26,6 +26,8 @@ CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}",
             # packed fp32 VALU ops stay off on this target
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in ordinary VGPRs: the decode kernel post-processes them on VALU
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-parameter"]
 
 

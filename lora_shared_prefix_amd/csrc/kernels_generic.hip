@@ -342,34 +342,84 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
 
 // Split-K merge with a log-sum-exp rule, then the one-time B_v up-projection:
 // o = (sum_i w_i acc_i + s * (sum_i w_i acc_r,i) B_v) / sum_i w_i l_i, w_i = 2^(m_i - M).
+// One block per output row (agent, q head); the row's partial slots are split over the
+// four waves, each lane summing up to four dimensions; weights are broadcast from LDS.
+constexpr int kCombineChunk = 512;  // slots whose weights sit in LDS at once
+
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
   using E = Elem<T>;
+  __shared__ float s_w[kCombineChunk];
+  __shared__ int s_slot[kCombineChunk];
+  __shared__ float s_red[256];
+  __shared__ float s_acc[4][256];
+  __shared__ float s_accr[4][64];
   __shared__ float s_ar[64];
   const int a = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int d = p.head_dim, r = p.rank, Hq = p.num_q_heads, h = g / p.group;
   const int n = p.num_kv_heads * d;
   const int s0 = p.plan[p.off_slot_ptr + a], s1 = p.plan[p.off_slot_ptr + a + 1];
   const int32_t* slots = p.plan + p.off_slot_list;
+
+  // global max of the partial maxima
   float M = -INFINITY;
-  for (int i = s0; i < s1; ++i) M = fmaxf(M, p.ws_ml[(size_t(slots[i]) * Hq + g) * 2]);
-  float Lsum = 0.f;
-  float A = 0.f, Ar = 0.f;
-  for (int i = s0; i < s1; ++i) {
-    const size_t row = size_t(slots[i]) * Hq + g;
-    const float m = p.ws_ml[row * 2];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    Lsum += w * p.ws_ml[row * 2 + 1];
-    if (tid < d) A += w * p.ws_acc[row * d + tid];
-    if (tid < r) Ar += w * p.ws_accr[row * r + tid];
+  for (int i = s0 + tid; i < s1; i += 256) M = fmaxf(M, p.ws_ml[(size_t(slots[i]) * Hq + g) * 2]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) s_red[tid] = fmaxf(s_red[tid], s_red[tid + st]);
+    __syncthreads();
   }
-  if (tid < r) s_ar[tid] = Ar;
+  M = s_red[0];
+  __syncthreads();
+
+  float lsum = 0.f;
+  float A[4] = {0.f, 0.f, 0.f, 0.f};
+  float Ar = 0.f;
+  for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, s1 - c0);
+    for (int i = tid; i < cn; i += 256) {
+      const int sl = slots[c0 + i];
+      const size_t row = size_t(sl) * Hq + g;
+      const float m = p.ws_ml[row * 2];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      s_w[i] = w;
+      s_slot[i] = sl;
+      lsum += w * p.ws_ml[row * 2 + 1];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = wv; i < cn; i += 4) {
+      const float w = s_w[i];
+      const size_t row = size_t(s_slot[i]) * Hq + g;
+      const float* src = p.ws_acc + row * d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (lane + 64 * e < d) A[e] += w * src[lane + 64 * e];
+      if (lane < r) Ar += w * p.ws_accr[row * r + lane];
+    }
+    __syncthreads();
+  }
+  // reduce over the four waves
+  for (int e = 0; e < 4; ++e)
+    if (lane + 64 * e < d) s_acc[wv][lane + 64 * e] = A[e];
+  if (lane < r) s_accr[wv][lane] = Ar;
+  s_red[tid] = lsum;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) s_red[tid] += s_red[tid + st];
+    __syncthreads();
+  }
+  const float Lsum = s_red[0];
+  if (tid < r) s_ar[tid] = s_accr[0][tid] + s_accr[1][tid] + s_accr[2][tid] + s_accr[3][tid];
   __syncthreads();
   if (tid < d) {
+    const float acc = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
     const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + tid;
     float res = 0.f;
     for (int k = 0; k < r; ++k) res += s_ar[k] * E::ld(bv, size_t(k) * n);
-    const float o = Lsum > 0.f ? (A + p.lora_scale * res) / Lsum : 0.f;
+    const float o = Lsum > 0.f ? (acc + p.lora_scale * res) / Lsum : 0.f;
     E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + tid, o);
   }
 }

@@ -1,20 +1,449 @@
-// MFMA (matrix-core) ResidualAttention kernels for gfx950.
+// MFMA (matrix-core) ResidualAttention decode kernel for gfx950: bf16 storage, d = 128,
+// r = 16, page size 16, up to 16 query columns (agents x GQA group) per wave.
+//
+// ForkKV study note, "7. 实现 cross-reference" (kernel; core barriers (1) and (2)) and
+// "4. 作者证明" (Eq.(4), reproduction checks 3, 4 and 6): for each page the key of every
+// aliasing agent is rebuilt on chip as bK + RoPE(s * rK B_k) -- RoPE after the
+// up-projection -- and the value path keeps a rank-r accumulator acc_r, rescaled with the
+// base accumulator, so that B_v is applied once, after the loop (combine kernel).
+//
+// Work layout (one workgroup = one KV head x one plan item = a run of logical pages that
+// all the item's agents map to the same physical base pages):
+//   * the base key/value tile of a page is loaded once per agent group and scored for all
+//     the group's agents and GQA heads: S_base = bK Q^T is one MFMA tile for all of them;
+//   * the residual key rK B_k is an MFMA (K = rank = 16) per agent and page; its result
+//     lands with the RoPE partners (dims j and j + 64) in the same lane, so the deferred
+//     rotation is applied in registers; S_a = S_base + RoPE(K_res,a) Q^T (MFMA again);
+//   * online softmax per query column with wave shuffles for the max and sum;
+//   * acc^T += bV^T P^T (shared by the group) and acc_r^T += rV_a^T P_a^T (per agent);
+//   * waves split the item's agents into groups and its pages into sub-ranges; partial
+//     states of one group are merged in LDS with the log-sum-exp rule, then written as
+//     one split-K partial per (item, agent, q head).
+//
+// MFMA lane layouts used (checked on gfx950): for a 16x16xK instruction lane l supplies
+// A[l % 16][kpl * (l / 16) + e] and B[kpl * (l / 16) + e][l % 16] (kpl = K / 4) and
+// receives D[4 * (l / 16) + i][l % 16].
 #include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
 
 #include "forkkv_internal.h"
 
 namespace forkkv {
+namespace {
 
-bool mfma_supported(int dtype, int head_dim, int rank, int group) {
-  (void)dtype; (void)head_dim; (void)rank; (void)group;
-  return false;
+typedef short s4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int kD = 128;       // head dim
+constexpr int kR = 16;        // rank
+constexpr int kWaves = 4;     // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTrigPad = 68;  // padded row of the static in-page trig table (floats)
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+
+// LDS layout (bytes)
+constexpr int kBkBytes = kItemAgents * 8 * 64 * 8;      // [agent][tile][lane][4 bf16]
+constexpr int kTrigBytes = 2 * kPage * kTrigPad * 4;    // cos, sin: [c][j] (scaled by s)
+constexpr int kPageTrigBytes = kWaves * 2 * 64 * 4;     // per wave: cos[64], sin[64]
+constexpr int kMergeFloats = 4 + 32 + 4;                // m, l, pad, pad | acc[32] | accr[4]
+constexpr int kMergeBytes = kWaves * 64 * kMergeFloats * 4;
+constexpr int kBkRawBytes = kItemAgents * kR * kD * 2;  // B_k rows before the permutation
+constexpr int kLdsMain = kBkBytes + (kTrigBytes + kPageTrigBytes > kBkRawBytes
+                                         ? kTrigBytes + kPageTrigBytes : kBkRawBytes);
+constexpr int kLdsBytes = kLdsMain > kMergeBytes ? kLdsMain : kMergeBytes;
+
+__device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma32(bf8 a, bf8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-int mfma_group_agents(int group) { return group > 0 ? 16 / group : 0; }
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const fl2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf2));
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+union U4 {
+  uint4 u;
+  bf8 b;
+};
+union U2 {
+  uint2 u;
+  s4 s;
+};
+
+// Dimension held by reconstruction tile T, row m (a permutation of 0..127 chosen so that
+// (a) tiles T and T + 4 hold the RoPE partners j and j + 64 at the same row, and (b) the
+// lane that receives rows 4g..4g+3 of tiles 2c, 2c+1 holds dims 32c + 8g .. 32c + 8g + 7,
+// i.e. exactly the natural-order K slice it must supply to the 16x16x32 score MFMA.
+__device__ __forceinline__ int perm_dim(int T, int m) {
+  return 32 * (T >> 1) + 8 * (m >> 2) + 4 * (T & 1) + (m & 3);
+}
+
+template <int A, bool kPipe>  // agents per group (columns = agents x G <= 16); prefetch
+__global__ void __launch_bounds__(kThreads)
+decode_mfma_kernel(DecodeParams p, int n_items) {
+  __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  const int Hkv = p.num_kv_heads;
+  // XCD-aware block order: consecutive blocks run on different XCDs (round robin), so the
+  // KV heads of one item are given block ids that share an XCD (and its L2), where the
+  // residual pages -- common to all heads -- are then fetched once.
+  const int b = blockIdx.x;
+  const int xcd = b & 7, s = b >> 3;
+  const int h = s % Hkv;
+  const int item = xcd + 8 * (s / Hkv);
+  if (item >= n_items) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
+  const int col = lane & 15, g4 = lane >> 4;
+  const int G = p.group, Hq = p.num_q_heads;
+  const int32_t* it = p.plan + p.off_items + item * kItemInts;
+  const int lp0 = it[0], np = it[1], na = it[2], slot_base = it[3];
+  const int n_groups = (na + A - 1) / A;
+  const int n_sub = kWaves / n_groups;  // >= 1 (the plan keeps na <= 4A)
+  const int gi = w % n_groups, si = w / n_groups;
+  const bool active = si < n_sub;
+  const int j0 = gi * A;
+  const int na_g = min(A, na - j0);
+
+  const uint16_t* bcache = static_cast<const uint16_t*>(p.bcache);
+  const uint16_t* rcache = static_cast<const uint16_t*>(p.rcache);
+  const uint16_t* Bk = static_cast<const uint16_t*>(p.Bk);
+  const uint16_t* q = static_cast<const uint16_t*>(p.q);
+  const int n = Hkv * kD;
+
+  uint2* bkl = reinterpret_cast<uint2*>(lds);                          // [j][T][lane]
+  float* trig_c = reinterpret_cast<float*>(lds + kBkBytes);            // [c][kTrigPad]
+  float* trig_s = trig_c + kPage * kTrigPad;
+  float* ptrig = reinterpret_cast<float*>(lds + kBkBytes + kTrigBytes) + w * 128;
+
+  // ---- stage B_k slices (A-operand order) and the in-page trig table ----------------------
+  // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
+  // trig-table area (filled only afterwards), then permute into the MFMA A-operand order.
+  {
+    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + kBkBytes);
+    for (int x = tid; x < na * kR * (kD / 8); x += kThreads) {  // 16-byte pieces
+      const int jj = x / (kR * 16), k = (x / 16) % kR, piece = x % 16;
+      const int a = it[4 + jj];
+      *reinterpret_cast<uint4*>(raw + (jj * kR + k) * kD + 8 * piece) =
+          *reinterpret_cast<const uint4*>(Bk + (size_t(a) * kR + k) * n + h * kD + 8 * piece);
+    }
+    __syncthreads();
+    for (int x = tid; x < na * 8 * 64; x += kThreads) {
+      const int jj = x / (8 * 64), T = (x / 64) % 8, l = x % 64;
+      const int dim = perm_dim(T, l & 15);
+      const uint16_t* src = raw + jj * kR * kD + dim;
+      const int k0 = 4 * (l >> 4);
+      uint2 v;
+      v.x = uint32_t(src[k0 * kD]) | (uint32_t(src[(k0 + 1) * kD]) << 16);
+      v.y = uint32_t(src[(k0 + 2) * kD]) | (uint32_t(src[(k0 + 3) * kD]) << 16);
+      bkl[x] = v;
+    }
+    __syncthreads();
+  }
+  const double omega = pow(static_cast<double>(p.rope_theta), -2.0 * lane / kD);  // j = lane
+  for (int x = tid; x < kPage * 64; x += kThreads) {
+    const int c = x / 64, j = x % 64;
+    const double wj = pow(static_cast<double>(p.rope_theta), -2.0 * j / kD);
+    double sv, cv;
+    sincos(c * wj, &sv, &cv);
+    trig_c[c * kTrigPad + j] = static_cast<float>(cv) * p.lora_scale;
+    trig_s[c * kTrigPad + j] = static_cast<float>(sv) * p.lora_scale;
+  }
+  __syncthreads();
+
+  // ---- this wave's query columns ----------------------------------------------------------
+  const int jc = col / G;                   // agent (within group) of this lane's column
+  const bool col_ok = active && col < na_g * G;
+  const int a_col = col_ok ? it[4 + j0 + jc] : 0;
+  const int len_col = col_ok ? p.plan[p.off_lens + a_col] : 0;
+  bf8 qv[4];
+  {
+    const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
+    for (int c = 0; c < 4; ++c) {
+      U4 t;
+      t.u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
+      qv[c] = t.b;
+    }
+  }
+  int agent[A], rlen[A];
+  for (int j = 0; j < A; ++j) {
+    agent[j] = (active && j < na_g) ? it[4 + j0 + j] : 0;
+    rlen[j] = (active && j < na_g) ? p.plan[p.off_lens + agent[j]] : 0;
+  }
+  const float qscale = p.sm_scale_log2;
+
+  f4 acc[8];
+  for (int t = 0; t < 8; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 accr = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int pps = (np + n_sub - 1) / n_sub;
+  const int lpa = active ? lp0 + si * pps : 0;
+  const int lpb = active ? min(lp0 + np, lpa + pps) : 0;
+  const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
+
+  // Page buffers: the loads of page lp + 1 are issued before page lp is computed
+  // (software pipelining; two register buffers, used alternately).
+  struct PageBuf {
+    U4 kt[4];
+    U2 vt[8];
+    U2 rk[A], rv[A];
+    bool ok;
+  };
+  auto load_page = [&](int lp, PageBuf& B) {
+    const int bp = p.btab[size_t(agent[0]) * p.max_pages + lp];
+    B.ok = bp >= 0 && bp < p.num_bpages;  // never read outside the pool
+    const size_t pg = B.ok ? bp : 0;
+    const uint16_t* kt_base = bcache + (pg * 2 * Hkv + h) * tile;
+    const uint16_t* vt_base = bcache + (pg * 2 * Hkv + Hkv + h) * tile;
+    for (int c = 0; c < 4; ++c)
+      B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + col * kD + 32 * c + 8 * g4);
+    for (int t = 0; t < 8; ++t)
+      B.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + (16 * t + col) * kPage + 4 * g4);
+    for (int j = 0; j < A; ++j) {
+      const int rp = j < na_g ? p.rtab[size_t(agent[j]) * p.max_pages + lp] : -1;
+      const bool ok = rp >= 0 && rp < p.num_rpages;
+      const uint16_t* rb = rcache + size_t(ok ? rp : 0) * 2 * kPage * kR;
+      B.rk[j].u = *reinterpret_cast<const uint2*>(rb + col * kR + 4 * g4);
+      B.rv[j].u = *reinterpret_cast<const uint2*>(rb + kPage * kR + col * kPage + 4 * g4);
+      if (!ok) {
+        B.rk[j].u = make_uint2(0, 0);
+        B.rv[j].u = make_uint2(0, 0);
+      }
+    }
+  };
+
+  auto compute_page = [&](int lp, PageBuf& B) {
+    if (!B.ok) return;
+    int vrows = 0;
+    for (int j = 0; j < A; ++j)
+      if (j < na_g) vrows = max(vrows, min(kPage, rlen[j] - lp * kPage));
+    // Rows no column may read are zeroed: their bytes are arbitrary (even NaN).
+    const bool row_ok = col < vrows;  // this lane's key row (tok = col) in the A operands
+    const int tv = vrows - 4 * g4;    // valid tokens among this lane's 4 (B / V operands)
+    auto mask4 = [&](uint2 v) {
+      if (tv < 4) {
+        if (tv <= 0) v.x = 0;
+        else if (tv == 1) v.x &= 0xffffu;
+        if (tv <= 2) v.y = 0;
+        else if (tv == 3) v.y &= 0xffffu;
+      }
+      return v;
+    };
+    if (!row_ok) {
+      for (int c = 0; c < 4; ++c) B.kt[c].u = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < A; ++j) B.rk[j].u = make_uint2(0, 0);
+    }
+    if (tv < 4) {
+      for (int t = 0; t < 8; ++t) B.vt[t].u = mask4(B.vt[t].u);
+      for (int j = 0; j < A; ++j) B.rv[j].u = mask4(B.rv[j].u);
+    }
+
+    // -- RoPE angles of this page: lane j computes t0 * omega_j, reduced in fp64 --
+    {
+      double ang = static_cast<double>(lp * kPage) * omega;
+      ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
+      float sv, cv;
+      sincosf(static_cast<float>(ang), &sv, &cv);
+      ptrig[lane] = cv;
+      ptrig[64 + lane] = sv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes above have landed
+    float ct[16], st[16];  // pair 8*half + 4*(T&1) + i  <->  j = 32*half + 8*g4 + 4*(T&1) + i
+    for (int half = 0; half < 2; ++half) {
+      const int jb = 32 * half + 8 * g4;
+      for (int e = 0; e < 8; ++e) {
+        const float c0 = ptrig[jb + e], s0 = ptrig[64 + jb + e];
+        const float cc = trig_c[col * kTrigPad + jb + e], ss = trig_s[col * kTrigPad + jb + e];
+        ct[8 * half + e] = c0 * cc - s0 * ss;  // s * cos((t0 + c) w_j)
+        st[8 * half + e] = s0 * cc + c0 * ss;  // s * sin((t0 + c) w_j)
+      }
+    }
+
+    // -- scores: shared base tile, then per agent the rotated residual --
+    f4 sb = f4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) sb = mfma32(B.kt[c].b, qv[c], sb);
+    f4 ssel = sb;
+    for (int j = 0; j < A; ++j) {
+      if (j >= na_g) break;
+      const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
+      U4 kr[4];
+      for (int half = 0; half < 2; ++half) {
+        // tiles T = 2half, 2half+1 (chunk half) and their partners T + 4 (chunk half + 2)
+        f4 d[4];
+        const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
+        for (int u = 0; u < 4; ++u) {
+          U2 a;
+          a.u = bkj[Ts[u] * 64];
+          d[u] = mfma16(a.s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
+        }
+        for (int u = 0; u < 2; ++u) {
+          for (int i = 0; i < 4; ++i) {
+            const float x = d[u][i], y = d[u + 2][i];
+            const float c = ct[8 * half + 4 * u + i], sn = st[8 * half + 4 * u + i];
+            d[u][i] = x * c - y * sn;
+            d[u + 2][i] = y * c + x * sn;
+          }
+        }
+        kr[half].u = make_uint4(pack_bf16x2(d[0][0], d[0][1]), pack_bf16x2(d[0][2], d[0][3]),
+                                pack_bf16x2(d[1][0], d[1][1]), pack_bf16x2(d[1][2], d[1][3]));
+        kr[half + 2].u = make_uint4(pack_bf16x2(d[2][0], d[2][1]), pack_bf16x2(d[2][2], d[2][3]),
+                                    pack_bf16x2(d[3][0], d[3][1]), pack_bf16x2(d[3][2], d[3][3]));
+      }
+      f4 sj = sb;
+      for (int c = 0; c < 4; ++c) sj = mfma32(kr[c].b, qv[c], sj);
+      if (jc == j) ssel = sj;
+    }
+
+    // -- online softmax over this page's 16 keys, per column (log2 domain) --
+    float sc[4];
+    float pmax = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int pos = lp * kPage + 4 * g4 + i;
+      sc[i] = (col_ok && pos < len_col) ? ssel[i] * qscale : -INFINITY;
+      pmax = fmaxf(pmax, sc[i]);
+    }
+    pmax = fmaxf(pmax, shfl_xor(pmax, 16));
+    pmax = fmaxf(pmax, shfl_xor(pmax, 32));
+    const float m_new = fmaxf(m_run, pmax);
+    float alpha = 1.f;
+    float pr[4];
+    if (m_new == -INFINITY) {
+      for (int i = 0; i < 4; ++i) pr[i] = 0.f;
+    } else {
+      // arguments are <= 0; v_exp_f32 flushes results below 2^-126 to zero, which only
+      // drops probabilities that are negligible next to the running maximum's 1.0
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+    }
+    l_run = l_run * alpha + (pr[0] + pr[1] + pr[2] + pr[3]);
+    m_run = m_new;
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    accr *= alpha;
+
+    U2 pb;
+    pb.u = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+    for (int t = 0; t < 8; ++t) acc[t] = mfma16(B.vt[t].s, pb.s, acc[t]);
+    for (int j = 0; j < A; ++j) {
+      if (j >= na_g) break;
+      U2 pj;
+      pj.u = (jc == j) ? pb.u : make_uint2(0, 0);
+      accr = mfma16(B.rv[j].s, pj.s, accr);
+    }
+  };
+
+  if constexpr (kPipe) {
+    PageBuf buf0, buf1;
+    if (lpa < lpb) load_page(lpa, buf0);
+    for (int lp = lpa; lp < lpb; lp += 2) {
+      if (lp + 1 < lpb) load_page(lp + 1, buf1);
+      compute_page(lp, buf0);
+      if (lp + 1 >= lpb) break;
+      if (lp + 2 < lpb) load_page(lp + 2, buf0);
+      compute_page(lp + 1, buf1);
+    }
+  } else {
+    for (int lp = lpa; lp < lpb; ++lp) {
+      PageBuf buf;
+      load_page(lp, buf);
+      compute_page(lp, buf);
+    }
+  }
+
+  // ---- merge the sub-range partials of each group (LSE rule), write split-K partials ----
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  __syncthreads();  // LDS is reused for the merge
+  float* mb = reinterpret_cast<float*>(lds) + (w * 64 + lane) * kMergeFloats;
+  mb[0] = m_run;
+  mb[1] = l_run;
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 4; ++i) mb[4 + 4 * t + i] = acc[t][i];
+  for (int i = 0; i < 4; ++i) mb[36 + i] = accr[i];
+  __syncthreads();
+  if (!active || si != 0) return;
+  for (int o = 1; o < n_sub; ++o) {
+    const float* ob = reinterpret_cast<float*>(lds) + ((gi + o * n_groups) * 64 + lane) * kMergeFloats;
+    const float m2 = ob[0];
+    const float M = fmaxf(m_run, m2);
+    if (M == -INFINITY) continue;
+    const float w1 = exp2f(m_run - M), w2 = exp2f(m2 - M);
+    l_run = l_run * w1 + ob[1] * w2;
+    for (int t = 0; t < 8; ++t)
+      for (int i = 0; i < 4; ++i) acc[t][i] = acc[t][i] * w1 + ob[4 + 4 * t + i] * w2;
+    for (int i = 0; i < 4; ++i) accr[i] = accr[i] * w1 + ob[36 + i] * w2;
+    m_run = M;
+  }
+  if (!col_ok) return;
+  const size_t row = (size_t(slot_base) + j0 + jc) * Hq + h * G + col % G;
+  for (int t = 0; t < 8; ++t)
+    *reinterpret_cast<float4*>(p.ws_acc + row * kD + 16 * t + 4 * g4) =
+        make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  *reinterpret_cast<float4*>(p.ws_accr + row * kR + 4 * g4) =
+      make_float4(accr[0], accr[1], accr[2], accr[3]);
+  if (g4 == 0) {
+    p.ws_ml[row * 2] = m_run;
+    p.ws_ml[row * 2 + 1] = l_run;
+  }
+}
+
+int agents_per_group(int group) { return group >= 1 && group <= 16 ? min(4, 16 / group) : 0; }
+
+}  // namespace
+
+bool mfma_supported(int dtype, int head_dim, int rank, int group) {
+  return dtype == FORKKV_DTYPE_BF16 && head_dim == kD && rank == kR &&
+         agents_per_group(group) >= 1;
+}
+
+// Agents per plan item: up to four groups of agents_per_group(G) each, at most 8.
+int mfma_group_agents(int group) {
+  const int A = agents_per_group(group);
+  return A > 0 ? min(kItemAgents, kWaves * A) : 0;
+}
 
 bool prefill_mfma_enabled() { return false; }
 
-hipError_t launch_decode_mfma(const DecodeParams&, hipStream_t) { return hipErrorNotSupported; }
+template <bool kPipe>
+hipError_t launch_decode_mfma_t(const DecodeParams& p, hipStream_t s) {
+  const int A = agents_per_group(p.group);
+  const int n_items = p.n_items;
+  const int blocks = 8 * p.num_kv_heads * ((n_items + 7) / 8);
+  switch (A) {
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<2, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<1, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// FORKKV_DECODE_PIPE=1 selects the register-prefetch variant (tuning aid; it needs about
+// 50 more VGPRs, halving occupancy, and measured slower on the decode workloads).
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
+  static const bool pipe = [] {
+    const char* e = std::getenv("FORKKV_DECODE_PIPE");
+    return e && e[0] == '1';
+  }();
+  return pipe ? launch_decode_mfma_t<true>(p, s) : launch_decode_mfma_t<false>(p, s);
+}
 
 hipError_t launch_prefill_mfma(const PrefillParams&, const int32_t*, hipStream_t) {
   return hipErrorNotSupported;
