@@ -22,11 +22,19 @@
  *
  * Storage (caller-owned device memory; the pages leave the layout open)
  * -----------------------------------------------------------------------
- *   bcache: [num_bpages][2][Hkv][P*d] elements.  Plane 0 = key tile, row-major
- *           [row][dim] (post-RoPE).  Plane 1 = value tile, transposed [dim][row].
- *   rcache: [num_rpages][2][P*r] elements.  Plane 0 = key residual [row][k];
- *           plane 1 = value residual, transposed [k][row].
- *   Element type: FORKKV_DTYPE_BF16 (bfloat16) or FORKKV_DTYPE_F32.  P = 16.
+ *   bcache: [num_bpages][2][Hkv][P*d] elements: plane 0 = post-RoPE keys,
+ *           plane 1 = values, one P x d tile per (page, plane, KV head).
+ *   rcache: [num_rpages][2][P*r] elements: plane 0 = key residual, plane 1 =
+ *           value residual, one P x r tile per (page, plane).
+ *   Inside a tile the elements are in the order the gfx950 matrix cores consume
+ *   them, so that every lane's MFMA operand is one contiguous 16- or 8-byte piece
+ *   (row t = position within the page, x = dimension, k = rank):
+ *     key            (t, x): (x / 8) * 128 + t * 8 + x % 8
+ *     value          (t, x): ((x / 16) * 4 + t / 4) * 64 + (x % 16) * 4 + t % 4
+ *     key residual   (t, k): (k / 4) * 64 + t * 4 + k % 4
+ *     value residual (t, k): (t / 4) * (4 * r) + k * 4 + t % 4
+ *   Element type: FORKKV_DTYPE_BF16 (bfloat16) or FORKKV_DTYPE_F32.  P = 16,
+ *   d a multiple of 16 (<= 256), r a multiple of 4 (<= 64).
  *   A slot is page * P + row; position t of a sequence lives in page
  *   table[t / P], row t % P.
  *
@@ -86,8 +94,8 @@ typedef struct {
   int32_t num_rpages;   /* pages in the residual pool */
   int32_t page_size;    /* P; must be 16 */
   int32_t num_kv_heads; /* Hkv */
-  int32_t head_dim;     /* d; even, 2..256 */
-  int32_t rank;         /* r; 1..64 */
+  int32_t head_dim;     /* d; multiple of 16, 16..256 */
+  int32_t rank;         /* r; multiple of 4, 4..64 */
   int32_t dtype;        /* FORKKV_DTYPE_* */
   const int32_t* bpage_order; /* host, nullable: initial base free-list order, a permutation */
   const int32_t* rpage_order; /* host, nullable: initial residual free-list order */

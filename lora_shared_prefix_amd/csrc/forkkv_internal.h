@@ -68,6 +68,20 @@ struct forkkv_plan {
 
 namespace forkkv {
 
+// Element offsets inside the pool tiles (P = 16): the order in which the gfx950 matrix
+// cores consume them, so that each lane's MFMA operand is one contiguous 8- or 16-byte
+// piece at lane * size (see include/forkkv.h, "Storage").
+struct TileOrder {
+  __host__ __device__ static constexpr int key(int t, int x) { return (x / 8) * 128 + t * 8 + x % 8; }
+  __host__ __device__ static constexpr int value(int t, int x) {
+    return ((x / 16) * 4 + t / 4) * 64 + (x % 16) * 4 + t % 4;
+  }
+  __host__ __device__ static constexpr int res_key(int t, int k) { return (k / 4) * 64 + t * 4 + k % 4; }
+  __host__ __device__ static constexpr int res_value(int t, int k, int r) {
+    return (t / 4) * (4 * r) + k * 4 + t % 4;
+  }
+};
+
 // Launch parameters of the decode kernels (passed by value).
 struct DecodeParams {
   const void* q;

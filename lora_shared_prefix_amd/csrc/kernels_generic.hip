@@ -174,9 +174,11 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
       for (int j = 0; j < na; ++j) vrows = max(vrows, min(kPage, limit[j] - lp * kPage));
     }
     for (int i = tid; i < kPage * d; i += kGenericThreads) {
-      sbk[i] = i / d < vrows ? E::ld(bcache, kbase + i) : 0.f;
-      const int dd = i / kPage, row = i % kPage;
-      sbv[row * d + dd] = row < vrows ? E::ld(bcache, vbase + i) : 0.f;
+      // stored tiles are in matrix-core operand order; see TileOrder
+      const int kt = (i % (kPage * 8)) / 8, kx = (i / (kPage * 8)) * 8 + i % 8;
+      sbk[kt * d + kx] = kt < vrows ? E::ld(bcache, kbase + i) : 0.f;
+      const int vt = ((i / 64) % 4) * 4 + i % 4, vx = (i / 256) * 16 + (i % 64) / 4;
+      sbv[vt * d + vx] = vt < vrows ? E::ld(bcache, vbase + i) : 0.f;
     }
     bool rok[kItemAgents];
     for (int j = 0; j < na; ++j) {
@@ -184,10 +186,11 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
       rok[j] = rpg >= 0 && rpg < nrp;
       const size_t rb = size_t(rok[j] ? rpg : 0) * 2 * kPage * r;
       for (int i = tid; i < kPage * r; i += kGenericThreads) {
-        srk[j * kPage * r + i] = (rok[j] && i / r < vrows) ? E::ld(rcache, rb + i) : 0.f;
-        const int k = i / kPage, row = i % kPage;
-        srv[(j * kPage + row) * r + k] =
-            (rok[j] && row < vrows) ? E::ld(rcache, rb + kPage * r + i) : 0.f;
+        const int kt = (i % 64) / 4, kk = (i / 64) * 4 + i % 4;
+        srk[(j * kPage + kt) * r + kk] = (rok[j] && kt < vrows) ? E::ld(rcache, rb + i) : 0.f;
+        const int vt = (i / (4 * r)) * 4 + i % 4, vk = (i % (4 * r)) / 4;
+        srv[(j * kPage + vt) * r + vk] =
+            (rok[j] && vt < vrows) ? E::ld(rcache, rb + kPage * r + i) : 0.f;
       }
     }
     for (int i = tid; i < kPage * half; i += kGenericThreads) {
@@ -342,85 +345,90 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
 
 // Split-K merge with a log-sum-exp rule, then the one-time B_v up-projection:
 // o = (sum_i w_i acc_i + s * (sum_i w_i acc_r,i) B_v) / sum_i w_i l_i, w_i = 2^(m_i - M).
-// One block per output row (agent, q head); the row's partial slots are split over the
-// four waves, each lane summing up to four dimensions; weights are broadcast from LDS.
-constexpr int kCombineChunk = 512;  // slots whose weights sit in LDS at once
+// Grid: (agent * Hq + q head, dimension half).  One pass reads every partial's (m, l)
+// and slot id into LDS; then four waves stream disjoint subsets of the partials, one
+// output dimension per lane, with independent loads in flight.
+constexpr int kCombineChunk = 512;   // partials whose weights sit in LDS at once
+constexpr int kCombineSplit = 2;     // blocks per output row (dimension halves)
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
   using E = Elem<T>;
   __shared__ float s_w[kCombineChunk];
-  __shared__ int s_slot[kCombineChunk];
-  __shared__ float s_red[256];
-  __shared__ float s_acc[4][256];
+  __shared__ int s_row[kCombineChunk];
+  __shared__ float s_red[8];
+  __shared__ float s_acc[4][128];
   __shared__ float s_accr[4][64];
   __shared__ float s_ar[64];
-  const int a = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int row_out = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int d = p.head_dim, r = p.rank, Hq = p.num_q_heads, h = g / p.group;
+  const int d = p.head_dim, r = p.rank, Hq = p.num_q_heads;
+  const int a = row_out / Hq, g = row_out % Hq, h = g / p.group;
   const int n = p.num_kv_heads * d;
+  const int dpb = (d + kCombineSplit - 1) / kCombineSplit;  // dims of this block
+  const int dim0 = part * dpb;
   const int s0 = p.plan[p.off_slot_ptr + a], s1 = p.plan[p.off_slot_ptr + a + 1];
   const int32_t* slots = p.plan + p.off_slot_list;
 
-  // global max of the partial maxima
+  // pass 1: global maximum of the partial maxima
   float M = -INFINITY;
   for (int i = s0 + tid; i < s1; i += 256) M = fmaxf(M, p.ws_ml[(size_t(slots[i]) * Hq + g) * 2]);
-  s_red[tid] = M;
+  M = wave_max(M);
+  if (lane == 0) s_red[wv] = M;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] = fmaxf(s_red[tid], s_red[tid + st]);
-    __syncthreads();
-  }
-  M = s_red[0];
-  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
-  float lsum = 0.f;
-  float A[4] = {0.f, 0.f, 0.f, 0.f};
-  float Ar = 0.f;
+  float lsum = 0.f, Ar = 0.f;
+  float A[2] = {0.f, 0.f};
   for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
     const int cn = min(kCombineChunk, s1 - c0);
+    __syncthreads();
     for (int i = tid; i < cn; i += 256) {
-      const int sl = slots[c0 + i];
-      const size_t row = size_t(sl) * Hq + g;
-      const float m = p.ws_ml[row * 2];
+      const int row = slots[c0 + i] * Hq + g;
+      const float m = p.ws_ml[size_t(row) * 2];
       const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
       s_w[i] = w;
-      s_slot[i] = sl;
-      lsum += w * p.ws_ml[row * 2 + 1];
+      s_row[i] = row;
+      lsum += w * p.ws_ml[size_t(row) * 2 + 1];
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 8
     for (int i = wv; i < cn; i += 4) {
       const float w = s_w[i];
-      const size_t row = size_t(s_slot[i]) * Hq + g;
-      const float* src = p.ws_acc + row * d;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (lane + 64 * e < d) A[e] += w * src[lane + 64 * e];
+      const size_t row = s_row[i];
+      const float* src = p.ws_acc + row * d + dim0;
+      for (int e = 0; e < 2; ++e)
+        if (lane + 64 * e < dpb && dim0 + lane + 64 * e < d) A[e] += w * src[lane + 64 * e];
       if (lane < r) Ar += w * p.ws_accr[row * r + lane];
     }
-    __syncthreads();
   }
-  // reduce over the four waves
-  for (int e = 0; e < 4; ++e)
-    if (lane + 64 * e < d) s_acc[wv][lane + 64 * e] = A[e];
-  if (lane < r) s_accr[wv][lane] = Ar;
-  s_red[tid] = lsum;
+  lsum = wave_sum(lsum);
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) s_red[tid] += s_red[tid + st];
-    __syncthreads();
-  }
-  const float Lsum = s_red[0];
+  if (lane == 0) s_red[4 + wv] = lsum;
+  for (int e = 0; e < 2; ++e)
+    if (lane + 64 * e < dpb) s_acc[wv][lane + 64 * e] = A[e];
+  if (lane < r) s_accr[wv][lane] = Ar;
+  __syncthreads();
+  const float Lsum = s_red[4] + s_red[5] + s_red[6] + s_red[7];
   if (tid < r) s_ar[tid] = s_accr[0][tid] + s_accr[1][tid] + s_accr[2][tid] + s_accr[3][tid];
   __syncthreads();
-  if (tid < d) {
+  if (tid < dpb && dim0 + tid < d) {
+    const int dim = dim0 + tid;
     const float acc = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
-    const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + tid;
+    const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + dim;
     float res = 0.f;
     for (int k = 0; k < r; ++k) res += s_ar[k] * E::ld(bv, size_t(k) * n);
     const float o = Lsum > 0.f ? (acc + p.lora_scale * res) / Lsum : 0.f;
-    E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + tid, o);
+    E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + dim, o);
   }
 }
 
@@ -440,16 +448,16 @@ __global__ void __launch_bounds__(256) prefill_write_kernel(PrefillParams p) {
   if (bpg >= 0 && bpg < p.num_bpages) {
     for (int idx = tid; idx < Hkv * d; idx += blockDim.x) {
       const int h = idx / d, dd = idx % d;
-      bc[(size_t(bpg) * 2 * Hkv + h) * kPage * d + row * d + dd] = kn[idx];
-      bc[(size_t(bpg) * 2 * Hkv + Hkv + h) * kPage * d + dd * kPage + row] = vn[idx];
+      bc[(size_t(bpg) * 2 * Hkv + h) * kPage * d + TileOrder::key(row, dd)] = kn[idx];
+      bc[(size_t(bpg) * 2 * Hkv + Hkv + h) * kPage * d + TileOrder::value(row, dd)] = vn[idx];
     }
   }
   if (rpg >= 0 && rpg < p.num_rpages) {
     const T* rkn = static_cast<const T*>(p.rk_new) + (size_t(a) * C + i) * r;
     const T* rvn = static_cast<const T*>(p.rv_new) + (size_t(a) * C + i) * r;
     for (int k = tid; k < r; k += blockDim.x) {
-      rc[size_t(rpg) * 2 * kPage * r + row * r + k] = rkn[k];
-      rc[size_t(rpg) * 2 * kPage * r + kPage * r + k * kPage + row] = rvn[k];
+      rc[size_t(rpg) * 2 * kPage * r + TileOrder::res_key(row, k)] = rkn[k];
+      rc[size_t(rpg) * 2 * kPage * r + kPage * r + TileOrder::res_value(row, k, r)] = rvn[k];
     }
   }
 }
@@ -462,7 +470,7 @@ __global__ void __launch_bounds__(256) cow_copy_kernel(T* bc, int Hkv, int d, in
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
     const int plane = i / (Hkv * kPage * d);
     const int rem = i % (kPage * d);
-    const int row = plane == 0 ? rem / d : rem % kPage;
+    const int row = plane == 0 ? (rem % (kPage * 8)) / 8 : ((rem / 64) % 4) * 4 + rem % 4;
     if (row < nrows) bc[size_t(dst) * total + i] = bc[size_t(src) * total + i];
   }
 }
@@ -505,8 +513,8 @@ hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agent
 }
 
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s) {
-  if (p.head_dim > 256 || p.rank > 64) return hipErrorInvalidValue;
-  dim3 grid(p.n_agents, p.num_q_heads);
+  if (p.head_dim > 2 * 128 || p.rank > 64) return hipErrorInvalidValue;
+  dim3 grid(p.n_agents * p.num_q_heads, kCombineSplit);
   if (dtype == FORKKV_DTYPE_F32)
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, p);
   else

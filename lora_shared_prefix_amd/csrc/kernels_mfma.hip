@@ -94,7 +94,7 @@ __device__ __forceinline__ int perm_dim(int T, int m) {
 }
 
 template <int A, bool kPipe>  // agents per group (columns = agents x G <= 16); prefetch
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeParams p, int n_items) {
   __shared__ __align__(16) unsigned char lds[kLdsBytes];
   const int Hkv = p.num_kv_heads;
@@ -155,14 +155,17 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     }
     __syncthreads();
   }
-  const double omega = pow(static_cast<double>(p.rope_theta), -2.0 * lane / kD);  // j = lane
+  // w_j = theta^(-2j/d) = 2^(-(2j/d) log2 theta); lane j keeps w_j in fp64 (j = lane)
+  const double log2_theta = log2(static_cast<double>(p.rope_theta));
+  const double omega = exp2(-2.0 * lane / kD * log2_theta);
   for (int x = tid; x < kPage * 64; x += kThreads) {
     const int c = x / 64, j = x % 64;
-    const double wj = pow(static_cast<double>(p.rope_theta), -2.0 * j / kD);
-    double sv, cv;
-    sincos(c * wj, &sv, &cv);
-    trig_c[c * kTrigPad + j] = static_cast<float>(cv) * p.lora_scale;
-    trig_s[c * kTrigPad + j] = static_cast<float>(sv) * p.lora_scale;
+    // in-page offsets c < 16: the angle c * w_j is small and sincosf is accurate there
+    const float ang = static_cast<float>(c * exp2(-2.0 * j / kD * log2_theta));
+    float sv, cv;
+    sincosf(ang, &sv, &cv);
+    trig_c[c * kTrigPad + j] = cv * p.lora_scale;
+    trig_s[c * kTrigPad + j] = sv * p.lora_scale;
   }
   __syncthreads();
 
@@ -197,6 +200,22 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int lpb = active ? min(lp0 + np, lpa + pps) : 0;
   const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
 
+  // cos/sin(t0 * w_j) for lane j = frequency j, at this wave's first page, with the angle
+  // reduced in fp64; later pages follow by the rotation (cos, sin)(16 w_j).  Over the at
+  // most 64 pages of a wave the recurrence drifts by a few 1e-6 rad at most.
+  float pc, ps, step_c, step_s;
+  {
+    double ang = static_cast<double>(lpa * kPage) * omega;
+    ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
+    double sv, cv;
+    sincos(ang, &sv, &cv);
+    pc = static_cast<float>(cv);
+    ps = static_cast<float>(sv);
+    sincos(kPage * omega, &sv, &cv);
+    step_c = static_cast<float>(cv);
+    step_s = static_cast<float>(sv);
+  }
+
   // Page buffers: the loads of page lp + 1 are issued before page lp is computed
   // (software pipelining; two register buffers, used alternately).
   struct PageBuf {
@@ -205,22 +224,38 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     U2 rk[A], rv[A];
     bool ok;
   };
+  // Page ids of this wave's sub-range (at most 64 pages: the plan keeps items within
+  // 64 pages): lane i holds the ids of page lpa + i, so a page's ids come from a
+  // readlane instead of a memory round trip.
+  const int id_base = lpa;
+  int vb = -1;
+  int vr[A];
+  auto fetch_ids = [&]() {
+    const int lpi = id_base + lane;
+    const bool in = lpi < lpb;
+    vb = in ? p.btab[size_t(agent[0]) * p.max_pages + lpi] : -1;
+    for (int j = 0; j < A; ++j)
+      vr[j] = (in && j < na_g) ? p.rtab[size_t(agent[j]) * p.max_pages + lpi] : -1;
+  };
+  if (lpa < lpb) fetch_ids();
+
   auto load_page = [&](int lp, PageBuf& B) {
-    const int bp = p.btab[size_t(agent[0]) * p.max_pages + lp];
+    const int bp = __builtin_amdgcn_readlane(vb, lp - id_base);
     B.ok = bp >= 0 && bp < p.num_bpages;  // never read outside the pool
     const size_t pg = B.ok ? bp : 0;
     const uint16_t* kt_base = bcache + (pg * 2 * Hkv + h) * tile;
     const uint16_t* vt_base = bcache + (pg * 2 * Hkv + Hkv + h) * tile;
+    // tiles are stored in operand order: lane l's piece is the l-th 16 B (K) / 8 B (V)
     for (int c = 0; c < 4; ++c)
-      B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + col * kD + 32 * c + 8 * g4);
+      B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + 512 * c + 8 * lane);
     for (int t = 0; t < 8; ++t)
-      B.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + (16 * t + col) * kPage + 4 * g4);
+      B.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
     for (int j = 0; j < A; ++j) {
-      const int rp = j < na_g ? p.rtab[size_t(agent[j]) * p.max_pages + lp] : -1;
+      const int rp = __builtin_amdgcn_readlane(vr[j], lp - id_base);
       const bool ok = rp >= 0 && rp < p.num_rpages;
       const uint16_t* rb = rcache + size_t(ok ? rp : 0) * 2 * kPage * kR;
-      B.rk[j].u = *reinterpret_cast<const uint2*>(rb + col * kR + 4 * g4);
-      B.rv[j].u = *reinterpret_cast<const uint2*>(rb + kPage * kR + col * kPage + 4 * g4);
+      B.rk[j].u = *reinterpret_cast<const uint2*>(rb + 4 * lane);
+      B.rv[j].u = *reinterpret_cast<const uint2*>(rb + kPage * kR + 4 * lane);
       if (!ok) {
         B.rk[j].u = make_uint2(0, 0);
         B.rv[j].u = make_uint2(0, 0);
@@ -254,40 +289,39 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       for (int j = 0; j < A; ++j) B.rv[j].u = mask4(B.rv[j].u);
     }
 
-    // -- RoPE angles of this page: lane j computes t0 * omega_j, reduced in fp64 --
-    {
-      double ang = static_cast<double>(lp * kPage) * omega;
-      ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
-      float sv, cv;
-      sincosf(static_cast<float>(ang), &sv, &cv);
-      ptrig[lane] = cv;
-      ptrig[64 + lane] = sv;
+    // -- RoPE angles of this page: lane j holds cos/sin(t0 * w_j) (see the recurrence) --
+    ptrig[lane] = pc;
+    ptrig[64 + lane] = ps;
+    {  // advance to the next page: rotate by 16 * w_j
+      const float c = pc * step_c - ps * step_s;
+      ps = ps * step_c + pc * step_s;
+      pc = c;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes above have landed
-    float ct[16], st[16];  // pair 8*half + 4*(T&1) + i  <->  j = 32*half + 8*g4 + 4*(T&1) + i
-    for (int half = 0; half < 2; ++half) {
-      const int jb = 32 * half + 8 * g4;
-      for (int e = 0; e < 8; ++e) {
-        const float c0 = ptrig[jb + e], s0 = ptrig[64 + jb + e];
-        const float cc = trig_c[col * kTrigPad + jb + e], ss = trig_s[col * kTrigPad + jb + e];
-        ct[8 * half + e] = c0 * cc - s0 * ss;  // s * cos((t0 + c) w_j)
-        st[8 * half + e] = s0 * cc + c0 * ss;  // s * sin((t0 + c) w_j)
-      }
-    }
 
     // -- scores: shared base tile, then per agent the rotated residual --
     f4 sb = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < 4; ++c) sb = mfma32(B.kt[c].b, qv[c], sb);
-    f4 ssel = sb;
-    for (int j = 0; j < A; ++j) {
-      if (j >= na_g) break;
-      const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
-      U4 kr[4];
-      for (int half = 0; half < 2; ++half) {
-        // tiles T = 2half, 2half+1 (chunk half) and their partners T + 4 (chunk half + 2)
+    f4 sj[A];
+    for (int j = 0; j < A; ++j) sj[j] = sb;
+    // Dims are handled in two halves: half h covers score chunks h and h + 2, i.e. the
+    // reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.
+    for (int half = 0; half < 2; ++half) {
+      // s * cos / s * sin of (t0 + c) * w_j for j = 32*half + 8*g4 + e  (c = this lane's row)
+      float ct[8], st[8];
+      const int jb = 32 * half + 8 * g4;
+      for (int e = 0; e < 8; ++e) {
+        const float c0 = ptrig[jb + e], s0 = ptrig[64 + jb + e];
+        const float cc = trig_c[col * kTrigPad + jb + e], ss = trig_s[col * kTrigPad + jb + e];
+        ct[e] = c0 * cc - s0 * ss;
+        st[e] = s0 * cc + c0 * ss;
+      }
+      const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
+      for (int j = 0; j < A; ++j) {
+        if (j >= na_g) break;
+        const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
         f4 d[4];
-        const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
         for (int u = 0; u < 4; ++u) {
           U2 a;
           a.u = bkj[Ts[u] * 64];
@@ -296,20 +330,23 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         for (int u = 0; u < 2; ++u) {
           for (int i = 0; i < 4; ++i) {
             const float x = d[u][i], y = d[u + 2][i];
-            const float c = ct[8 * half + 4 * u + i], sn = st[8 * half + 4 * u + i];
+            const float c = ct[4 * u + i], sn = st[4 * u + i];
             d[u][i] = x * c - y * sn;
             d[u + 2][i] = y * c + x * sn;
           }
         }
-        kr[half].u = make_uint4(pack_bf16x2(d[0][0], d[0][1]), pack_bf16x2(d[0][2], d[0][3]),
-                                pack_bf16x2(d[1][0], d[1][1]), pack_bf16x2(d[1][2], d[1][3]));
-        kr[half + 2].u = make_uint4(pack_bf16x2(d[2][0], d[2][1]), pack_bf16x2(d[2][2], d[2][3]),
-                                    pack_bf16x2(d[3][0], d[3][1]), pack_bf16x2(d[3][2], d[3][3]));
+        U4 k0, k2;
+        k0.u = make_uint4(pack_bf16x2(d[0][0], d[0][1]), pack_bf16x2(d[0][2], d[0][3]),
+                          pack_bf16x2(d[1][0], d[1][1]), pack_bf16x2(d[1][2], d[1][3]));
+        k2.u = make_uint4(pack_bf16x2(d[2][0], d[2][1]), pack_bf16x2(d[2][2], d[2][3]),
+                          pack_bf16x2(d[3][0], d[3][1]), pack_bf16x2(d[3][2], d[3][3]));
+        sj[j] = mfma32(k0.b, qv[half], sj[j]);
+        sj[j] = mfma32(k2.b, qv[half + 2], sj[j]);
       }
-      f4 sj = sb;
-      for (int c = 0; c < 4; ++c) sj = mfma32(kr[c].b, qv[c], sj);
-      if (jc == j) ssel = sj;
     }
+    f4 ssel = sb;
+    for (int j = 0; j < A; ++j)
+      if (jc == j) ssel = sj[j];
 
     // -- online softmax over this page's 16 keys, per column (log2 domain) --
     float sc[4];
@@ -321,21 +358,24 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     }
     pmax = fmaxf(pmax, shfl_xor(pmax, 16));
     pmax = fmaxf(pmax, shfl_xor(pmax, 32));
-    const float m_new = fmaxf(m_run, pmax);
-    float alpha = 1.f;
-    float pr[4];
-    if (m_new == -INFINITY) {
-      for (int i = 0; i < 4; ++i) pr[i] = 0.f;
-    } else {
-      // arguments are <= 0; v_exp_f32 flushes results below 2^-126 to zero, which only
-      // drops probabilities that are negligible next to the running maximum's 1.0
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+    // The reference maximum m_run only moves when a column's page maximum exceeds it by
+    // more than 8 (log2 units): probabilities then stay below 2^8 and the rescale of the
+    // accumulators (acc AND acc_r, by the same factor) is skipped on almost every page.
+    const bool grow = pmax > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+      const float m_new = grow ? pmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+      l_run *= alpha;
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+      accr *= alpha;
+      m_run = m_new;
     }
-    l_run = l_run * alpha + (pr[0] + pr[1] + pr[2] + pr[3]);
-    m_run = m_new;
-    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-    accr *= alpha;
+    // arguments are <= 8; v_exp_f32 flushes results below 2^-126 to zero, which only drops
+    // probabilities negligible next to the reference's 1.0
+    const float m_ref = fmaxf(m_run, -1e30f);  // no -inf - -inf for columns without keys
+    float pr[4];
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
+    l_run += (pr[0] + pr[1] + pr[2] + pr[3]);
 
     U2 pb;
     pb.u = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
@@ -349,14 +389,18 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   };
 
   if constexpr (kPipe) {
+    // The prefetch is issued unconditionally (past the end it re-reads the last page, an
+    // L2 hit) so that every wait below only covers the older buffer's loads.
     PageBuf buf0, buf1;
-    if (lpa < lpb) load_page(lpa, buf0);
-    for (int lp = lpa; lp < lpb; lp += 2) {
-      if (lp + 1 < lpb) load_page(lp + 1, buf1);
-      compute_page(lp, buf0);
-      if (lp + 1 >= lpb) break;
-      if (lp + 2 < lpb) load_page(lp + 2, buf0);
-      compute_page(lp + 1, buf1);
+    if (lpa < lpb) {
+      load_page(lpa, buf0);
+      for (int lp = lpa; lp < lpb; lp += 2) {
+        load_page(min(lp + 1, lpb - 1), buf1);
+        compute_page(lp, buf0);
+        if (lp + 1 >= lpb) break;
+        load_page(min(lp + 2, lpb - 1), buf0);
+        compute_page(lp + 1, buf1);
+      }
     }
   } else {
     for (int lp = lpa; lp < lpb; ++lp) {
@@ -435,12 +479,11 @@ hipError_t launch_decode_mfma_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// FORKKV_DECODE_PIPE=1 selects the register-prefetch variant (tuning aid; it needs about
-// 50 more VGPRs, halving occupancy, and measured slower on the decode workloads).
+// FORKKV_DECODE_PIPE=0 selects the variant without register prefetch (tuning aid).
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   static const bool pipe = [] {
     const char* e = std::getenv("FORKKV_DECODE_PIPE");
-    return e && e[0] == '1';
+    return !(e && e[0] == '0');
   }();
   return pipe ? launch_decode_mfma_t<true>(p, s) : launch_decode_mfma_t<false>(p, s);
 }

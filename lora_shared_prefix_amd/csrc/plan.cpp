@@ -62,6 +62,8 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   if (o.max_agents_per_item < 0 || o.pages_per_item < 0) return FORKKV_EINVAL;
   if (o.max_agents_per_item > 0) cap = std::min(cap, o.max_agents_per_item);
   int ppi = o.pages_per_item > 0 ? o.pages_per_item : (kernel == FORKKV_KERNEL_MFMA ? 32 : 16);
+  // the MFMA kernel keeps a wave's page ids in one register: at most 64 pages per item
+  if (kernel == FORKKV_KERNEL_MFMA) ppi = std::min(ppi, 64);
 
   // 1. Maximal runs of logical pages with an identical set of agents sharing the page.
   std::vector<Run> runs;

@@ -25,8 +25,9 @@ bool valid_desc(const forkkv_pool_desc* d) {
   if (d->page_size != kPage) return false;
   if (d->num_bpages < 1 || d->num_rpages < 1) return false;
   if (d->num_kv_heads < 1 || d->num_kv_heads > 64) return false;
-  if (d->head_dim < 2 || d->head_dim > 256 || (d->head_dim & 1)) return false;
-  if (d->rank < 1 || d->rank > 64) return false;
+  // tiles are stored in matrix-core operand order: 16-dim and 4-rank blocks
+  if (d->head_dim < 16 || d->head_dim > 256 || (d->head_dim % 16)) return false;
+  if (d->rank < 4 || d->rank > 64 || (d->rank % 4)) return false;
   if (d->dtype != FORKKV_DTYPE_F32 && d->dtype != FORKKV_DTYPE_BF16) return false;
   return true;
 }

@@ -18,8 +18,9 @@ from __future__ import annotations
 import numpy as np
 
 from .rope import rope_rotate, rope_unrotate
-from .storage import (base_key_rows, base_value_rows, decode_values, res_key_rows,
-                      res_value_rows)
+from .storage import (base_key_rows, base_value_rows, decode_values, key_offset,
+                      res_key_offset, res_key_rows, res_value_offset, res_value_rows,
+                      value_offset)
 
 
 class Geometry:
@@ -101,16 +102,17 @@ def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk
     bp, rp = bpool.copy(), rpool.copy()
     N, C = k_new.shape[0], k_new.shape[1]
     P, d, r = geo.P, geo.d, geo.r
+    dims, ranks = np.arange(d), np.arange(r)
     for a in range(N):
         for i in range(C):
             t = int(start_pos[a]) + i
             page, row = int(btab[a][t // P]), t % P
             for h in range(geo.Hkv):
-                bp[page, 0, h, row * d:(row + 1) * d] = k_new[a, i, h]
-                bp[page, 1, h, np.arange(d) * P + row] = v_new[a, i, h]
+                bp[page, 0, h, key_offset(row, dims)] = k_new[a, i, h]
+                bp[page, 1, h, value_offset(row, dims)] = v_new[a, i, h]
             page = int(rtab[a][t // P])
-            rp[page, 0, row * r:(row + 1) * r] = rk_new[a, i]
-            rp[page, 1, np.arange(r) * P + row] = rv_new[a, i]
+            rp[page, 0, res_key_offset(row, ranks)] = rk_new[a, i]
+            rp[page, 1, res_value_offset(row, ranks, r)] = rv_new[a, i]
     return bp, rp
 
 

@@ -1,13 +1,21 @@
 """Reading stored pool bytes as fp64 values (oracle side; test infrastructure).
 
-Layout of the pools (fixed by this library; the pages leave it open):
-base pool ``[page][plane][kv_head][P*d]`` with plane 0 = key tile ``[row][dim]``
-and plane 1 = value tile ``[dim][row]``; residual pool ``[page][plane][P*r]``
-with plane 0 = key residual ``[row][k]`` and plane 1 = value residual ``[k][row]``.
+Pool layout (fixed by this library; the pages leave it open).  A base page is
+``[plane][kv_head][P*d]`` elements, a residual page ``[plane][P*r]``, with P = 16.
+Inside a tile the elements sit in the order the gfx950 matrix cores consume them:
+
+* base key   (row t, dim x):  ``(x // 8) * (16 * 8) + t * 8 + x % 8``
+* base value (row t, dim x):  ``((x // 16) * 4 + t // 4) * 64 + (x % 16) * 4 + t % 4``
+* key residual   (row t, rank k): ``(k // 4) * (16 * 4) + t * 4 + k % 4``
+* value residual (row t, rank k): ``(t // 4) * (4 * r) + k * 4 + t % 4``
+
+so d must be a multiple of 16 and r a multiple of 4.
 """
 from __future__ import annotations
 
 import numpy as np
+
+P = 16
 
 
 def decode_values(arr: np.ndarray, dtype: str) -> np.ndarray:
@@ -20,38 +28,50 @@ def decode_values(arr: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def _pages_rows(tab_row: np.ndarray, positions: np.ndarray, P: int):
-    lp = positions // P
-    return tab_row[lp].astype(np.int64), (positions % P).astype(np.int64)
+def key_offset(t, x):
+    return (x // 8) * (P * 8) + t * 8 + x % 8
 
 
-def base_key_rows(bpool, btab_row, positions, head, P, d, dtype):
+def value_offset(t, x):
+    return ((x // 16) * 4 + t // 4) * 64 + (x % 16) * 4 + t % 4
+
+
+def res_key_offset(t, k):
+    return (k // 4) * (P * 4) + t * 4 + k % 4
+
+
+def res_value_offset(t, k, r):
+    return (t // 4) * (4 * r) + k * 4 + t % 4
+
+
+def _pages_rows(tab_row: np.ndarray, positions: np.ndarray, P_: int):
+    lp = positions // P_
+    return tab_row[lp].astype(np.int64), (positions % P_).astype(np.int64)
+
+
+def base_key_rows(bpool, btab_row, positions, head, P_, d, dtype):
     """Stored (post-RoPE) base keys of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P)
-    tiles = bpool[:, 0, head, :]
-    idx = rows[:, None] * d + np.arange(d)[None, :]
-    return decode_values(tiles[pages[:, None], idx], dtype)
+    pages, rows = _pages_rows(btab_row, positions, P_)
+    idx = key_offset(rows[:, None], np.arange(d)[None, :])
+    return decode_values(bpool[:, 0, head, :][pages[:, None], idx], dtype)
 
 
-def base_value_rows(bpool, btab_row, positions, head, P, d, dtype):
+def base_value_rows(bpool, btab_row, positions, head, P_, d, dtype):
     """Base values of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P)
-    tiles = bpool[:, 1, head, :]
-    idx = np.arange(d)[None, :] * P + rows[:, None]
-    return decode_values(tiles[pages[:, None], idx], dtype)
+    pages, rows = _pages_rows(btab_row, positions, P_)
+    idx = value_offset(rows[:, None], np.arange(d)[None, :])
+    return decode_values(bpool[:, 1, head, :][pages[:, None], idx], dtype)
 
 
-def res_key_rows(rpool, rtab_row, positions, P, r, dtype):
+def res_key_rows(rpool, rtab_row, positions, P_, r, dtype):
     """Rank-r key residuals (no RoPE) at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P)
-    tiles = rpool[:, 0, :]
-    idx = rows[:, None] * r + np.arange(r)[None, :]
-    return decode_values(tiles[pages[:, None], idx], dtype)
+    pages, rows = _pages_rows(rtab_row, positions, P_)
+    idx = res_key_offset(rows[:, None], np.arange(r)[None, :])
+    return decode_values(rpool[:, 0, :][pages[:, None], idx], dtype)
 
 
-def res_value_rows(rpool, rtab_row, positions, P, r, dtype):
+def res_value_rows(rpool, rtab_row, positions, P_, r, dtype):
     """Rank-r value residuals at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P)
-    tiles = rpool[:, 1, :]
-    idx = np.arange(r)[None, :] * P + rows[:, None]
-    return decode_values(tiles[pages[:, None], idx], dtype)
+    pages, rows = _pages_rows(rtab_row, positions, P_)
+    idx = res_value_offset(rows[:, None], np.arange(r)[None, :], r)
+    return decode_values(rpool[:, 1, :][pages[:, None], idx], dtype)

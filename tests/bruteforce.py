@@ -31,10 +31,12 @@ def _key_value(P, d, r, dtype, bpool, rpool, btab_a, rtab_a, Bk_a, Bv_a, h, t, s
     else:
         lp, row = divmod(t, P)
         bp, rp = btab_a[lp], rtab_a[lp]
-        bk = [_val(bpool[bp][0][h][row * d + j], dtype) for j in range(d)]
-        bv = [_val(bpool[bp][1][h][j * P + row], dtype) for j in range(d)]
-        rk = [_val(rpool[rp][0][row * r + k], dtype) for k in range(r)]
-        rv = [_val(rpool[rp][1][k * P + row], dtype) for k in range(r)]
+        # tiles are stored in matrix-core operand order (see include/forkkv.h)
+        bk = [_val(bpool[bp][0][h][(j // 8) * 128 + row * 8 + j % 8], dtype) for j in range(d)]
+        bv = [_val(bpool[bp][1][h][((j // 16) * 4 + row // 4) * 64 + (j % 16) * 4 + row % 4],
+                   dtype) for j in range(d)]
+        rk = [_val(rpool[rp][0][(k // 4) * 64 + row * 4 + k % 4], dtype) for k in range(r)]
+        rv = [_val(rpool[rp][1][(row // 4) * 4 * r + k * 4 + row % 4], dtype) for k in range(r)]
     half = d // 2
     key = [0.0] * d
     for j in range(half):

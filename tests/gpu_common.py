@@ -4,7 +4,8 @@ from __future__ import annotations
 import numpy as np
 
 from oracle import PoolModel
-from oracle.storage import decode_values
+from oracle.storage import (decode_values, key_offset, res_key_offset, res_value_offset,
+                            value_offset)
 
 # Tolerance (bf16 inputs, fp32 accumulation): max-abs error <= 1e-2 and the largest
 # absolute error relative to the largest reference magnitude (a normwise relative
@@ -51,14 +52,15 @@ def model_tables(num_bpages, num_rpages, perm_b, perm_r, ops, agents, max_pages)
 
 
 def apply_cows_host(bpool, cows, Hkv, d):
-    """Row copies of fork packing applied to a host pool (K rows and V^T columns)."""
+    """Row copies of fork packing applied to a host pool (the first n rows, K and V)."""
     out = bpool.copy()
+    dims = np.arange(d)
     for src, dst, n in cows:
         for h in range(Hkv):
-            k = out[src, 0, h].reshape(16, d)
-            out[dst, 0, h].reshape(16, d)[:n] = k[:n]
-            v = out[src, 1, h].reshape(d, 16)
-            out[dst, 1, h].reshape(d, 16)[:, :n] = v[:, :n]
+            for plane, off in ((0, key_offset), (1, value_offset)):
+                for row in range(n):
+                    idx = off(row, dims)
+                    out[dst, plane, h, idx] = out[src, plane, h, idx]
     return out
 
 
@@ -76,15 +78,16 @@ def poison_unused(bpool, rpool, used_b, used_r, dtype, d, r):
     """Fill every slot the batch never reads with NaN (bit pattern for bf16)."""
     nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC0)
     bp, rp = bpool.copy(), rpool.copy()
+    dims, ranks = np.arange(d), np.arange(r)
     for page in range(bp.shape[0]):
         for row in range(16):
             if (page, row) not in used_b:
                 for h in range(bp.shape[2]):
-                    bp[page, 0, h].reshape(16, d)[row] = nan
-                    bp[page, 1, h].reshape(d, 16)[:, row] = nan
+                    bp[page, 0, h, key_offset(row, dims)] = nan
+                    bp[page, 1, h, value_offset(row, dims)] = nan
     for page in range(rp.shape[0]):
         for row in range(16):
             if (page, row) not in used_r:
-                rp[page, 0].reshape(16, r)[row] = nan
-                rp[page, 1].reshape(r, 16)[:, row] = nan
+                rp[page, 0, res_key_offset(row, ranks)] = nan
+                rp[page, 1, res_value_offset(row, ranks, r)] = nan
     return bp, rp

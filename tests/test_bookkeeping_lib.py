@@ -17,7 +17,7 @@ from workloads import CONFIGS, chunk_ops, pool_ops
 ITEM_INTS = 12
 
 
-def _pair(nb, nr, perm_b=None, perm_r=None, Hkv=1, d=8, r=4):
+def _pair(nb, nr, perm_b=None, perm_r=None, Hkv=1, d=16, r=4):
     lib_pool = fk.Pool(nb, nr, Hkv, d, r, "f32", perm_b, perm_r)
     model = PoolModel(nb, nr, 16, perm_b, perm_r)
     return lib_pool, model
@@ -121,7 +121,7 @@ def test_random_operations_match_model(seed):
 
 
 def test_error_codes():
-    lp = fk.Pool(4, 4, 1, 8, 4, "f32")
+    lp = fk.Pool(4, 4, 1, 16, 4, "f32")
     h = lp.create(True)
     lp.append(h, 40)
     with pytest.raises(fk.ForkKVError) as e:
@@ -138,10 +138,11 @@ def test_error_codes():
         lp.free(h)
     assert e.value.code == fk.EINVAL
     with pytest.raises(fk.ForkKVError) as e:
-        fk.Pool(4, 4, 1, 8, 4, "f32", bpage_order=[0, 1, 1, 2])
+        fk.Pool(4, 4, 1, 16, 4, "f32", bpage_order=[0, 1, 1, 2])
     assert e.value.code == fk.EINVAL
-    with pytest.raises(fk.ForkKVError):
-        fk.Pool(4, 4, 1, 7, 4, "f32")          # odd head_dim
+    for d, r in [(7, 4), (24, 4), (16, 6), (16, 0), (272, 4)]:
+        with pytest.raises(fk.ForkKVError):   # d % 16, r % 4 and ranges
+            fk.Pool(4, 4, 1, d, r, "f32")
     # device call on a host-only pool
     with pytest.raises(fk.ForkKVError) as e:
         lp.cow_copy([(0, 1, 3)], stream=type("S", (), {"cuda_stream": 0})())
@@ -208,7 +209,7 @@ def test_plan_random_topologies(seed, cap, ppi):
     from tests.cases import random_ops
     rng = np.random.default_rng(2000 + seed)
     ops, agents = random_ops(rng, 5, max_prefix=90, max_suffix=50)
-    lp = fk.Pool(128, 128, 2, 8, 4, "f32", rng.permutation(128), rng.permutation(128))
+    lp = fk.Pool(128, 128, 2, 16, 4, "f32", rng.permutation(128), rng.permutation(128))
     names, _ = lp.replay(ops)
     hs = [names[a] for a in agents]
     plan = fk.Plan(lp, hs, 4, kernel=fk.KERNEL_GENERIC, max_agents_per_item=cap, pages_per_item=ppi)
@@ -216,7 +217,7 @@ def test_plan_random_topologies(seed, cap, ppi):
 
 
 def test_plan_rejects_base_only_and_bad_heads():
-    lp = fk.Pool(8, 8, 2, 8, 4, "f32")
+    lp = fk.Pool(8, 8, 2, 16, 4, "f32")
     root = lp.create(False)
     lp.append(root, 20)
     with pytest.raises(fk.ForkKVError):

@@ -122,7 +122,7 @@ def _tiny_batch(seed, dtype, kernel, poison=True, **kw):
                 num_kv_heads=case["Hkv"], num_q_heads=case["Hq"], head_dim=case["d"],
                 rank=case["r"], dtype=dtype)
     pm, hs, bt, rt, lens = model_tables(case["num_bpages"], case["num_rpages"], case["perm_b"],
-                                        case["perm_r"], case["ops"], case["agents"], 8)
+                                        case["perm_r"], case["ops"], case["agents"], 32)
     # the fork packs of unaligned tails copy rows on the device; mirror them on the host
     cows = []
     pm2 = type(pm)(case["num_bpages"], case["num_rpages"], 16, case["perm_b"], case["perm_r"])
@@ -151,26 +151,35 @@ def _tiny_batch(seed, dtype, kernel, poison=True, **kw):
     return case, arrays, host_after, b, bt, rt, lens
 
 
-@pytest.mark.parametrize("seed", range(4))
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_ragged_tiny_batches(seed, dtype):
+RAGGED = [(0, "f32", fk.KERNEL_GENERIC), (1, "f32", fk.KERNEL_GENERIC),
+          (2, "f32", fk.KERNEL_GENERIC), (3, "f32", fk.KERNEL_GENERIC),
+          (0, "bf16", fk.KERNEL_GENERIC), (1, "bf16", fk.KERNEL_GENERIC),
+          (2, "bf16", fk.KERNEL_GENERIC), (3, "bf16", fk.KERNEL_GENERIC),
+          (2, "bf16", fk.KERNEL_MFMA), (4, "bf16", fk.KERNEL_MFMA), (5, "bf16", fk.KERNEL_MFMA),
+          (6, "bf16", fk.KERNEL_MFMA)]
+
+
+@pytest.mark.parametrize("seed,dtype,kernel", RAGGED)
+def test_ragged_tiny_batches(seed, dtype, kernel):
     """Odd lengths, unaligned forks (device row copy), NaN in every unread slot."""
-    d, r = [(8, 3), (64, 8), (128, 16), (32, 5)][seed]
+    d, r = [(16, 4), (64, 8), (128, 16), (32, 12), (128, 16), (128, 16), (128, 16)][seed]
+    Hq = [8, 8, 8, 8, 8, 20, 16][seed]  # G = 4, 10 (one agent per group), 8
     case, arrays, host_after, b, bt, rt, lens = _tiny_batch(
-        700 + seed, dtype, fk.KERNEL_GENERIC, Hq=8, Hkv=2, d=d, r=r, n_agents=5,
-        max_prefix=70, max_suffix=40)
+        700 + seed, dtype, kernel, Hq=Hq, Hkv=2, d=d, r=r, n_agents=[5, 5, 5, 5, 7, 3, 6][seed],
+        max_prefix=[70, 70, 70, 70, 300, 90, 200][seed], max_suffix=40, num_pages=128)
+    assert b.plan.info["kernel"] == kernel
     # the copy-on-write rows landed bit-exactly
     got_pool = b.bcache.cpu().numpy()
     got_pool = got_pool.view(np.uint16) if dtype == "bf16" else got_pool
     assert np.array_equal(got_pool.view(np.uint8), host_after.view(np.uint8))
     out = b.decode(case["lora_scale"], case["sm_scale"], case["theta"])
     torch.cuda.synchronize()
-    ref = decode_attention(Geometry(page_size=16, num_q_heads=8, num_kv_heads=2, head_dim=d,
+    ref = decode_attention(Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=2, head_dim=d,
                                     rank=r, dtype=dtype), host_after, arrays["rpool"], bt, rt,
                            lens, case["q"], case["Bk"], case["Bv"], case["lora_scale"],
                            case["sm_scale"], case["theta"])
     g = gpu_values(out, dtype)
-    assert_close(g, ref, f"ragged seed={seed} {dtype}", scale_abs=True)
+    assert_close(g, ref, f"ragged seed={seed} {dtype} kernel={kernel}", scale_abs=True)
     if dtype == "f32":
         assert errors(g, ref)[1] < 1e-5
 
@@ -242,14 +251,14 @@ def test_sharing_invariance():
 
 
 def test_empty_agent_and_errors():
-    geom = dict(num_bpages=16, num_rpages=16, num_kv_heads=1, num_q_heads=2, head_dim=8, rank=2,
+    geom = dict(num_bpages=16, num_rpages=16, num_kv_heads=1, num_q_heads=2, head_dim=16, rank=4,
                 dtype="f32")
     rng = np.random.default_rng(0)
-    arrays = dict(bpool=rng.standard_normal((16, 2, 1, 128)).astype(np.float32),
-                  rpool=rng.standard_normal((16, 2, 32)).astype(np.float32),
-                  q=rng.standard_normal((2, 2, 8)).astype(np.float32),
-                  Bk=rng.standard_normal((2, 2, 8)).astype(np.float32),
-                  Bv=rng.standard_normal((2, 2, 8)).astype(np.float32))
+    arrays = dict(bpool=rng.standard_normal((16, 2, 1, 256)).astype(np.float32),
+                  rpool=rng.standard_normal((16, 2, 64)).astype(np.float32),
+                  q=rng.standard_normal((2, 2, 16)).astype(np.float32),
+                  Bk=rng.standard_normal((2, 4, 16)).astype(np.float32),
+                  Bv=rng.standard_normal((2, 4, 16)).astype(np.float32))
     ops = [("create", "root", 0), ("append", "root", 20), ("fork", "root", 0, "a0"),
            ("fork", "root", 16, "a1")]
     b = DeviceBatch(geom, arrays, ops, ["a0", "a1"])

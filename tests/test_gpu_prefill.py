@@ -51,7 +51,7 @@ def _run(geom, arrays, ops, agents, perm_b, perm_r, C, s, sm, theta, samples=Non
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_tiny_prefill(seed, dtype):
     C = [5, 16, 23][seed]
-    d, r = [(8, 3), (64, 8), (128, 16)][seed]
+    d, r = [(16, 4), (64, 8), (128, 16)][seed]
     case = tiny_case(900 + seed, dtype, Hq=8, Hkv=2, d=d, r=r, n_agents=3, chunk=C,
                      max_prefix=60, max_suffix=20)
     case["ops"] = [op if op[0] != "fork" else (op[0], op[1], (op[2] // 16) * 16, op[3])

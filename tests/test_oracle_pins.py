@@ -82,9 +82,9 @@ def test_tiny_config_matches_brute_force():
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_random_tiny_decode_matches_brute_force(seed, dtype):
-    """Odd lengths, unaligned forks, partial pages, d in {4, 8}, r in {1, 2, 3}."""
-    d = [4, 8][seed % 2]
-    r = [1, 2, 3][seed % 3]
+    """Odd lengths, unaligned forks, partial pages, d in {16, 32}, r in {4, 8, 12}."""
+    d = [16, 32][seed % 2]
+    r = [4, 8, 12][seed % 3]
     case = tiny_case(100 + seed, dtype, Hq=4, Hkv=2, d=d, r=r, n_agents=3)
     bt, rt, lens, _, _ = _build(case)
     assert _nrel(_oracle_decode(case, bt, rt, lens), _brute(case, bt, rt, lens)) < 1e-12
@@ -94,7 +94,7 @@ def test_random_tiny_decode_matches_brute_force(seed, dtype):
 def test_random_tiny_prefill_matches_brute_force(seed):
     """Chunked prefill: write-then-attend with a causal mask that includes the query itself."""
     C = 5
-    case = tiny_case(200 + seed, "f32", Hq=2, Hkv=1, d=4, r=2, n_agents=2, chunk=C)
+    case = tiny_case(200 + seed, "f32", Hq=2, Hkv=1, d=16, r=4, n_agents=2, chunk=C)
     pm = PoolModel(64, 64, 16, case["perm_b"], case["perm_r"])
     names = pm.replay(case["ops"])
     hs = [names[a] for a in case["agents"]]
@@ -108,7 +108,7 @@ def test_random_tiny_prefill_matches_brute_force(seed):
             case["rk_new"], case["rv_new"], case["Bk"], case["Bv"], case["lora_scale"],
             case["sm_scale"], case["theta"])
     o = prefill_attention(geo, *args)
-    b = np.array(brute_prefill(16, 2, 1, 4, 2, "f32", *args))
+    b = np.array(brute_prefill(16, 2, 1, 16, 4, "f32", *args))
     assert _nrel(o, b) < 1e-12
     # sampled rows equal the full computation bit for bit
     samples = [(1, 3, 0), (0, 0, 1), (0, 4, 0)]
@@ -121,7 +121,7 @@ def test_random_tiny_prefill_matches_brute_force(seed):
 
 @pytest.mark.parametrize("variant", ["zero_B", "zero_scale"])
 def test_zero_adapter_equals_sdpa(variant):
-    case = tiny_case(7, "f32", Hq=6, Hkv=2, d=8, r=3, n_agents=3)
+    case = tiny_case(7, "f32", Hq=6, Hkv=2, d=16, r=4, n_agents=3)
     if variant == "zero_B":
         case["Bk"] = np.zeros_like(case["Bk"])
         case["Bv"] = np.zeros_like(case["Bv"])
@@ -132,8 +132,8 @@ def test_zero_adapter_equals_sdpa(variant):
     geo = _geo(case)
     for a in range(3):
         pos = np.arange(lens[a])
-        K = np.stack([base_key_rows(case["bpool"], bt[a], pos, h, 16, 8, "f32") for h in range(2)])
-        V = np.stack([base_value_rows(case["bpool"], bt[a], pos, h, 16, 8, "f32") for h in range(2)])
+        K = np.stack([base_key_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32") for h in range(2)])
+        V = np.stack([base_value_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32") for h in range(2)])
         K = torch.from_numpy(np.repeat(K, geo.G, axis=0))[None]
         V = torch.from_numpy(np.repeat(V, geo.G, axis=0))[None]
         q = torch.from_numpy(decode_values(case["q"][a], "f32"))[None, :, None, :]
@@ -177,21 +177,21 @@ def test_rope_invariants():
 # ---- C4 / C5: deferred RoPE and associativity (reproduction checks 3 and 4) ------------------
 
 def test_deferred_rope_and_associativity():
-    case = tiny_case(11, "f32", Hq=4, Hkv=2, d=8, r=3, n_agents=2)
+    case = tiny_case(11, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=2)
     bt, rt, lens, _, _ = _build(case)
     geo = _geo(case)
     s = case["lora_scale"]
     for a in range(2):
         pos = np.arange(lens[a])
-        rk = oracle.res_key_rows(case["rpool"], rt[a], pos, 16, 3, "f32")
-        rv = oracle.res_value_rows(case["rpool"], rt[a], pos, 16, 3, "f32")
+        rk = oracle.res_key_rows(case["rpool"], rt[a], pos, 16, 4, "f32")
+        rv = oracle.res_value_rows(case["rpool"], rt[a], pos, 16, 4, "f32")
         Bk = decode_values(case["Bk"][a], "f32")
         Bv = decode_values(case["Bv"][a], "f32")
         for h in range(2):
-            bk = base_key_rows(case["bpool"], bt[a], pos, h, 16, 8, "f32")
-            bv = base_value_rows(case["bpool"], bt[a], pos, h, 16, 8, "f32")
+            bk = base_key_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32")
+            bv = base_value_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32")
             K, V = merged_kv(geo, bk, bv, rk, rv, Bk, Bv, h, pos, s, case["theta"])
-            cols = slice(8 * h, 8 * h + 8)
+            cols = slice(16 * h, 16 * h + 16)
             # RoPE(xW + s xA B) = stored base + RoPE(s xA B)
             assert np.abs(K - (bk + rope_rotate(s * (rk @ Bk[:, cols]), pos, case["theta"]))).max() < 1e-12
             # Eq.(4): P (V_b + s V_r B_v) = P V_b + s (P V_r) B_v
@@ -205,7 +205,7 @@ def test_deferred_rope_and_associativity():
 
 @pytest.mark.parametrize("seed", range(4))
 def test_fused_split_k_form_equals_oracle(seed):
-    case = tiny_case(300 + seed, "f32", Hq=4, Hkv=2, d=8, r=3, n_agents=3, max_prefix=70,
+    case = tiny_case(300 + seed, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=3, max_prefix=70,
                      max_suffix=40)
     bt, rt, lens, _, _ = _build(case)
     rng = np.random.default_rng(seed)
@@ -223,7 +223,7 @@ def test_fused_split_k_form_equals_oracle(seed):
 
 def test_skipping_residual_rescale_is_detected():
     """The note's check 6: acc_r must be rescaled like acc, else B_v's term is misweighted."""
-    case = tiny_case(400, "f32", Hq=4, Hkv=2, d=8, r=3, n_agents=2, max_prefix=70, max_suffix=40)
+    case = tiny_case(400, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=2, max_prefix=70, max_suffix=40)
     case["Bv"] = (np.asarray(case["Bv"]) * 5).astype(np.float32)
     bt, rt, lens, _, _ = _build(case)
     args = (_geo(case), case["bpool"], case["rpool"], bt, rt, lens, case["q"], case["Bk"],
@@ -273,7 +273,7 @@ def _merged_variant(kind):
                                       "wrong_head_cols", "pos_off_by_one", "drop_v_residual",
                                       "gqa_map"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
-    case = tiny_case(500, "f32", Hq=4, Hkv=2, d=8, r=3, n_agents=2)
+    case = tiny_case(500, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=2)
     case["lora_scale"] = 2.0
     bt, rt, lens, _, _ = _build(case)
     if mutation == "rope_sign":
@@ -300,3 +300,30 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
     except (IndexError, ValueError):
         return  # the mistake crashed the oracle: caught
     assert not (_nrel(o, brute) < 1e-9), f"mutation {mutation} not detected"
+
+
+# ---- storage layout: the documented tile orders are bijections with lane-linear reads ------
+
+def test_tile_orders_are_permutations_with_lane_linear_operands():
+    from oracle.storage import key_offset, res_key_offset, res_value_offset, value_offset
+    t = np.arange(16)[:, None]
+    for d in (16, 64, 128, 256):
+        x = np.arange(d)[None, :]
+        assert sorted(key_offset(t, x).ravel()) == list(range(16 * d))
+        assert sorted(value_offset(t, x).ravel()) == list(range(16 * d))
+    for r in (4, 8, 16, 64):
+        k = np.arange(r)[None, :]
+        assert sorted(res_key_offset(t, k).ravel()) == list(range(16 * r))
+        assert sorted(res_value_offset(t, k, r).ravel()) == list(range(16 * r))
+    # MFMA lane l (col = l % 16, g = l // 16): the piece it supplies is contiguous at l*size
+    for l in range(64):
+        col, g = l % 16, l // 16
+        for c in range(4):      # key tile, 16x16x32 A operand: row col, dims 32c + 8g + e
+            assert [key_offset(col, 32 * c + 8 * g + e) for e in range(8)] == \
+                [512 * c + 8 * l + e for e in range(8)]
+        for T in range(8):      # value tile, 16x16x16 A operand: dim 16T + col, rows 4g + e
+            assert [value_offset(4 * g + e, 16 * T + col) for e in range(4)] == \
+                [256 * T + 4 * l + e for e in range(4)]
+        # residuals, r = 16: key as B operand (ranks 4g + e of row col), value as A operand
+        assert [res_key_offset(col, 4 * g + e) for e in range(4)] == [4 * l + e for e in range(4)]
+        assert [res_value_offset(4 * g + e, col, 16) for e in range(4)] == [4 * l + e for e in range(4)]

@@ -6,14 +6,12 @@ workload's sharing topology.  Both the oracle's bookkeeping model and the HIP
 library replay the same operation list with their own code.
 
 Storage layout of the two page pools (the pages are silent on it; this build
-fixes it, and both sides read the same bytes):
-
-* base pool ``bpool[num_bpages][2][Hkv][P*d]``: plane 0 holds the post-RoPE
-  base key tile row-major ``[row][dim]``; plane 1 holds the base value tile
-  transposed ``[dim][row]``.
-* residual pool ``rpool[num_rpages][2][P*r]``: plane 0 holds the rank-r key
-  residual row-major ``[row][k]``; plane 1 holds the value residual transposed
-  ``[k][row]``.
+fixes it, and both sides read the same bytes): a base page is
+``bpool[page][plane][Hkv][P*d]`` (plane 0 = post-RoPE keys, plane 1 = values)
+and a residual page ``rpool[page][plane][P*r]`` (plane 0 = key residual,
+plane 1 = value residual); inside each tile the elements are in the order the
+matrix cores consume them (see ``include/forkkv.h``).  The draws below fill whole
+pools with i.i.d. values, so the tile order does not affect them.
 
 Draw recipe (seeded ``numpy.random.default_rng(seed)``, PCG64), in this order:
 base-page permutation, residual-page permutation, the whole base pool, the whole
