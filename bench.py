@@ -88,6 +88,56 @@ def cpu_baseline(cfg, x, ops, agents, n_sample):
                       f"fp64 numpy, {dt:.1f} s; host cpus={len(os.sched_getaffinity(0))}"}
 
 
+MFMA_PEAK_BF16_TFLOPS = 2500.0
+
+
+def prefill_flops(cfg):
+    """Dense attention flops of one prefill call: QK^T and PV over keys 0..pos, plus the
+    rank-r value accumulator, per (agent, chunk query, q head)."""
+    total = 0
+    for i in range(cfg.chunk_len):
+        keys = cfg.prefix_len + i + 1
+        total += keys
+    per_key = 2 * cfg.head_dim * 2 + 2 * cfg.rank
+    return cfg.n_agents * cfg.num_q_heads * total * per_key
+
+
+def bench_prefill(steps, warmup):
+    """Chunk tokens/s of the prefill call (row write + causal attention) on workload 4."""
+    import numpy as np
+    import torch
+    from lora_shared_prefix_amd.session import DeviceBatch, to_device, workload_geom
+    from workloads import CONFIGS, draw_inputs, pool_ops
+    cfg = CONFIGS[4]
+    log(f"drawing inputs of {cfg.name}")
+    x = draw_inputs(cfg)
+    ops, agents = pool_ops(cfg)
+    b = DeviceBatch(workload_geom(cfg), x, ops, agents, x["perm_b"], x["perm_r"], plan=False)
+    b.reserve_chunk(cfg.chunk_len)
+    chunk = {k: to_device(x[k]) for k in ("q", "k_new", "v_new", "rk_new", "rv_new")}
+    out = torch.empty_like(chunk["q"])
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    n = max(3, steps // 10)
+    for _ in range(max(1, warmup // 5)):
+        b.prefill(chunk, cfg.lora_scale, sm, cfg.rope_theta, out=out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(n):
+        b.prefill(chunk, cfg.lora_scale, sm, cfg.rope_theta, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    fl = prefill_flops(cfg)
+    tflops = fl / (ms * 1e-3) / 1e12
+    log(f"prefill {ms:.3f} ms per call, {tflops:.1f} TFLOP/s")
+    return {"workload": cfg.name, "calls": n, "ms_per_call": ms,
+            "chunk_tokens_per_s": cfg.n_agents * cfg.chunk_len / (ms * 1e-3),
+            "dense_flops_per_call": fl, "tflops": tflops,
+            "mfma_frac": tflops / MFMA_PEAK_BF16_TFLOPS, "peak_tflops": MFMA_PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +148,8 @@ def main():
     ap.add_argument("--pages-per-item", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="agents timed on the oracle (0 = skip)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing chunked prefill on the Qwen3-8B 131072-prefix workload")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many MiB (PMC scaling)")
     args = ap.parse_args()
@@ -222,6 +274,10 @@ def main():
         "combine_avg_us": comb_avg * 1e3,
         "warm_split_avg_us": wsplit / max(wl, 1) * 1e3,
     }
+    if not args.no_prefill:
+        del batches, first  # free the decode inputs before the 1.2 GB prefill workload
+        torch.cuda.empty_cache()
+        result["prefill"] = bench_prefill(args.steps, args.warmup)
     if args.cpu_sample > 0:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(cfg, x, ops, agents, args.cpu_sample)

@@ -100,3 +100,39 @@ def test_qwen3_shape_scaled_prefill():
     idx = tuple(np.array(samples).T)
     assert np.all(np.isfinite(gv))
     assert_close(gv[idx], ref[idx], "qwen3-shape scaled prefill")
+
+
+def test_qwen3_8b_chunked_prefill_workload():
+    """Workload 4 at full size: 8 agents x 512-token chunks over a 131072-token shared prefix.
+
+    Written rows are checked bit for bit at sampled slots; attention is checked on sampled
+    (agent, query, head) rows the oracle computes one by one.
+    """
+    cfg = CONFIGS[4]
+    print(f"[gpu-prefill] drawing inputs of {cfg.name}", flush=True)
+    x = draw_inputs(cfg)
+    ops, agents = pool_ops(cfg)
+    samples = [(a, i, g) for a in (0, 3, 7) for i in (0, 1, 255, 511) for g in (0, 17, 31)]
+    b, out, ref, bt, rt, start, g = _run(workload_geom(cfg), x, ops, agents, x["perm_b"],
+                                          x["perm_r"], cfg.chunk_len, cfg.lora_scale,
+                                          1 / np.sqrt(cfg.head_dim), cfg.rope_theta,
+                                          samples=samples)
+    gv = gpu_values(out, "bf16")
+    assert np.all(np.isfinite(gv))
+    idx = tuple(np.array(samples).T)
+    assert_close(gv[idx], ref[idx], "qwen3-8b chunked prefill (sampled rows)")
+    # a sample of the written rows, bit for bit
+    from oracle.storage import key_offset, res_key_offset, res_value_offset, value_offset
+    bpool = _host(b.bcache, "bf16")
+    rpool = _host(b.rcache, "bf16")
+    dims, ranks = np.arange(128), np.arange(16)
+    for a in (0, 5):
+        for i in (0, 17, 511):
+            t = start[a] + i
+            page, row = bt[a][t // 16], t % 16
+            for h in (0, 7):
+                assert np.array_equal(bpool[page, 0, h, key_offset(row, dims)], x["k_new"][a, i, h])
+                assert np.array_equal(bpool[page, 1, h, value_offset(row, dims)], x["v_new"][a, i, h])
+            rpage = rt[a][t // 16]
+            assert np.array_equal(rpool[rpage, 0, res_key_offset(row, ranks)], x["rk_new"][a, i])
+            assert np.array_equal(rpool[rpage, 1, res_value_offset(row, ranks, 16)], x["rv_new"][a, i])
