@@ -180,7 +180,9 @@ int forkkv_cow_copy(forkkv_pool* pool, const forkkv_cow_op* ops, int32_t n_ops,
 typedef struct {
   int32_t kernel;             /* FORKKV_KERNEL_*; 0 = auto */
   int32_t max_agents_per_item;/* 0 = the kernel's maximum */
-  int32_t pages_per_item;     /* split-K length in pages; 0 = auto */
+  int32_t pages_per_item;     /* split-K length: pages per item (generic kernel) or pages per
+                                 wave (MFMA kernel, <= 64); 0 = auto (MFMA: items sized so the
+                                 grid fits one round of resident waves, balanced per wave) */
 } forkkv_plan_opts;
 
 typedef struct {

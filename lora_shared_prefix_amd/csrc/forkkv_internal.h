@@ -16,11 +16,12 @@ constexpr int kPage = 16;
 
 // One decode work item: a run of logical pages that every listed agent maps to the same
 // physical base pages, processed by one workgroup per KV head.
-//   [0] first logical page   [1] number of pages   [2] number of agents
-//   [3] first partial slot (agent j of the item writes slot first + j)
+//   [0] first logical page   [1] number of pages   [2] number of agents   [3] unused
 //   [4 .. 4+kItemAgents) agent indices
+//   [4+kItemAgents .. 4+2*kItemAgents) partial slot of each agent; the slots of one agent
+//   are consecutive (slot_ptr[a] .. slot_ptr[a+1]), so the combine needs no slot list
 constexpr int kItemAgents = 8;
-constexpr int kItemInts = 4 + kItemAgents;
+constexpr int kItemInts = 4 + 2 * kItemAgents;
 
 // Plan blob header (int32 words), followed by the sections at the given offsets.
 enum : int {
@@ -144,5 +145,6 @@ int generic_lds_bytes(int na, int rows, int d, int r);
 bool prefill_mfma_enabled();
 bool mfma_supported(int dtype, int head_dim, int rank, int group);
 int mfma_group_agents(int group);
+int mfma_agents_per_wave(int group);
 
 }  // namespace forkkv

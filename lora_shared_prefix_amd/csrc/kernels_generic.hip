@@ -98,8 +98,9 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
   const int n = Hkv * d;
 
   // ---- work description -----------------------------------------------------------------
-  int na, lp_begin, lp_end, rows, slot_base = 0;
+  int na, lp_begin, lp_end, rows;
   int agents[kItemAgents];
+  int slot_of[kItemAgents];
   int limit[kItemAgents];  // decode: keys t < limit[j]
   int a_pf = 0, q0 = 0, start = 0, C = 0, QB = 0;
   if constexpr (kPrefill) {
@@ -121,9 +122,9 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     lp_begin = it[0];
     lp_end = it[0] + it[1];
     na = it[2];
-    slot_base = it[3];
     for (int j = 0; j < kItemAgents; ++j) {
       agents[j] = j < na ? it[4 + j] : 0;
+      slot_of[j] = j < na ? it[4 + kItemAgents + j] : 0;
       limit[j] = j < na ? dp.plan[dp.off_lens + agents[j]] : 0;
     }
     rows = na * G;
@@ -323,7 +324,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
       const int e = tid + i * kGenericThreads;
       if (e < rows * d) {
         const int row = e / d, dd = e % d, j = row / G, g = row % G;
-        dp.ws_acc[((size_t(slot_base) + j) * Hq + h * G + g) * d + dd] = acc[i];
+        dp.ws_acc[(size_t(slot_of[j]) * Hq + h * G + g) * d + dd] = acc[i];
       }
     }
 #pragma unroll
@@ -331,12 +332,12 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
       const int e = tid + i * kGenericThreads;
       if (e < rows * r) {
         const int row = e / r, k = e % r, j = row / G, g = row % G;
-        dp.ws_accr[((size_t(slot_base) + j) * Hq + h * G + g) * r + k] = accr[i];
+        dp.ws_accr[(size_t(slot_of[j]) * Hq + h * G + g) * r + k] = accr[i];
       }
     }
     for (int row = tid; row < rows; row += kGenericThreads) {
       const int j = row / G, g = row % G;
-      const size_t o = ((size_t(slot_base) + j) * Hq + h * G + g) * 2;
+      const size_t o = (size_t(slot_of[j]) * Hq + h * G + g) * 2;
       dp.ws_ml[o] = sm[row];
       dp.ws_ml[o + 1] = sl[row];
     }
@@ -345,90 +346,128 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
 
 // Split-K merge with a log-sum-exp rule, then the one-time B_v up-projection:
 // o = (sum_i w_i acc_i + s * (sum_i w_i acc_r,i) B_v) / sum_i w_i l_i, w_i = 2^(m_i - M).
-// Grid: (agent * Hq + q head, dimension half).  One pass reads every partial's (m, l)
-// and slot id into LDS; then four waves stream disjoint subsets of the partials, one
-// output dimension per lane, with independent loads in flight.
-constexpr int kCombineChunk = 512;   // partials whose weights sit in LDS at once
-constexpr int kCombineSplit = 2;     // blocks per output row (dimension halves)
+// One block per output row (agent, q head).  Thread (group sg of 8, lane l of 32) takes
+// partials sg, sg + 8, ... and dims 4l..4l+3 (+128): all of its loads of a chunk are issued
+// before any is used, so a row costs about one memory round trip; each thread merges its
+// partials online and the eight groups are merged through LDS with the same rule.
+constexpr int kCombineGroups = 8;
+constexpr int kCombinePer = 12;   // partials per thread per chunk
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-template <typename T>
+template <typename T, int kDG>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
+  // kDG = float4 dim groups per thread: the 32 lanes of a group cover 128 dims each
   using E = Elem<T>;
-  __shared__ float s_w[kCombineChunk];
-  __shared__ int s_row[kCombineChunk];
-  __shared__ float s_red[8];
-  __shared__ float s_acc[4][128];
-  __shared__ float s_accr[4][64];
-  __shared__ float s_ar[64];
-  const int row_out = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  constexpr int kBvRegs = 16;  // B_v rows fetched before the merge; the rest after it
+  __shared__ float s_m[kCombineGroups];
+  __shared__ float s_l[kCombineGroups];
+  __shared__ float4 s_acc[kCombineGroups][32 * kDG];
+  __shared__ float4 s_ar[kCombineGroups][16];
+  __shared__ float s_arf[64];
+  const int row_out = blockIdx.x, tid = threadIdx.x;
+  const int sg = tid >> 5, l32 = tid & 31;
   const int d = p.head_dim, r = p.rank, Hq = p.num_q_heads;
   const int a = row_out / Hq, g = row_out % Hq, h = g / p.group;
   const int n = p.num_kv_heads * d;
-  const int dpb = (d + kCombineSplit - 1) / kCombineSplit;  // dims of this block
-  const int dim0 = part * dpb;
+  // the partials of agent a are slots s0 .. s1-1 (consecutive)
   const int s0 = p.plan[p.off_slot_ptr + a], s1 = p.plan[p.off_slot_ptr + a + 1];
-  const int32_t* slots = p.plan + p.off_slot_list;
+  const int ar_q = min(4 * l32, r - 4);     // rank quad this lane reads (clamped)
+  const int od = min(tid, d - 1);           // output dim of this thread
+  const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + od;
+  float bvv[kBvRegs];
+#pragma unroll
+  for (int k = 0; k < kBvRegs; ++k) bvv[k] = E::ld(bv, size_t(min(k, r - 1)) * n);
 
-  // pass 1: global maximum of the partial maxima
-  float M = -INFINITY;
-  for (int i = s0 + tid; i < s1; i += 256) M = fmaxf(M, p.ws_ml[(size_t(slots[i]) * Hq + g) * 2]);
-  M = wave_max(M);
-  if (lane == 0) s_red[wv] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
-  float lsum = 0.f, Ar = 0.f;
-  float A[2] = {0.f, 0.f};
-  for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
-    const int cn = min(kCombineChunk, s1 - c0);
-    __syncthreads();
-    for (int i = tid; i < cn; i += 256) {
-      const int row = slots[c0 + i] * Hq + g;
-      const float m = p.ws_ml[size_t(row) * 2];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      s_w[i] = w;
-      s_row[i] = row;
-      lsum += w * p.ws_ml[size_t(row) * 2 + 1];
+  float m_t = -INFINITY, l_t = 0.f;
+  float4 A4[kDG], Ar4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int e = 0; e < kDG; ++e) A4[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = s0; c0 < s1; c0 += kCombineGroups * kCombinePer) {
+    float mv[kCombinePer], lv[kCombinePer];
+    float4 av[kCombinePer][kDG], arv[kCombinePer];
+    // every load of the chunk is issued before any is used (indices clamped in range)
+#pragma unroll
+    for (int u = 0; u < kCombinePer; ++u) {
+      const int i = c0 + sg + kCombineGroups * u;
+      const size_t row = size_t(min(i, s1 - 1)) * Hq + g;
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + row * 2);
+      mv[u] = i < s1 ? ml.x : -INFINITY;
+      lv[u] = ml.y;
+#pragma unroll
+      for (int e = 0; e < kDG; ++e)
+        av[u][e] = *reinterpret_cast<const float4*>(p.ws_acc + row * d +
+                                                    min(4 * l32 + 128 * e, d - 4));
+      arv[u] = *reinterpret_cast<const float4*>(p.ws_accr + row * r + ar_q);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int i = wv; i < cn; i += 4) {
-      const float w = s_w[i];
-      const size_t row = s_row[i];
-      const float* src = p.ws_acc + row * d + dim0;
-      for (int e = 0; e < 2; ++e)
-        if (lane + 64 * e < dpb && dim0 + lane + 64 * e < d) A[e] += w * src[lane + 64 * e];
-      if (lane < r) Ar += w * p.ws_accr[row * r + lane];
+    float mc = m_t;
+#pragma unroll
+    for (int u = 0; u < kCombinePer; ++u) mc = fmaxf(mc, mv[u]);
+    if (mc != -INFINITY) {
+      const float sc = exp2f(m_t - mc);  // 0 while nothing merged yet
+      l_t *= sc;
+#pragma unroll
+      for (int e = 0; e < kDG; ++e) {
+        A4[e].x *= sc; A4[e].y *= sc; A4[e].z *= sc; A4[e].w *= sc;
+      }
+      Ar4.x *= sc; Ar4.y *= sc; Ar4.z *= sc; Ar4.w *= sc;
+      m_t = mc;
+#pragma unroll
+      for (int u = 0; u < kCombinePer; ++u) {
+        const float wgt = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - mc);
+        l_t += wgt * lv[u];
+#pragma unroll
+        for (int e = 0; e < kDG; ++e) {
+          A4[e].x += wgt * av[u][e].x; A4[e].y += wgt * av[u][e].y;
+          A4[e].z += wgt * av[u][e].z; A4[e].w += wgt * av[u][e].w;
+        }
+        Ar4.x += wgt * arv[u].x; Ar4.y += wgt * arv[u].y;
+        Ar4.z += wgt * arv[u].z; Ar4.w += wgt * arv[u].w;
+      }
     }
   }
-  lsum = wave_sum(lsum);
+  // merge the eight groups (threads of one group hold the same m_t and l_t)
+  if (l32 == 0) {
+    s_m[sg] = m_t;
+    s_l[sg] = l_t;
+  }
   __syncthreads();
-  if (lane == 0) s_red[4 + wv] = lsum;
-  for (int e = 0; e < 2; ++e)
-    if (lane + 64 * e < dpb) s_acc[wv][lane + 64 * e] = A[e];
-  if (lane < r) s_accr[wv][lane] = Ar;
+  float M = -INFINITY;
+  for (int k = 0; k < kCombineGroups; ++k) M = fmaxf(M, s_m[k]);
+  const float sc = (m_t == -INFINITY) ? 0.f : exp2f(m_t - M);
+#pragma unroll
+  for (int e = 0; e < kDG; ++e) {
+    float4 v = A4[e];
+    v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+    if (4 * l32 + 128 * e < d) s_acc[sg][l32 + 32 * e] = v;
+  }
+  if (4 * l32 < r) s_ar[sg][l32] = make_float4(Ar4.x * sc, Ar4.y * sc, Ar4.z * sc, Ar4.w * sc);
   __syncthreads();
-  const float Lsum = s_red[4] + s_red[5] + s_red[6] + s_red[7];
-  if (tid < r) s_ar[tid] = s_accr[0][tid] + s_accr[1][tid] + s_accr[2][tid] + s_accr[3][tid];
+  if (tid < r) {
+    float ar = 0.f;
+    for (int k = 0; k < kCombineGroups; ++k) {
+      const float4 v = s_ar[k][tid >> 2];
+      ar += (tid & 3) == 0 ? v.x : (tid & 3) == 1 ? v.y : (tid & 3) == 2 ? v.z : v.w;
+    }
+    s_arf[tid] = ar;
+  }
   __syncthreads();
-  if (tid < dpb && dim0 + tid < d) {
-    const int dim = dim0 + tid;
-    const float acc = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
-    const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * r * n + size_t(h) * d + dim;
+  float Lsum = 0.f;
+  for (int k = 0; k < kCombineGroups; ++k)
+    Lsum += (s_m[k] == -INFINITY) ? 0.f : exp2f(s_m[k] - M) * s_l[k];
+  // output: thread tid writes dim tid (d <= 256); B_v is applied once, to the merged sum
+  if (tid < d) {
+    float acc = 0.f;
+    const int q4 = tid >> 2, c4 = tid & 3;
+    for (int k = 0; k < kCombineGroups; ++k) {
+      const float4 v = s_acc[k][q4];
+      acc += c4 == 0 ? v.x : c4 == 1 ? v.y : c4 == 2 ? v.z : v.w;
+    }
     float res = 0.f;
-    for (int k = 0; k < r; ++k) res += s_ar[k] * E::ld(bv, size_t(k) * n);
+#pragma unroll
+    for (int k = 0; k < kBvRegs; ++k)
+      if (k < r) res += s_arf[k] * bvv[k];
+    for (int k = kBvRegs; k < r; ++k) res += s_arf[k] * E::ld(bv, size_t(k) * n);
     const float o = Lsum > 0.f ? (acc + p.lora_scale * res) / Lsum : 0.f;
-    E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + dim, o);
+    E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + tid, o);
   }
 }
 
@@ -513,12 +552,16 @@ hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agent
 }
 
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s) {
-  if (p.head_dim > 2 * 128 || p.rank > 64) return hipErrorInvalidValue;
-  dim3 grid(p.n_agents * p.num_q_heads, kCombineSplit);
-  if (dtype == FORKKV_DTYPE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+  if (p.head_dim > 256 || p.rank > 64) return hipErrorInvalidValue;
+  dim3 grid(p.n_agents * p.num_q_heads);
+  const bool wide = p.head_dim > 128;
+  if (dtype == FORKKV_DTYPE_F32) {
+    if (wide) hipLaunchKernelGGL((combine_kernel<float, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<float, 1>), grid, dim3(256), 0, s, p);
+  } else {
+    if (wide) hipLaunchKernelGGL((combine_kernel<uint16_t, 2>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<uint16_t, 1>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

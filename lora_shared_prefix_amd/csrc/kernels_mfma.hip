@@ -112,7 +112,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int col = lane & 15, g4 = lane >> 4;
   const int G = p.group, Hq = p.num_q_heads;
   const int32_t* it = p.plan + p.off_items + item * kItemInts;
-  const int lp0 = it[0], np = it[1], na = it[2], slot_base = it[3];
+  const int lp0 = it[0], np = it[1], na = it[2];
   const int n_groups = (na + A - 1) / A;
   const int n_sub = kWaves / n_groups;  // >= 1 (the plan keeps na <= 4A)
   const int gi = w % n_groups, si = w / n_groups;
@@ -224,8 +224,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     U2 rk[A], rv[A];
     bool ok;
   };
-  // Page ids of this wave's sub-range (at most 64 pages: the plan keeps items within
-  // 64 pages): lane i holds the ids of page lpa + i, so a page's ids come from a
+  // Page ids of this wave's sub-range (at most 64 pages: the plan sizes items so that no
+  // wave gets more): lane i holds the ids of page lpa + i, so a page's ids come from a
   // readlane instead of a memory round trip.
   const int id_base = lpa;
   int vb = -1;
@@ -435,7 +435,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     m_run = M;
   }
   if (!col_ok) return;
-  const size_t row = (size_t(slot_base) + j0 + jc) * Hq + h * G + col % G;
+  const size_t row = size_t(it[4 + kItemAgents + j0 + jc]) * Hq + h * G + col % G;
   for (int t = 0; t < 8; ++t)
     *reinterpret_cast<float4*>(p.ws_acc + row * kD + 16 * t + 4 * g4) =
         make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
@@ -757,6 +757,8 @@ bool mfma_supported(int dtype, int head_dim, int rank, int group) {
   return dtype == FORKKV_DTYPE_BF16 && head_dim == kD && rank == kR &&
          agents_per_group(group) >= 1;
 }
+
+int mfma_agents_per_wave(int group) { return agents_per_group(group); }
 
 // Agents per plan item: up to four groups of agents_per_group(G) each, at most 8.
 int mfma_group_agents(int group) {

@@ -61,9 +61,7 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   }
   if (o.max_agents_per_item < 0 || o.pages_per_item < 0) return FORKKV_EINVAL;
   if (o.max_agents_per_item > 0) cap = std::min(cap, o.max_agents_per_item);
-  int ppi = o.pages_per_item > 0 ? o.pages_per_item : (kernel == FORKKV_KERNEL_MFMA ? 32 : 16);
-  // the MFMA kernel keeps a wave's page ids in one register: at most 64 pages per item
-  if (kernel == FORKKV_KERNEL_MFMA) ppi = std::min(ppi, 64);
+  int ppi = o.pages_per_item > 0 ? o.pages_per_item : 16;
 
   // 1. Maximal runs of logical pages with an identical set of agents sharing the page.
   std::vector<Run> runs;
@@ -91,24 +89,54 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
     open.swap(next_open);
   }
 
-  // 2. Cut runs into items: agent chunks of <= cap, page chunks of <= ppi.
+  // 2. Cut runs into items: agent chunks of <= cap, page chunks of <= item_pages(chunk).
+  //
+  // The MFMA kernel runs four waves per item: the chunk's agents form n_groups groups of
+  // up to A agents and the item's pages are split into 4 / n_groups sub-ranges, one per
+  // wave.  Its items are sized by pages per wave (at most 64: a wave keeps its page ids in
+  // one register) so that the whole grid fits one round of resident waves when possible
+  // (256 compute units x 8 waves on MI355X) with every wave doing about the same work.
+  const int A = kernel == FORKKV_KERNEL_MFMA ? forkkv::mfma_agents_per_wave(group_q) : 0;
+  auto n_sub_of = [&](int32_t na) { return 4 / ((na + A - 1) / A); };
+  int32_t ppw = 0;  // MFMA: pages per wave
+  if (kernel == FORKKV_KERNEL_MFMA) {
+    const int64_t slots = 2048;
+    auto waves_for = [&](int32_t pw) {
+      int64_t wv = 0;
+      for (const Run& r : runs)
+        for (size_t a0 = 0; a0 < r.agents.size(); a0 += cap) {
+          const int32_t na = static_cast<int32_t>(std::min<size_t>(cap, r.agents.size() - a0));
+          const int32_t item_pages = pw * n_sub_of(na);
+          wv += 4 * int64_t((r.lp1 - r.lp0 + item_pages - 1) / item_pages);
+        }
+      return wv * g.num_kv_heads;
+    };
+    if (o.pages_per_item > 0) {
+      ppw = std::max(1, std::min(64, o.pages_per_item));  // fixed split (tuning)
+    } else {
+      ppw = 1;
+      while (ppw < 64 && waves_for(ppw) > slots) ++ppw;
+    }
+  }
   std::vector<int32_t> items;
-  std::vector<std::vector<int32_t>> agent_slots(n);
+  std::vector<int32_t> per_agent(n, 0);  // partials per agent (slot numbering below)
   int32_t n_slots = 0;
   for (const Run& r : runs) {
     for (size_t a0 = 0; a0 < r.agents.size(); a0 += cap) {
       const int32_t na = static_cast<int32_t>(std::min<size_t>(cap, r.agents.size() - a0));
-      for (int32_t lp = r.lp0; lp < r.lp1; lp += ppi) {
-        const int32_t np = std::min(ppi, r.lp1 - lp);
+      const int32_t item_pages = kernel == FORKKV_KERNEL_MFMA ? ppw * n_sub_of(na) : ppi;
+      for (int32_t lp = r.lp0; lp < r.lp1; lp += item_pages) {
+        const int32_t np = std::min(item_pages, r.lp1 - lp);
         int32_t it[kItemInts];
         std::fill(it, it + kItemInts, -1);
         it[0] = lp;
         it[1] = np;
         it[2] = na;
-        it[3] = n_slots;
+        it[3] = 0;
         for (int32_t j = 0; j < na; ++j) {
-          it[4 + j] = r.agents[a0 + j];
-          agent_slots[r.agents[a0 + j]].push_back(n_slots + j);
+          const int32_t a = r.agents[a0 + j];
+          it[4 + j] = a;
+          it[4 + kItemAgents + j] = per_agent[a]++;  // index within the agent, for now
         }
         n_slots += na;
         items.insert(items.end(), it, it + kItemInts);
@@ -116,6 +144,13 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
     }
   }
   const int32_t n_items = static_cast<int32_t>(items.size() / kItemInts);
+  // slots of agent a: slot_ptr[a] + (its index), consecutive per agent
+  std::vector<int32_t> slot_ptr(n + 1, 0);
+  for (int32_t a = 0; a < n; ++a) slot_ptr[a + 1] = slot_ptr[a] + per_agent[a];
+  for (int32_t i = 0; i < n_items; ++i) {
+    int32_t* it = items.data() + size_t(i) * kItemInts;
+    for (int32_t j = 0; j < it[2]; ++j) it[4 + kItemAgents + j] += slot_ptr[it[4 + j]];
+  }
 
   forkkv_plan* pl = new (std::nothrow) forkkv_plan();
   if (!pl) return FORKKV_ENOMEM;
@@ -145,14 +180,8 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   b[forkkv::kHdrOffLens] = static_cast<int32_t>(b.size());
   for (int32_t a = 0; a < n; ++a) b.push_back(S[a]->len);
   b[forkkv::kHdrOffSlotPtr] = static_cast<int32_t>(b.size());
-  int32_t acc = 0;
-  b.push_back(0);
-  for (int32_t a = 0; a < n; ++a) {
-    acc += static_cast<int32_t>(agent_slots[a].size());
-    b.push_back(acc);
-  }
-  b[forkkv::kHdrOffSlotList] = static_cast<int32_t>(b.size());
-  for (int32_t a = 0; a < n; ++a) b.insert(b.end(), agent_slots[a].begin(), agent_slots[a].end());
+  b.insert(b.end(), slot_ptr.begin(), slot_ptr.end());
+  b[forkkv::kHdrOffSlotList] = static_cast<int32_t>(b.size());  // empty: slots are ranges
 
   const size_t rows = size_t(n_slots) * num_q_heads;
   pl->ws_off_acc = align256(rows * 2 * sizeof(float));

@@ -14,7 +14,7 @@ from oracle import PoolError, PoolModel
 from tests.pool_scenarios import fanout_ops, read_table
 from workloads import CONFIGS, chunk_ops, pool_ops
 
-ITEM_INTS = 12
+ITEM_INTS = 20   # lp0, pages, agents, unused, 8 agent ids, 8 slot ids
 
 
 def _pair(nb, nr, perm_b=None, perm_r=None, Hkv=1, d=16, r=4):
@@ -163,13 +163,14 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
     per_agent = {a: [] for a in range(n_agents)}
     for i in range(n_items):
         it = blob[off_items + i * ITEM_INTS: off_items + (i + 1) * ITEM_INTS]
-        lp0, npg, na, sb = it[:4]
+        lp0, npg, na = it[:3]
         agents = it[4:4 + na]
+        slots = it[12:12 + na]
         assert 1 <= na <= group_cap and npg >= 1 and agents == sorted(agents)
-        for j, a in enumerate(agents):
-            assert sb + j not in slots_seen
-            slots_seen.add(sb + j)
-            per_agent[a].append(sb + j)
+        for a, sl in zip(agents, slots):
+            assert sl not in slots_seen
+            slots_seen.add(sl)
+            per_agent[a].append(sl)
         for lpg in range(lp0, lp0 + npg):
             pages = {bt[a][lpg] for a in agents}
             assert len(pages) == 1 and -1 not in pages
@@ -178,15 +179,18 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
                 covered[(a, lpg)] = i
     want = {(a, lpg) for a in range(n_agents) for lpg in range(-(-lens[a] // 16))}
     assert set(covered) == want
-    # pages aliased by several agents are never split across items of the same agent chunk
+    # the partial slots of each agent are exactly the range slot_ptr[a] .. slot_ptr[a+1]
+    assert blob[off_ptr] == 0 and off_list == off_ptr + n_agents + 1
     for a in range(n_agents):
         ptr0, ptr1 = blob[off_ptr + a], blob[off_ptr + a + 1]
-        assert sorted(blob[off_list + ptr0: off_list + ptr1]) == sorted(per_agent[a])
+        assert sorted(per_agent[a]) == list(range(ptr0, ptr1))
     assert slots_seen == set(range(n_slots))
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3])
-@pytest.mark.parametrize("kernel", [fk.KERNEL_GENERIC])
+@pytest.mark.parametrize("idx,kernel", [(0, fk.KERNEL_GENERIC), (1, fk.KERNEL_GENERIC),
+                                        (2, fk.KERNEL_GENERIC), (3, fk.KERNEL_GENERIC),
+                                        (1, fk.KERNEL_MFMA), (2, fk.KERNEL_MFMA),
+                                        (3, fk.KERNEL_MFMA)])
 def test_plan_covers_workloads(idx, kernel):
     cfg = CONFIGS[idx]
     lp = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim, cfg.rank,
@@ -199,8 +203,18 @@ def test_plan_covers_workloads(idx, kernel):
     _check_plan(lp, lp.tables(hs, mp), hs, plan, 8)
     # shared pages are read once per agent chunk, not once per agent
     blob = plan.blob()
-    shared_items = [blob[16 + i * ITEM_INTS + 2] for i in range(blob[2])]
-    assert max(shared_items) == min(cfg.agents_per_session, 8 if kernel == fk.KERNEL_GENERIC else 4)
+    items = [blob[16 + i * ITEM_INTS: 16 + (i + 1) * ITEM_INTS] for i in range(blob[2])]
+    assert max(it[2] for it in items) == min(cfg.agents_per_session, 8)
+    if kernel == fk.KERNEL_MFMA:
+        # four waves per item: agents in groups of A = min(4, 16 // G), pages split over the
+        # remaining waves; no wave may get more than 64 pages, and the grid fits one round
+        A = min(4, 16 // cfg.group)
+        waves = 0
+        for it in items:
+            n_sub = 4 // (-(-it[2] // A))
+            assert -(-it[1] // n_sub) <= 64
+            waves += 4
+        assert waves * cfg.num_kv_heads <= 2048 or cfg.name.startswith("qwen25")
 
 
 @pytest.mark.parametrize("seed", range(6))
