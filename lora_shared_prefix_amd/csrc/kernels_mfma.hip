@@ -27,6 +27,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "forkkv_internal.h"
 
@@ -41,19 +42,20 @@ constexpr int kD = 128;       // head dim
 constexpr int kR = 16;        // rank
 constexpr int kWaves = 4;     // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTrigPad = 68;  // padded row of the static in-page trig table (floats)
+constexpr int kTrigPad = 72;  // padded row of the static in-page trig table (fp16)
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // LDS layout (bytes)
 constexpr int kBkBytes = kItemAgents * 8 * 64 * 8;      // [agent][tile][lane][4 bf16]
-constexpr int kTrigBytes = 2 * kPage * kTrigPad * 4;    // cos, sin: [c][j] (scaled by s)
-constexpr int kPageTrigBytes = kWaves * 2 * 64 * 4;     // per wave: cos[64], sin[64]
+constexpr int kTrigBytes = 2 * kPage * kTrigPad * 2;    // cos, sin: [c][j] (scaled by s)
+constexpr int kPageTrigBytes = kWaves * 2 * 64 * 2;     // per wave: cos[64], sin[64]
+constexpr int kQhBytes = kWaves * 4 * 64 * 16;          // per wave: fp16 q, [chunk][lane]
 constexpr int kMergeFloats = 4 + 32 + 4;                // m, l, pad, pad | acc[32] | accr[4]
 constexpr int kMergeBytes = kWaves * 64 * kMergeFloats * 4;
 constexpr int kBkRawBytes = kItemAgents * kR * kD * 2;  // B_k rows before the permutation
-constexpr int kLdsMain = kBkBytes + (kTrigBytes + kPageTrigBytes > kBkRawBytes
-                                         ? kTrigBytes + kPageTrigBytes : kBkRawBytes);
+constexpr int kLdsMain = kBkBytes + (kTrigBytes + kPageTrigBytes + kQhBytes > kBkRawBytes
+                                         ? kTrigBytes + kPageTrigBytes + kQhBytes : kBkRawBytes);
 constexpr int kLdsBytes = kLdsMain > kMergeBytes ? kLdsMain : kMergeBytes;
 
 __device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
@@ -62,6 +64,46 @@ __device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
 __device__ __forceinline__ f4 mfma32(bf8 a, bf8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 h8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f4 mfma32h(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+union H8 {
+  h2 p[4];
+  h8 v;
+  uint4 u;
+};
+// Two floats -> fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ h2 pack_f16x2(float lo, float hi) {
+  const float2 f = {lo, hi};
+  typedef float fv2 __attribute__((ext_vector_type(2)));
+  return __builtin_convertvector(fv2{f.x, f.y}, h2);
+}
+// a * b - c * d and a * b + c * d with one fixed rounding sequence (c * d rounded, then one
+// fused multiply-add), so every instantiation of the kernels rounds the same way.
+__device__ __forceinline__ h2 mul_sub2(h2 a, h2 b, h2 c, h2 d) {
+#pragma clang fp contract(off)
+  const h2 t = c * d;
+  return __builtin_elementwise_fma(a, b, -t);
+}
+__device__ __forceinline__ h2 mul_add2(h2 a, h2 b, h2 c, h2 d) {
+#pragma clang fp contract(off)
+  const h2 t = c * d;
+  return __builtin_elementwise_fma(a, b, t);
+}
+__device__ __forceinline__ float mul_sub(float a, float b, float c, float d) {
+#pragma clang fp contract(off)
+  const float t = c * d;
+  return __builtin_fmaf(a, b, -t);
+}
+__device__ __forceinline__ float mul_add(float a, float b, float c, float d) {
+#pragma clang fp contract(off)
+  const float t = c * d;
+  return __builtin_fmaf(a, b, t);
+}
+// Zero residual page, read in place of a page a sequence does not have.
+__device__ __align__(16) uint16_t g_zero_res[2 * kPage * kR];
 
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float fl2 __attribute__((ext_vector_type(2)));
@@ -93,7 +135,7 @@ __device__ __forceinline__ int perm_dim(int T, int m) {
   return 32 * (T >> 1) + 8 * (m >> 2) + 4 * (T & 1) + (m & 3);
 }
 
-template <int A, bool kPipe>  // agents per group (columns = agents x G <= 16); prefetch
+template <int A>  // agents per group (columns = agents x G <= 16)
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeParams p, int n_items) {
   __shared__ __align__(16) unsigned char lds[kLdsBytes];
@@ -127,9 +169,11 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int n = Hkv * kD;
 
   uint2* bkl = reinterpret_cast<uint2*>(lds);                          // [j][T][lane]
-  float* trig_c = reinterpret_cast<float*>(lds + kBkBytes);            // [c][kTrigPad]
-  float* trig_s = trig_c + kPage * kTrigPad;
-  float* ptrig = reinterpret_cast<float*>(lds + kBkBytes + kTrigBytes) + w * 128;
+  _Float16* trig_c = reinterpret_cast<_Float16*>(lds + kBkBytes);      // [c][kTrigPad]
+  _Float16* trig_s = trig_c + kPage * kTrigPad;
+  _Float16* ptrig = reinterpret_cast<_Float16*>(lds + kBkBytes + kTrigBytes) + w * 128;
+  uint4* qh_lds =
+      reinterpret_cast<uint4*>(lds + kBkBytes + kTrigBytes + kPageTrigBytes) + w * 4 * 64;
 
   // ---- stage B_k slices (A-operand order) and the in-page trig table ----------------------
   // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
@@ -164,8 +208,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     const float ang = static_cast<float>(c * exp2(-2.0 * j / kD * log2_theta));
     float sv, cv;
     sincosf(ang, &sv, &cv);
-    trig_c[c * kTrigPad + j] = cv * p.lora_scale;
-    trig_s[c * kTrigPad + j] = sv * p.lora_scale;
+    trig_c[c * kTrigPad + j] = static_cast<_Float16>(cv * p.lora_scale);
+    trig_s[c * kTrigPad + j] = static_cast<_Float16>(sv * p.lora_scale);
   }
   __syncthreads();
 
@@ -182,6 +226,19 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       t.u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
       qv[c] = t.b;
     }
+  }
+  // the rotated residual keys are formed in fp16 (packed arithmetic) and scored against
+  // an fp16 copy of q; the shared base tile is scored in bf16
+  // an fp16 copy of q; the shared base tile is scored in bf16.  The fp16 copy lives in
+  // LDS (this wave's slot, lane-linear) and is read where it is used.
+  for (int c = 0; c < 4; ++c) {
+    U4 t;
+    t.b = qv[c];
+    const uint32_t wds[4] = {t.u.x, t.u.y, t.u.z, t.u.w};
+    H8 hq;
+    for (int e = 0; e < 4; ++e)
+      hq.p[e] = pack_f16x2(__uint_as_float(wds[e] << 16), __uint_as_float(wds[e] & 0xffff0000u));
+    qh_lds[c * 64 + lane] = hq.u;
   }
   int agent[A], rlen[A];
   for (int j = 0; j < A; ++j) {
@@ -216,13 +273,17 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     step_s = static_cast<float>(sv);
   }
 
-  // Page buffers: the loads of page lp + 1 are issued before page lp is computed
-  // (software pipelining; two register buffers, used alternately).
-  struct PageBuf {
+  // Page buffers.  The key-side operands of page lp + 1 (base key tile, residual keys) are
+  // loaded while page lp is computed (two register buffers, used alternately); the
+  // value-side operands of page lp are loaded when its computation starts and used last.
+  struct KBuf {
     U4 kt[4];
+    U2 rk[A];
+    int bp;
+  };
+  struct VBuf {
     U2 vt[8];
-    U2 rk[A], rv[A];
-    bool ok;
+    U2 rv[A];
   };
   // Page ids of this wave's sub-range (at most 64 pages: the plan sizes items so that no
   // wave gets more): lane i holds the ids of page lpa + i, so a page's ids come from a
@@ -239,122 +300,157 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   };
   if (lpa < lpb) fetch_ids();
 
-  auto load_page = [&](int lp, PageBuf& B) {
-    const int bp = __builtin_amdgcn_readlane(vb, lp - id_base);
-    B.ok = bp >= 0 && bp < p.num_bpages;  // never read outside the pool
-    const size_t pg = B.ok ? bp : 0;
-    const uint16_t* kt_base = bcache + (pg * 2 * Hkv + h) * tile;
-    const uint16_t* vt_base = bcache + (pg * 2 * Hkv + Hkv + h) * tile;
+  // residual page of agent j at page lp (the zero page where the sequence has none)
+  auto res_page = [&](int lp, int j) -> const uint16_t* {
+    const int rp = __builtin_amdgcn_readlane(vr[j], lp - id_base);
+    const bool ok = rp >= 0 && rp < p.num_rpages;
+    return ok ? rcache + size_t(rp) * 2 * kPage * kR : g_zero_res;
+  };
+  // The page routines take the group's agent count NA as a compile-time constant, so the
+  // per-agent work is straight-line code.
+  auto load_k = [&](int lp, KBuf& B, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    B.bp = __builtin_amdgcn_readlane(vb, lp - id_base);
+    const bool ok = B.bp >= 0 && B.bp < p.num_bpages;  // never read outside the pool
+    const uint16_t* kt_base = bcache + (size_t(ok ? B.bp : 0) * 2 * Hkv + h) * tile;
     // tiles are stored in operand order: lane l's piece is the l-th 16 B (K) / 8 B (V)
     for (int c = 0; c < 4; ++c)
       B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + 512 * c + 8 * lane);
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      B.rk[j].u = *reinterpret_cast<const uint2*>(res_page(lp, j) + 4 * lane);
+  };
+  auto load_v = [&](int lp, int bp, VBuf& V, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    const uint16_t* vt_base = bcache + (size_t(bp) * 2 * Hkv + Hkv + h) * tile;
     for (int t = 0; t < 8; ++t)
-      B.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
-    for (int j = 0; j < A; ++j) {
-      const int rp = __builtin_amdgcn_readlane(vr[j], lp - id_base);
-      const bool ok = rp >= 0 && rp < p.num_rpages;
-      const uint16_t* rb = rcache + size_t(ok ? rp : 0) * 2 * kPage * kR;
-      B.rk[j].u = *reinterpret_cast<const uint2*>(rb + 4 * lane);
-      B.rv[j].u = *reinterpret_cast<const uint2*>(rb + kPage * kR + 4 * lane);
-      if (!ok) {
-        B.rk[j].u = make_uint2(0, 0);
-        B.rv[j].u = make_uint2(0, 0);
-      }
-    }
+      V.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      V.rv[j].u = *reinterpret_cast<const uint2*>(res_page(lp, j) + kPage * kR + 4 * lane);
   };
 
-  auto compute_page = [&](int lp, PageBuf& B) {
-    if (!B.ok) return;
-    int vrows = 0;
-    for (int j = 0; j < A; ++j)
-      if (j < na_g) vrows = max(vrows, min(kPage, rlen[j] - lp * kPage));
+  auto compute_page = [&](int lp, KBuf& B, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    if (!(B.bp >= 0 && B.bp < p.num_bpages)) return;  // wave-uniform
+    VBuf V;
+    load_v(lp, B.bp, V, na_c);
+    int vrows = 0, minrows = kPage;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      vrows = max(vrows, min(kPage, rlen[j] - lp * kPage));
+      minrows = min(minrows, rlen[j] - lp * kPage);
+    }
     // Rows no column may read are zeroed: their bytes are arbitrary (even NaN).
     const bool row_ok = col < vrows;  // this lane's key row (tok = col) in the A operands
     const int tv = vrows - 4 * g4;    // valid tokens among this lane's 4 (B / V operands)
-    auto mask4 = [&](uint2 v) {
-      if (tv < 4) {
-        if (tv <= 0) v.x = 0;
-        else if (tv == 1) v.x &= 0xffffu;
-        if (tv <= 2) v.y = 0;
-        else if (tv == 3) v.y &= 0xffffu;
-      }
-      return v;
-    };
-    if (!row_ok) {
+    if (vrows < kPage && !row_ok) {   // (vrows < 16 only on a sequence's last page)
       for (int c = 0; c < 4; ++c) B.kt[c].u = make_uint4(0, 0, 0, 0);
-      for (int j = 0; j < A; ++j) B.rk[j].u = make_uint2(0, 0);
-    }
-    if (tv < 4) {
-      for (int t = 0; t < 8; ++t) B.vt[t].u = mask4(B.vt[t].u);
-      for (int j = 0; j < A; ++j) B.rv[j].u = mask4(B.rv[j].u);
+      for (int j = 0; j < NA; ++j) B.rk[j].u = make_uint2(0, 0);
     }
 
     // -- RoPE angles of this page: lane j holds cos/sin(t0 * w_j) (see the recurrence) --
-    ptrig[lane] = pc;
-    ptrig[64 + lane] = ps;
+    ptrig[lane] = static_cast<_Float16>(pc);
+    ptrig[64 + lane] = static_cast<_Float16>(ps);
     {  // advance to the next page: rotate by 16 * w_j
-      const float c = pc * step_c - ps * step_s;
-      ps = ps * step_c + pc * step_s;
+      const float c = mul_sub(pc, step_c, ps, step_s);
+      ps = mul_add(ps, step_c, pc, step_s);
       pc = c;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes above have landed
 
-    // -- scores: shared base tile, then per agent the rotated residual --
-    f4 sb = f4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < 4; ++c) sb = mfma32(B.kt[c].b, qv[c], sb);
-    f4 sj[A];
-    for (int j = 0; j < A; ++j) sj[j] = sb;
-    // Dims are handled in two halves: half h covers score chunks h and h + 2, i.e. the
-    // reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.
+    // s * cos / s * sin of (t0 + c) * w_j for j = 32*half + 8*g4 + e (c = this lane's key
+    // row), as fp16 pairs (e, e + 1)
+    h2 ct[2][4], st[2][4];
+#pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // s * cos / s * sin of (t0 + c) * w_j for j = 32*half + 8*g4 + e  (c = this lane's row)
-      float ct[8], st[8];
       const int jb = 32 * half + 8 * g4;
-      for (int e = 0; e < 8; ++e) {
-        const float c0 = ptrig[jb + e], s0 = ptrig[64 + jb + e];
-        const float cc = trig_c[col * kTrigPad + jb + e], ss = trig_s[col * kTrigPad + jb + e];
-        ct[e] = c0 * cc - s0 * ss;
-        st[e] = s0 * cc + c0 * ss;
-      }
-      const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
-      for (int j = 0; j < A; ++j) {
-        if (j >= na_g) break;
-        const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
-        f4 d[4];
-        for (int u = 0; u < 4; ++u) {
-          U2 a;
-          a.u = bkj[Ts[u] * 64];
-          d[u] = mfma16(a.s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
-        }
-        for (int u = 0; u < 2; ++u) {
-          for (int i = 0; i < 4; ++i) {
-            const float x = d[u][i], y = d[u + 2][i];
-            const float c = ct[4 * u + i], sn = st[4 * u + i];
-            d[u][i] = x * c - y * sn;
-            d[u + 2][i] = y * c + x * sn;
-          }
-        }
-        U4 k0, k2;
-        k0.u = make_uint4(pack_bf16x2(d[0][0], d[0][1]), pack_bf16x2(d[0][2], d[0][3]),
-                          pack_bf16x2(d[1][0], d[1][1]), pack_bf16x2(d[1][2], d[1][3]));
-        k2.u = make_uint4(pack_bf16x2(d[2][0], d[2][1]), pack_bf16x2(d[2][2], d[2][3]),
-                          pack_bf16x2(d[3][0], d[3][1]), pack_bf16x2(d[3][2], d[3][3]));
-        sj[j] = mfma32(k0.b, qv[half], sj[j]);
-        sj[j] = mfma32(k2.b, qv[half + 2], sj[j]);
+      H8 c0, s0, cc, ss;
+      c0.u = *reinterpret_cast<const uint4*>(ptrig + jb);
+      s0.u = *reinterpret_cast<const uint4*>(ptrig + 64 + jb);
+      cc.u = *reinterpret_cast<const uint4*>(trig_c + col * kTrigPad + jb);
+      ss.u = *reinterpret_cast<const uint4*>(trig_s + col * kTrigPad + jb);
+      for (int e = 0; e < 4; ++e) {
+        ct[half][e] = mul_sub2(c0.p[e], cc.p[e], s0.p[e], ss.p[e]);
+        st[half][e] = mul_add2(s0.p[e], cc.p[e], c0.p[e], ss.p[e]);
       }
     }
-    f4 ssel = sb;
-    for (int j = 0; j < A; ++j)
+
+    // -- scores: shared base tile, plus for each agent its rotated residual key --
+    f4 sb = f4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) sb = mfma32(B.kt[c].b, qv[c], sb);
+    // Work units u = (half, agent): half h covers score chunks h and h + 2, i.e. the
+    // reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.  The units are
+    // software-pipelined: the reconstruction MFMAs of unit u + 1 are issued before the
+    // rotation arithmetic of unit u, so the matrix core and the vector ALU work together.
+    constexpr int NU = 2 * NA;
+    f4 sj[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) sj[j] = f4{0.f, 0.f, 0.f, 0.f};
+    auto recon = [&](int u, f4 (&d)[4]) {
+      const int half = u / NA, j = u % NA;
+      const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
+      const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
+      for (int k = 0; k < 4; ++k) {
+        U2 a;
+        a.u = bkj[Ts[k] * 64];
+        d[k] = mfma16(a.s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
+      }
+    };
+    auto rotate_score = [&](int u, const f4 (&d)[4]) {
+      const int half = u / NA, j = u % NA;
+      // rotate the partner pairs (tile k, tile k + 2) on packed fp16 values
+      H8 k0, k2;
+      for (int k = 0; k < 2; ++k) {
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const h2 x = pack_f16x2(d[k][2 * q2], d[k][2 * q2 + 1]);
+          const h2 y = pack_f16x2(d[k + 2][2 * q2], d[k + 2][2 * q2 + 1]);
+          const h2 c = ct[half][2 * k + q2], sn = st[half][2 * k + q2];
+          k0.p[2 * k + q2] = mul_sub2(x, c, y, sn);
+          k2.p[2 * k + q2] = mul_add2(y, c, x, sn);
+        }
+      }
+      H8 q0, q2v;
+      q0.u = qh_lds[half * 64 + lane];
+      q2v.u = qh_lds[(half + 2) * 64 + lane];
+      sj[j] = mfma32h(k0.v, q0.v, sj[j]);
+      sj[j] = mfma32h(k2.v, q2v.v, sj[j]);
+    };
+    f4 dA[4], dB[4];
+    recon(0, dA);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (u % 2 == 0) {
+        if (u + 1 < NU) recon(u + 1, dB);
+        rotate_score(u, dA);
+      } else {
+        if (u + 1 < NU) recon(u + 1, dA);
+        rotate_score(u, dB);
+      }
+    }
+    f4 ssel = sj[0];
+#pragma unroll
+    for (int j = 1; j < NA; ++j)
       if (jc == j) ssel = sj[j];
+    ssel += sb;
 
     // -- online softmax over this page's 16 keys, per column (log2 domain) --
     float sc[4];
     float pmax = -INFINITY;
-    for (int i = 0; i < 4; ++i) {
-      const int pos = lp * kPage + 4 * g4 + i;
-      sc[i] = (col_ok && pos < len_col) ? ssel[i] * qscale : -INFINITY;
-      pmax = fmaxf(pmax, sc[i]);
+    if (minrows >= kPage) {
+      // every agent of the group has all 16 keys of the page; columns without an agent
+      // (zero q) only ever touch their own, unwritten, state
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = ssel[i] * qscale;
+        pmax = fmaxf(pmax, sc[i]);
+      }
+    } else {
+      for (int i = 0; i < 4; ++i) {
+        const int pos = lp * kPage + 4 * g4 + i;
+        sc[i] = (col_ok && pos < len_col) ? ssel[i] * qscale : -INFINITY;
+        pmax = fmaxf(pmax, sc[i]);
+      }
     }
     pmax = fmaxf(pmax, shfl_xor(pmax, 16));
     pmax = fmaxf(pmax, shfl_xor(pmax, 32));
@@ -379,35 +475,45 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
     U2 pb;
     pb.u = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
-    for (int t = 0; t < 8; ++t) acc[t] = mfma16(B.vt[t].s, pb.s, acc[t]);
-    for (int j = 0; j < A; ++j) {
-      if (j >= na_g) break;
+    if (tv < 4) {  // (only on a sequence's last page)
+      auto mask4 = [&](uint2 v) {
+        if (tv <= 0) v.x = 0;
+        else if (tv == 1) v.x &= 0xffffu;
+        if (tv <= 2) v.y = 0;
+        else if (tv == 3) v.y &= 0xffffu;
+        return v;
+      };
+      for (int t = 0; t < 8; ++t) V.vt[t].u = mask4(V.vt[t].u);
+      for (int j = 0; j < NA; ++j) V.rv[j].u = mask4(V.rv[j].u);
+    }
+    for (int t = 0; t < 8; ++t) acc[t] = mfma16(V.vt[t].s, pb.s, acc[t]);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
       U2 pj;
       pj.u = (jc == j) ? pb.u : make_uint2(0, 0);
-      accr = mfma16(B.rv[j].s, pj.s, accr);
+      accr = mfma16(V.rv[j].s, pj.s, accr);
     }
   };
 
-  if constexpr (kPipe) {
+  auto run_pages = [&](auto na_c) {
     // The prefetch is issued unconditionally (past the end it re-reads the last page, an
     // L2 hit) so that every wait below only covers the older buffer's loads.
-    PageBuf buf0, buf1;
-    if (lpa < lpb) {
-      load_page(lpa, buf0);
-      for (int lp = lpa; lp < lpb; lp += 2) {
-        load_page(min(lp + 1, lpb - 1), buf1);
-        compute_page(lp, buf0);
-        if (lp + 1 >= lpb) break;
-        load_page(min(lp + 2, lpb - 1), buf0);
-        compute_page(lp + 1, buf1);
-      }
+    KBuf buf0, buf1;
+    load_k(lpa, buf0, na_c);
+    for (int lp = lpa; lp < lpb; lp += 2) {
+      load_k(min(lp + 1, lpb - 1), buf1, na_c);
+      compute_page(lp, buf0, na_c);
+      if (lp + 1 >= lpb) break;
+      load_k(min(lp + 2, lpb - 1), buf0, na_c);
+      compute_page(lp + 1, buf1, na_c);
     }
-  } else {
-    for (int lp = lpa; lp < lpb; ++lp) {
-      PageBuf buf;
-      load_page(lp, buf);
-      compute_page(lp, buf);
-    }
+  };
+  if (lpa < lpb) {
+    // na_g is wave-uniform: one branch selects the straight-line variant
+    if (na_g >= A) run_pages(std::integral_constant<int, A>{});
+    if constexpr (A > 3) if (na_g == 3) run_pages(std::integral_constant<int, 3>{});
+    if constexpr (A > 2) if (na_g == 2) run_pages(std::integral_constant<int, 2>{});
+    if constexpr (A > 1) if (na_g == 1) run_pages(std::integral_constant<int, 1>{});
   }
 
   // ---- merge the sub-range partials of each group (LSE rule), write split-K partials ----
@@ -767,22 +873,20 @@ int mfma_group_agents(int group) {
 }
 
 
-template <bool kPipe>
-hipError_t launch_decode_mfma_t(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   const int A = agents_per_group(p.group);
   const int n_items = p.n_items;
   const int blocks = 8 * p.num_kv_heads * ((n_items + 7) / 8);
   switch (A) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<2, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<1, kPipe>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<2>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<1>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// FORKKV_DECODE_PIPE=0 selects the variant without register prefetch (tuning aid).
 bool prefill_mfma_enabled() { return true; }
 
 hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t*, hipStream_t s) {
@@ -791,15 +895,6 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t*, hipStream
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3(blocks), dim3(kPfThreads), 0, s, p, n_rblocks);
   return hipGetLastError();
 }
-
-hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
-  static const bool pipe = [] {
-    const char* e = std::getenv("FORKKV_DECODE_PIPE");
-    return !(e && e[0] == '0');
-  }();
-  return pipe ? launch_decode_mfma_t<true>(p, s) : launch_decode_mfma_t<false>(p, s);
-}
-
 
 
 }  // namespace forkkv
