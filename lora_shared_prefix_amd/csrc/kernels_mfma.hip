@@ -117,6 +117,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column's rows): two
+// butterfly steps with the cross-row lane swaps (no LDS round trip)
+__device__ __forceinline__ float max_over_rows(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 union U4 {
   uint4 u;
@@ -280,6 +290,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     U4 kt[4];
     U2 rk[A];
     int bp;
+    const uint16_t* rb[A];  // residual pages of the group's agents (wave-uniform)
   };
   struct VBuf {
     U2 vt[8];
@@ -291,50 +302,55 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int id_base = lpa;
   int vb = -1;
   int vr[A];
+  // Ids are checked here, once: out-of-pool ids become -1 (page skipped / zero residual).
   auto fetch_ids = [&]() {
     const int lpi = id_base + lane;
     const bool in = lpi < lpb;
     vb = in ? p.btab[size_t(agent[0]) * p.max_pages + lpi] : -1;
-    for (int j = 0; j < A; ++j)
+    if (vb >= p.num_bpages) vb = -1;
+    for (int j = 0; j < A; ++j) {
       vr[j] = (in && j < na_g) ? p.rtab[size_t(agent[j]) * p.max_pages + lpi] : -1;
+      if (vr[j] >= p.num_rpages) vr[j] = -1;
+    }
   };
   if (lpa < lpb) fetch_ids();
+  const uint16_t* const zero_res = g_zero_res;
 
   // residual page of agent j at page lp (the zero page where the sequence has none)
   auto res_page = [&](int lp, int j) -> const uint16_t* {
     const int rp = __builtin_amdgcn_readlane(vr[j], lp - id_base);
-    const bool ok = rp >= 0 && rp < p.num_rpages;
-    return ok ? rcache + size_t(rp) * 2 * kPage * kR : g_zero_res;
+    return rp >= 0 ? rcache + size_t(rp) * 2 * kPage * kR : zero_res;
   };
   // The page routines take the group's agent count NA as a compile-time constant, so the
   // per-agent work is straight-line code.
   auto load_k = [&](int lp, KBuf& B, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
     B.bp = __builtin_amdgcn_readlane(vb, lp - id_base);
-    const bool ok = B.bp >= 0 && B.bp < p.num_bpages;  // never read outside the pool
-    const uint16_t* kt_base = bcache + (size_t(ok ? B.bp : 0) * 2 * Hkv + h) * tile;
+    const uint16_t* kt_base = bcache + (size_t(max(B.bp, 0)) * 2 * Hkv + h) * tile;
     // tiles are stored in operand order: lane l's piece is the l-th 16 B (K) / 8 B (V)
     for (int c = 0; c < 4; ++c)
       B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + 512 * c + 8 * lane);
 #pragma unroll
-    for (int j = 0; j < NA; ++j)
-      B.rk[j].u = *reinterpret_cast<const uint2*>(res_page(lp, j) + 4 * lane);
+    for (int j = 0; j < NA; ++j) {
+      B.rb[j] = res_page(lp, j);
+      B.rk[j].u = *reinterpret_cast<const uint2*>(B.rb[j] + 4 * lane);
+    }
   };
-  auto load_v = [&](int lp, int bp, VBuf& V, auto na_c) {
+  auto load_v = [&](const KBuf& B, VBuf& V, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    const uint16_t* vt_base = bcache + (size_t(bp) * 2 * Hkv + Hkv + h) * tile;
+    const uint16_t* vt_base = bcache + (size_t(B.bp) * 2 * Hkv + Hkv + h) * tile;
     for (int t = 0; t < 8; ++t)
       V.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
 #pragma unroll
     for (int j = 0; j < NA; ++j)
-      V.rv[j].u = *reinterpret_cast<const uint2*>(res_page(lp, j) + kPage * kR + 4 * lane);
+      V.rv[j].u = *reinterpret_cast<const uint2*>(B.rb[j] + kPage * kR + 4 * lane);
   };
 
   auto compute_page = [&](int lp, KBuf& B, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    if (!(B.bp >= 0 && B.bp < p.num_bpages)) return;  // wave-uniform
+    if (B.bp < 0) return;  // wave-uniform
     VBuf V;
-    load_v(lp, B.bp, V, na_c);
+    load_v(B, V, na_c);
     int vrows = 0, minrows = kPage;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
@@ -388,15 +404,16 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     f4 sj[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) sj[j] = f4{0.f, 0.f, 0.f, 0.f};
-    auto recon = [&](int u, f4 (&d)[4]) {
+    // B_k operands of a unit (four 8-byte LDS reads), fetched one unit before their use
+    auto bk_ops = [&](int u, U2 (&a)[4]) {
       const int half = u / NA, j = u % NA;
       const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
       const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
-      for (int k = 0; k < 4; ++k) {
-        U2 a;
-        a.u = bkj[Ts[k] * 64];
-        d[k] = mfma16(a.s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
-      }
+      for (int k = 0; k < 4; ++k) a[k].u = bkj[Ts[k] * 64];
+    };
+    auto recon = [&](int u, const U2 (&a)[4], f4 (&d)[4]) {
+      const int j = u % NA;
+      for (int k = 0; k < 4; ++k) d[k] = mfma16(a[k].s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
     };
     auto rotate_score = [&](int u, const f4 (&d)[4]) {
       const int half = u / NA, j = u % NA;
@@ -418,14 +435,19 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       sj[j] = mfma32h(k2.v, q2v.v, sj[j]);
     };
     f4 dA[4], dB[4];
-    recon(0, dA);
+    U2 oA[4], oB[4];
+    bk_ops(0, oA);
+    if (NU > 1) bk_ops(1, oB);
+    recon(0, oA, dA);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       if (u % 2 == 0) {
-        if (u + 1 < NU) recon(u + 1, dB);
+        if (u + 2 < NU) bk_ops(u + 2, oA);
+        if (u + 1 < NU) recon(u + 1, oB, dB);
         rotate_score(u, dA);
       } else {
-        if (u + 1 < NU) recon(u + 1, dA);
+        if (u + 2 < NU) bk_ops(u + 2, oB);
+        if (u + 1 < NU) recon(u + 1, oA, dA);
         rotate_score(u, dB);
       }
     }
@@ -452,8 +474,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         pmax = fmaxf(pmax, sc[i]);
       }
     }
-    pmax = fmaxf(pmax, shfl_xor(pmax, 16));
-    pmax = fmaxf(pmax, shfl_xor(pmax, 32));
+    pmax = max_over_rows(pmax);
     // The reference maximum m_run only moves when a column's page maximum exceeds it by
     // more than 8 (log2 units): probabilities then stay below 2^8 and the rescale of the
     // accumulators (acc AND acc_r, by the same factor) is skipped on almost every page.
