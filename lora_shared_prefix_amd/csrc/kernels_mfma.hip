@@ -774,21 +774,25 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       }
     }
     U4 pb[2];  // P^T operands, K = 32 keys: elements 0..3 page 0, 4..7 page 1
+    // Both pages exist and lie entirely before the chunk (every key precedes every query):
+    // no mask at all.  Rows past the chunk have zero q and are never written, so they need
+    // none either.  (Wave-uniform.)
+    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < start;
     for (int rt = 0; rt < 2; ++rt) {
       float sc[8], pmax = -INFINITY;
-      for (int pgi = 0; pgi < 2; ++pgi) {
-        const int lp = 2 * it + pgi;
-        // pages entirely before the chunk need no causal mask (every key <= start)
-        const bool causal = lp * kPage + kPage - 1 > start;
-        for (int i = 0; i < 4; ++i) {
-          const int pos = lp * kPage + 4 * g4 + i;
-          const bool ok = rok[rt] && lp < lp_end && (!causal || pos <= qpos[rt]);
-          sc[4 * pgi + i] = ok ? sc4[pgi][rt][i] * qscale : -INFINITY;
-          pmax = fmaxf(pmax, sc[4 * pgi + i]);
+      if (unmasked) {
+        for (int pgi = 0; pgi < 2; ++pgi)
+          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[pgi][rt][i] * qscale;
+      } else {
+        for (int pgi = 0; pgi < 2; ++pgi) {
+          const int lp = 2 * it + pgi;
+          const int lim = lp < lp_end ? qpos[rt] - lp * kPage - 4 * g4 : -1;  // keys i <= lim
+          for (int i = 0; i < 4; ++i)
+            sc[4 * pgi + i] = i <= lim ? sc4[pgi][rt][i] * qscale : -INFINITY;
         }
       }
-      pmax = fmaxf(pmax, shfl_xor(pmax, 16));
-      pmax = fmaxf(pmax, shfl_xor(pmax, 32));
+      for (int e = 0; e < 8; ++e) pmax = fmaxf(pmax, sc[e]);
+      pmax = max_over_rows(pmax);
       const bool grow = pmax > m_run[rt] + 8.f;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = grow ? pmax : m_run[rt];
