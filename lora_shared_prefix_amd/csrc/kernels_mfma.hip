@@ -679,12 +679,20 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     uint4 v;      // quarter tp of page pg's value tile (operand pieces of lanes 2l, 2l+1)
     uint2 rv;     // value-residual operand of page pg (staged by the tp == 0 waves)
   };
-  auto load = [&](int it, PfBuf& B) {
-    const int lp = min(2 * it + pg, lp_end - 1);
+  // Page ids: lane i holds the ids of this wave's page at iteration 64 k + i (block k),
+  // checked against the pools once here; a page's ids then come from a readlane.
+  int ids_b = 0, ids_r = 0;
+  auto fetch_ids = [&](int blk) {
+    const int lp = min(2 * (64 * blk + lane) + pg, lp_end - 1);
     const int bp = p.btab[size_t(a) * p.max_pages + lp];
     const int rp = p.rtab[size_t(a) * p.max_pages + lp];
-    const size_t pb = (bp >= 0 && bp < p.num_bpages) ? bp : 0;
-    const size_t pr = (rp >= 0 && rp < p.num_rpages) ? rp : 0;
+    ids_b = (bp >= 0 && bp < p.num_bpages) ? bp : 0;
+    ids_r = (rp >= 0 && rp < p.num_rpages) ? rp : 0;
+  };
+  auto load = [&](int it, PfBuf& B) {
+    if ((it & 63) == 0) fetch_ids(it >> 6);  // wave-uniform
+    const size_t pb = __builtin_amdgcn_readlane(ids_b, it & 63);
+    const size_t pr = __builtin_amdgcn_readlane(ids_r, it & 63);
     const uint16_t* kt = bcache + (pb * 2 * Hkv + h) * tile;
     const uint16_t* vt = bcache + (pb * 2 * Hkv + Hkv + h) * tile;
     const uint16_t* rb_ = rcache + pr * 2 * kPage * kR;
@@ -750,15 +758,15 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // (tokens 4 g .. 4 g + 3, g = ((2l) mod 64) / 16); its value-residual piece is its own.
     const int last = lp < lp_end ? start + C - lp * kPage : 0;
     uint4 v = B.v;
-    const int tvv = last - 4 * (((2 * lane) & 63) >> 4);
-    m2(tvv, v.x, v.y);
-    m2(tvv, v.z, v.w);
-    s_v[buf][pg][tp * 64 + lane] = v;
-    if (tp == 0) {
-      uint2 rv = B.rv;
+    uint2 rv = B.rv;
+    if (last < kPage) {  // wave-uniform: only the pages at the end of the sequence
+      const int tvv = last - 4 * (((2 * lane) & 63) >> 4);
+      m2(tvv, v.x, v.y);
+      m2(tvv, v.z, v.w);
       m2(last - 4 * g4, rv.x, rv.y);
-      s_rv[buf][pg][lane] = rv;
     }
+    s_v[buf][pg][tp * 64 + lane] = v;
+    if (tp == 0) s_rv[buf][pg][lane] = rv;
   };
 
   auto compute = [&](int it) {
@@ -779,20 +787,20 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // none either.  (Wave-uniform.)
     const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < start;
     for (int rt = 0; rt < 2; ++rt) {
+      // raw scores (q.k); the softmax scale (> 0, log2 units) is applied inside the exp
       float sc[8], pmax = -INFINITY;
       if (unmasked) {
         for (int pgi = 0; pgi < 2; ++pgi)
-          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[pgi][rt][i] * qscale;
+          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[pgi][rt][i];
       } else {
         for (int pgi = 0; pgi < 2; ++pgi) {
           const int lp = 2 * it + pgi;
           const int lim = lp < lp_end ? qpos[rt] - lp * kPage - 4 * g4 : -1;  // keys i <= lim
-          for (int i = 0; i < 4; ++i)
-            sc[4 * pgi + i] = i <= lim ? sc4[pgi][rt][i] * qscale : -INFINITY;
+          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[pgi][rt][i] : -INFINITY;
         }
       }
       for (int e = 0; e < 8; ++e) pmax = fmaxf(pmax, sc[e]);
-      pmax = max_over_rows(pmax);
+      pmax = max_over_rows(pmax) * qscale;
       const bool grow = pmax > m_run[rt] + 8.f;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = grow ? pmax : m_run[rt];
@@ -805,7 +813,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       const float m_ref = fmaxf(m_run[rt], -1e30f);
       float pr[8], sum = 0.f;
       for (int e = 0; e < 8; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_ref);
+        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref));
         sum += pr[e];
       }
       l_run[rt] += sum;
@@ -829,9 +837,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   };
 
   // The register buffer is refilled for iteration it + 1 as soon as iteration it has been
-  // staged, so those loads fly during the whole compute phase.  Two LDS buffers alternate,
-  // so one barrier per iteration suffices: iteration it + 1 stages into the other buffer,
-  // and iteration it + 2 waits behind the next barrier.
+  // staged, so those loads fly during the whole compute phase.  Two LDS
+  // buffers alternate, so one barrier per iteration suffices: iteration it + 1 stages into
+  // the other buffer, and iteration it + 2 waits behind the next barrier.
   PfBuf pb_;
   load(0, pb_);
   anchor(0);
