@@ -43,6 +43,14 @@ def _mfma_ok(dtype, d, r, G):
 _CACHE = {}
 
 
+def _poison(t):
+    """Fill an output tensor with NaN (fp32) or the bf16 NaN bit pattern (16-bit storage)."""
+    if t.dtype == torch.float32:
+        t.fill_(float("nan"))
+    else:
+        t.fill_(0x7FC0)
+
+
 def _workload(idx):
     if idx not in _CACHE:
         cfg = CONFIGS[idx]
@@ -65,6 +73,7 @@ def _run_workload(idx, kernel, sample_agents=None, sample_heads=None, arrays=Non
     assert np.array_equal(bt, b.btab_host) and np.array_equal(rt, b.rtab_host)
     assert list(lens) == list(b.lens)
     sm = 1.0 / np.sqrt(cfg.head_dim)
+    _poison(b.out)  # every output row must be written by the call
     out = b.decode(cfg.lora_scale, sm, cfg.rope_theta)
     torch.cuda.synchronize()
     g = gpu_values(out, cfg.dtype)
@@ -172,6 +181,7 @@ def test_ragged_tiny_batches(seed, dtype, kernel):
     got_pool = b.bcache.cpu().numpy()
     got_pool = got_pool.view(np.uint16) if dtype == "bf16" else got_pool
     assert np.array_equal(got_pool.view(np.uint8), host_after.view(np.uint8))
+    _poison(b.out)  # every output row must be written by the call
     out = b.decode(case["lora_scale"], case["sm_scale"], case["theta"])
     torch.cuda.synchronize()
     ref = decode_attention(Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=2, head_dim=d,
@@ -248,6 +258,30 @@ def test_sharing_invariance():
     torch.cuda.synchronize()
     assert_close(gpu_values(o1, "bf16"), gpu_values(o2, "bf16"), "sharing invariance",
                  max_abs=2e-3, max_rel=5e-3)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_graph_replay_matches_eager(kernel):
+    """A decode call captured in a HIP graph gives the eager call's bytes on every replay
+    (three replays, with eager work on the output between them)."""
+    cfg, x = _workload(1)
+    ops, agents = pool_ops(cfg)
+    b = DeviceBatch(workload_geom(cfg), x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    eager = b.decode(cfg.lora_scale, sm, cfg.rope_theta).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.decode(cfg.lora_scale, sm, cfg.rope_theta)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        b.out.fill_(float(rep + 1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(b.out.view(torch.int16), eager.view(torch.int16))
+        print(f"[parity] graph replay {rep} kernel={kernel}: bitwise equal={same}", flush=True)
+        assert same
 
 
 def test_empty_agent_and_errors():
