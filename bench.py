@@ -141,6 +141,155 @@ def bench_prefill(steps, warmup):
             "mfma_frac": tflops / MFMA_PEAK_BF16_TFLOPS, "peak_tflops": MFMA_PEAK_BF16_TFLOPS}
 
 
+def bench_decode(idx, steps, warmup, kernel, pages_per_item, copies_arg):
+    """Decode step time (graph replay), split/combine launch times (events) on workload idx."""
+    import numpy as np
+    import torch
+
+    from lora_shared_prefix_amd import forkkv as fk
+    from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
+    from workloads import CONFIGS, draw_inputs, pool_ops
+
+    cfg = CONFIGS[idx]
+    assert cfg.kind == "decode"
+    log(f"drawing inputs of {cfg.name}")
+    x = draw_inputs(cfg)
+    ops, agents = pool_ops(cfg)
+    geom = workload_geom(cfg)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    unique = cfg.sessions * cfg.prefix_len + cfg.n_agents * cfg.suffix_len
+    split_bytes, step_bytes = algorithmic_bytes(cfg, unique)
+    ws_mb = step_bytes / 1e6
+    copies = copies_arg or max(1, int(np.ceil(3 * 256e6 / (split_bytes))))
+    log(f"uploading {copies} input copies (working set {ws_mb:.1f} MB each)")
+    first = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel,
+                        pages_per_item=pages_per_item)
+    batches = [first]
+    for _ in range(copies - 1):
+        b = DeviceBatch.__new__(DeviceBatch)
+        b.__dict__.update(first.__dict__)
+        b.bcache = first.bcache.clone()
+        b.rcache = first.rcache.clone()
+        b.q, b.Bk, b.Bv = first.q.clone(), first.Bk.clone(), first.Bv.clone()
+        b.out = torch.empty_like(first.out)
+        b.pool = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim,
+                         cfg.rank, cfg.dtype, x["perm_b"], x["perm_r"], b.bcache, b.rcache)
+        b.pool.replay(ops)
+        batches.append(b)
+    plan = first.plan
+    kname = "mfma" if plan.info["kernel"] == fk.KERNEL_MFMA else "generic"
+    log(f"plan: kernel={kname} items={plan.info['n_items']} slots={plan.info['n_slots']} "
+        f"workspace={plan.info['workspace_bytes'] / 1e6:.1f} MB")
+
+    def step(i):
+        b = batches[i % copies]
+        fk.residual_attn_decode(b.pool, plan, b.q, b.Bk, b.Bv, first.btab, first.rtab, b.out,
+                                first.workspace, cfg.lora_scale, sm, cfg.rope_theta)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # eager calls, for context: each call also pays the host-side (Python) launch cost
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    eager_ms_step = t0.elapsed_time(t1) / steps
+    # 1) the timed region: the K steps captured once as a HIP graph (K decode calls, the
+    #    input copies in rotation), replayed once untimed, then once timed, bracketed by
+    #    events on the replay stream; no per-call events or host launches inside
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / steps
+    # 2) the same K steps again with HIP events recorded by the library around each kernel
+    #    launch (on the launch stream): average launch duration of the split and combine
+    plan.timing()  # drop anything recorded so far
+    plan.set_timing(True)
+    split_ms = comb_ms = 0.0
+    launches = 0
+    split_samples = []
+    for i in range(steps):
+        step(i)
+        if (i + 1) % copies == 0 or i + 1 == steps:  # read the events of this rotation
+            torch.cuda.synchronize()
+            sm_, cm_, n_ = plan.timing()
+            split_ms, comb_ms, launches = split_ms + sm_, comb_ms + cm_, launches + n_
+            split_samples.append(sm_ / max(n_, 1))
+    plan.set_timing(False)
+    split_avg = split_ms / max(launches, 1)
+    comb_avg = comb_ms / max(launches, 1)
+    log(f"step {ms_step * 1e3:.1f} us (eager {eager_ms_step * 1e3:.1f} us); split "
+        f"{split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us")
+
+    # warm (cache-resident) figure for context: the same copy every step
+    plan.set_timing(True)
+    for _ in range(steps):
+        fk.residual_attn_decode(first.pool, plan, first.q, first.Bk, first.Bv, first.btab,
+                                first.rtab, first.out, first.workspace, cfg.lora_scale, sm,
+                                cfg.rope_theta)
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    wsplit, _, wl = plan.timing()
+
+    achieved = split_bytes / (split_avg * 1e-3) / 1e9
+    traffic = load_traffic(kname) if idx == 2 else None
+    pct = np.percentile(np.array(split_samples) * 1e3, [10, 50, 90]).tolist()
+    return {
+        "_cfg": cfg, "_x": x, "_ops": ops, "_agents": agents,
+        "agent_tokens_per_s": cfg.n_agents / (ms_step * 1e-3),
+        "ms_per_step": ms_step,
+        "config": {"workload": cfg.name, "agents": cfg.n_agents, "sessions": cfg.sessions,
+                   "shared_prefix": cfg.prefix_len, "private_suffix": cfg.suffix_len,
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "rank": cfg.rank, "page_size": 16, "kernel": kname,
+                   "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": f"residual_attn_{kname} (split-K decode)",
+                     "algorithmic_bytes_per_launch": split_bytes,
+                     "avg_launch_us": split_avg * 1e3},
+        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "split_us_p10_p50_p90": pct,
+        "combine_avg_us": comb_avg * 1e3,
+        "eager_ms_per_step": eager_ms_step,
+        "warm_split_avg_us": wsplit / max(wl, 1) * 1e3,
+    }
+
+
+def copy_bandwidth_gbs():
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy (practical ceiling)."""
+    import torch
+    n = 2 ** 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 10
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +300,8 @@ def main():
     ap.add_argument("--pages-per-item", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--cpu-sample", type=int, default=2, help="agents timed on the oracle (0 = skip)")
+    ap.add_argument("--no-more-workloads", action="store_true",
+                    help="skip the extra decode figures of workloads 1 and 3")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing chunked prefill on the Qwen3-8B 131072-prefix workload")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -180,127 +331,51 @@ def main():
         log(f"copy calibration: {n * 4} bytes read and written per copy, 3 copies")
         return
 
-    cfg = CONFIGS[args.workload]
-    assert cfg.kind == "decode"
     kernel = {"auto": fk.KERNEL_AUTO, "generic": fk.KERNEL_GENERIC, "mfma": fk.KERNEL_MFMA}[args.kernel]
-    log(f"drawing inputs of {cfg.name}")
-    x = draw_inputs(cfg)
-    ops, agents = pool_ops(cfg)
-    geom = workload_geom(cfg)
-    sm = 1.0 / np.sqrt(cfg.head_dim)
-    unique = cfg.sessions * cfg.prefix_len + cfg.n_agents * cfg.suffix_len
-    split_bytes, step_bytes = algorithmic_bytes(cfg, unique)
-    ws_mb = step_bytes / 1e6
-    copies = args.copies or max(1, int(np.ceil(3 * 256e6 / (split_bytes))))
-    log(f"uploading {copies} input copies (working set {ws_mb:.1f} MB each)")
-    first = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel,
-                        pages_per_item=args.pages_per_item)
-    batches = [first]
-    for _ in range(copies - 1):
-        arrays = {}
-        b = DeviceBatch.__new__(DeviceBatch)
-        b.__dict__.update(first.__dict__)
-        b.bcache = first.bcache.clone()
-        b.rcache = first.rcache.clone()
-        b.q, b.Bk, b.Bv = first.q.clone(), first.Bk.clone(), first.Bv.clone()
-        b.out = torch.empty_like(first.out)
-        b.pool = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim,
-                         cfg.rank, cfg.dtype, x["perm_b"], x["perm_r"], b.bcache, b.rcache)
-        b.pool.replay(ops)
-        batches.append(b)
-    plan = first.plan
-    kname = "mfma" if plan.info["kernel"] == fk.KERNEL_MFMA else "generic"
-    log(f"plan: kernel={kname} items={plan.info['n_items']} slots={plan.info['n_slots']} "
-        f"workspace={plan.info['workspace_bytes'] / 1e6:.1f} MB")
-
-    def step(i):
-        b = batches[i % copies]
-        fk.residual_attn_decode(b.pool, plan, b.q, b.Bk, b.Bv, first.btab, first.rtab, b.out,
-                                first.workspace, cfg.lora_scale, sm, cfg.rope_theta)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # eager calls, for context: each call also pays the host-side (Python) launch cost
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    eager_ms_step = t0.elapsed_time(t1) / args.steps
-    # 1) the timed region: the K steps captured once as a HIP graph (K decode calls, the
-    #    input copies in rotation), replayed once untimed, then once timed, bracketed by
-    #    events on the replay stream; no per-call events or host launches inside
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    t0.record()
-    graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
-    # 2) the same K steps again with HIP events recorded by the library around each kernel
-    #    launch (on the launch stream): average launch duration of the split and combine
-    plan.timing()  # drop anything recorded so far
-    plan.set_timing(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    plan.set_timing(False)
-    split_ms, comb_ms, launches = plan.timing()
-    split_avg = split_ms / max(launches, 1)
-    comb_avg = comb_ms / max(launches, 1)
-    log(f"step {ms_step * 1e3:.1f} us (eager {eager_ms_step * 1e3:.1f} us); split "
-        f"{split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us")
-
-    # warm (cache-resident) figure for context: the same copy every step
-    plan.set_timing(True)
-    for _ in range(args.steps):
-        fk.residual_attn_decode(first.pool, plan, first.q, first.Bk, first.Bv, first.btab,
-                                first.rtab, first.out, first.workspace, cfg.lora_scale, sm,
-                                cfg.rope_theta)
-    torch.cuda.synchronize()
-    plan.set_timing(False)
-    wsplit, _, wl = plan.timing()
-
-    achieved = split_bytes / (split_avg * 1e-3) / 1e9
-    traffic = load_traffic(kname)
+    d = bench_decode(args.workload, args.steps, args.warmup, kernel, args.pages_per_item,
+                     args.copies)
+    cfg, x, ops, agents = d.pop("_cfg"), d.pop("_x"), d.pop("_ops"), d.pop("_agents")
+    ceiling = copy_bandwidth_gbs()
+    log(f"device copy bandwidth {ceiling:.0f} GB/s (read + write bytes / time, 1 GiB copy)")
     result = {
         "metric": "ResidualAttention decode agent-tokens/s + achieved HBM GB/s (% roofline), 1 GPU",
-        "value": cfg.n_agents / (ms_step * 1e-3),
+        "value": d["agent_tokens_per_s"],
         "unit": "agent-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": d["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) caches and queries, B ~ N(0, 0.02^2))",
-        "config": {"workload": cfg.name, "agents": cfg.n_agents, "shared_prefix": cfg.prefix_len,
-                   "private_suffix": cfg.suffix_len, "q_heads": cfg.num_q_heads,
-                   "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "rank": cfg.rank,
-                   "page_size": 16, "kernel": kname, "input_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"residual_attn_{kname} (split-K decode)",
-                     "algorithmic_bytes_per_launch": split_bytes,
-                     "avg_launch_us": split_avg * 1e3},
-        "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
-        "combine_avg_us": comb_avg * 1e3,
-        "eager_ms_per_step": eager_ms_step,
-        "warm_split_avg_us": wsplit / max(wl, 1) * 1e3,
+        "config": d["config"],
+        "roofline": d["roofline"],
+        "step_hbm_gbs": d["step_hbm_gbs"],
+        "split_us_p10_p50_p90": d["split_us_p10_p50_p90"],
+        "combine_avg_us": d["combine_avg_us"],
+        "eager_ms_per_step": d["eager_ms_per_step"],
+        "warm_split_avg_us": d["warm_split_avg_us"],
+        "copy_bandwidth_gbs": ceiling,
+        "split_frac_of_copy_bandwidth": d["roofline"]["achieved"] / ceiling,
     }
+    if not args.no_more_workloads and args.workload == 2:
+        others = {}
+        for idx in (1, 3):
+            torch.cuda.empty_cache()
+            o = bench_decode(idx, max(10, args.steps // 2), max(2, args.warmup // 2), kernel, 0, 0)
+            for k in ("_cfg", "_x", "_ops", "_agents"):
+                o.pop(k)
+            others[o["config"]["workload"]] = {
+                "agent_tokens_per_s": o["agent_tokens_per_s"], "ms_per_step": o["ms_per_step"],
+                "split_avg_us": o["roofline"]["avg_launch_us"],
+                "split_hbm_gbs": o["roofline"]["achieved"], "split_frac": o["roofline"]["frac"],
+                "algorithmic_bytes_per_launch": o["roofline"]["algorithmic_bytes_per_launch"],
+                "combine_avg_us": o["combine_avg_us"], "config": o["config"]}
+        result["other_decode_workloads"] = others
     if not args.no_prefill:
-        del batches, first  # free the decode inputs before the 1.2 GB prefill workload
-        torch.cuda.empty_cache()
+        torch.cuda.empty_cache()  # the decode inputs are freed by now
         result["prefill"] = bench_prefill(args.steps, args.warmup)
     if args.cpu_sample > 0:
         log("timing the fp64 oracle on the host")

@@ -93,29 +93,49 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   //
   // The MFMA kernel runs four waves per item: the chunk's agents form n_groups groups of
   // up to A agents and the item's pages are split into 4 / n_groups sub-ranges, one per
-  // wave.  Its items are sized by pages per wave (at most 64: a wave keeps its page ids in
-  // one register) so that the whole grid fits one round of resident waves when possible
-  // (256 compute units x 8 waves on MI355X) with every wave doing about the same work.
+  // wave.  Its items are sized so that the whole grid fits one round of resident waves when
+  // possible (256 compute units x 8 waves on MI355X) and every wave does about the same
+  // work: a page costs a wave about kPageShared + kPageAgent x (agents of its group) (the
+  // shared base score, softmax and value product, then the per-agent key rebuild, rotation
+  // and score), so waves of small groups take proportionally more pages.  At most 64 pages
+  // per wave: a wave keeps its page ids in one register.
+  constexpr int32_t kPageShared = 11, kPageAgent = 4;  // measured VALU-issue ratio
   const int A = kernel == FORKKV_KERNEL_MFMA ? forkkv::mfma_agents_per_wave(group_q) : 0;
   auto n_sub_of = [&](int32_t na) { return 4 / ((na + A - 1) / A); };
-  int32_t ppw = 0;  // MFMA: pages per wave
+  auto page_cost = [&](int32_t na) { return kPageShared + kPageAgent * std::min(na, A); };
+  int32_t target = 0;   // MFMA: cost budget per wave
+  int32_t fixed_pw = 0; // MFMA: explicit pages per wave (tuning)
+  auto pages_per_wave = [&](int32_t na) {
+    if (fixed_pw > 0) return fixed_pw;
+    return std::max<int32_t>(1, std::min<int32_t>(64, target / page_cost(na)));
+  };
   if (kernel == FORKKV_KERNEL_MFMA) {
     const int64_t slots = 2048;
-    auto waves_for = [&](int32_t pw) {
+    auto waves_now = [&]() {
       int64_t wv = 0;
       for (const Run& r : runs)
         for (size_t a0 = 0; a0 < r.agents.size(); a0 += cap) {
           const int32_t na = static_cast<int32_t>(std::min<size_t>(cap, r.agents.size() - a0));
-          const int32_t item_pages = pw * n_sub_of(na);
+          const int32_t item_pages = pages_per_wave(na) * n_sub_of(na);
           wv += 4 * int64_t((r.lp1 - r.lp0 + item_pages - 1) / item_pages);
         }
       return wv * g.num_kv_heads;
     };
     if (o.pages_per_item > 0) {
-      ppw = std::max(1, std::min(64, o.pages_per_item));  // fixed split (tuning)
+      fixed_pw = std::max(1, std::min(64, o.pages_per_item));
     } else {
-      ppw = 1;
-      while (ppw < 64 && waves_for(ppw) > slots) ++ppw;
+      // smallest per-wave budget whose grid fits one round (waves only fall as it grows)
+      const int32_t top = 64 * page_cost(A);
+      int32_t lo = page_cost(1), hi = top;
+      target = hi;
+      if (waves_now() <= slots) {
+        while (lo < hi) {
+          target = lo + (hi - lo) / 2;
+          if (waves_now() <= slots) hi = target;
+          else lo = target + 1;
+        }
+        target = lo;
+      }
     }
   }
   std::vector<int32_t> items;
@@ -124,7 +144,8 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   for (const Run& r : runs) {
     for (size_t a0 = 0; a0 < r.agents.size(); a0 += cap) {
       const int32_t na = static_cast<int32_t>(std::min<size_t>(cap, r.agents.size() - a0));
-      const int32_t item_pages = kernel == FORKKV_KERNEL_MFMA ? ppw * n_sub_of(na) : ppi;
+      const int32_t item_pages =
+          kernel == FORKKV_KERNEL_MFMA ? pages_per_wave(na) * n_sub_of(na) : ppi;
       for (int32_t lp = r.lp0; lp < r.lp1; lp += item_pages) {
         const int32_t np = std::min(item_pages, r.lp1 - lp);
         int32_t it[kItemInts];
