@@ -236,6 +236,31 @@ typedef struct {
 int forkkv_residual_attn_decode(const forkkv_decode_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
+ * Decode step with append: each agent's newest token is stored into the pools first, then
+ * the agent's query attends to its keys 0 .. len-1, the new token included.  The caller
+ * has reserved the token with forkkv_seq_append (running the copy-on-write row copy it
+ * reports with forkkv_cow_copy, so a tail page shared after a fork is first packed into a
+ * private page -- ForkServe README, "Design vs APC": pack plus an n_valid-row copy, not a
+ * whole page), re-exported the tables and built the plan over the new lengths.  Within one
+ * call the rows are written before any attention reads them (Penelope review, 部件二:
+ * each layer writes the batch's K/V, then attends).
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  forkkv_decode_args decode; /* as for decode; every plan length counts the new token (>= 1)
+                                and q is post-RoPE at position len - 1 */
+  const void* k_new;         /* device [N][Hkv][d], post-RoPE base key of the new token */
+  const void* v_new;         /* device [N][Hkv][d] */
+  const void* rk_new;        /* device [N][r], key residual of the new token (no RoPE) */
+  const void* rv_new;        /* device [N][r] */
+} forkkv_decode_append_args;
+
+/* Same errors as forkkv_residual_attn_decode; FORKKV_EINVAL also for a null row pointer or
+ * a plan length below 1.  The new rows land at position len - 1 of each agent, in the
+ * pages the tables name for it. */
+int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* args,
+                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
  * Chunked prefill: agent a appends C rows at positions start_pos[a] .. start_pos[a]+C-1
  * (the caller has already reserved them with forkkv_seq_append and uploaded the tables).
  * The kernel first stores the chunk rows into the pools, then every chunk query

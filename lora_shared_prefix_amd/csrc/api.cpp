@@ -63,10 +63,15 @@ int forkkv_plan_timing(forkkv_plan* pl, double* split_ms, double* combine_ms, in
   return rc;
 }
 
-int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate decode arguments and fill the kernel parameters (no launch).
+int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   if (!a || !a->pool || !a->plan) return FORKKV_EINVAL;
   const forkkv_pool* pool = a->pool;
-  forkkv_plan* pl = const_cast<forkkv_plan*>(a->plan);
+  const forkkv_plan* pl = a->plan;
   if (!same_geometry(pool->desc, pl->geo)) return FORKKV_EINVAL;
   if (!pool->bcache) return FORKKV_ESTATE;
   if (pl->n_agents == 0) return FORKKV_OK;
@@ -80,7 +85,8 @@ int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream)
     return FORKKV_EINVAL;
 
   const forkkv_pool_desc& g = pool->desc;
-  forkkv::DecodeParams p{};
+  forkkv::DecodeParams& p = *out;
+  p = forkkv::DecodeParams{};
   p.q = a->q;
   p.Bk = a->Bk;
   p.Bv = a->Bv;
@@ -111,8 +117,11 @@ int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream)
   p.lora_scale = a->lora_scale;
   p.sm_scale_log2 = a->sm_scale * kLog2e;
   p.rope_theta = a->rope_theta;
+  return FORKKV_OK;
+}
 
-  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+// Split kernel + combine on the stream, with the plan's optional event timing.
+int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hipStream_t stream) {
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   if (pl->timing) {
     for (auto& e : ev) {
@@ -124,12 +133,12 @@ int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream)
     if (ev[0] && hipEventRecord(ev[0], stream) != hipSuccess) return FORKKV_EHIP;
     hipError_t err = pl->kernel == FORKKV_KERNEL_MFMA
                          ? forkkv::launch_decode_mfma(p, stream)
-                         : forkkv::launch_decode_generic(p, g.dtype, pl->group, stream);
+                         : forkkv::launch_decode_generic(p, dtype, pl->group, stream);
     if (err != hipSuccess) return FORKKV_EHIP;
     if (ev[1] && hipEventRecord(ev[1], stream) != hipSuccess) return FORKKV_EHIP;
   }
   if (ev[2] && hipEventRecord(ev[2], stream) != hipSuccess) return FORKKV_EHIP;
-  if (forkkv::launch_combine(p, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  if (forkkv::launch_combine(p, dtype, stream) != hipSuccess) return FORKKV_EHIP;
   if (ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return FORKKV_EHIP;
   if (pl->timing) {
     if (pl->n_items > 0) {
@@ -142,6 +151,56 @@ int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream)
   }
   if (hipGetLastError() != hipSuccess) return FORKKV_EHIP;
   return FORKKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream) {
+  forkkv::DecodeParams p;
+  const int rc = prepare_decode(a, &p);
+  if (rc != FORKKV_OK || a->plan->n_agents == 0) return rc;
+  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+  return launch_decode(const_cast<forkkv_plan*>(a->plan), p, a->pool->desc.dtype, stream);
+}
+
+int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipStream_t stream) {
+  if (!a) return FORKKV_EINVAL;
+  forkkv::DecodeParams p;
+  const int rc = prepare_decode(&a->decode, &p);
+  const forkkv_plan* pl = a->decode.plan;
+  if (rc != FORKKV_OK || pl->n_agents == 0) return rc;
+  if (!a->k_new || !a->v_new || !a->rk_new || !a->rv_new) return FORKKV_EINVAL;
+  // every agent's captured length counts its new token
+  const int32_t off_lens = pl->blob[forkkv::kHdrOffLens];
+  for (int32_t i = 0; i < pl->n_agents; ++i)
+    if (pl->blob[off_lens + i] < 1) return FORKKV_EINVAL;
+  const forkkv_pool_desc& g = a->decode.pool->desc;
+  forkkv::PrefillParams w{};
+  w.k_new = a->k_new;
+  w.v_new = a->v_new;
+  w.rk_new = a->rk_new;
+  w.rv_new = a->rv_new;
+  w.bcache = a->decode.pool->bcache;
+  w.rcache = a->decode.pool->rcache;
+  w.btab = a->decode.btab;
+  w.rtab = a->decode.rtab;
+  w.start_pos = p.plan + off_lens;  // the plan's lengths, on the device
+  w.pos_bias = -1;                  // the new token sits at position length - 1
+  w.n_agents = pl->n_agents;
+  w.chunk_len = 1;
+  w.num_q_heads = pl->num_q_heads;
+  w.num_kv_heads = g.num_kv_heads;
+  w.head_dim = g.head_dim;
+  w.rank = g.rank;
+  w.group = p.group;
+  w.max_pages = a->decode.max_pages;
+  w.num_bpages = g.num_bpages;
+  w.num_rpages = g.num_rpages;
+  (void)hipGetLastError();
+  if (forkkv::launch_prefill_write(w, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  return launch_decode(const_cast<forkkv_plan*>(pl), p, g.dtype, stream);
 }
 
 int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t stream) {

@@ -119,6 +119,7 @@ struct PrefillParams {
   void* out;
   int32_t n_agents, chunk_len, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
+  int32_t pos_bias;         // row i of agent a is stored at position start_pos[a] + pos_bias + i
   float lora_scale, sm_scale_log2, rope_theta;
 };
 

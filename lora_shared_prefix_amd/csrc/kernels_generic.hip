@@ -476,7 +476,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) prefill_write_kernel(PrefillParams p) {
   const int i = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
   const int d = p.head_dim, r = p.rank, Hkv = p.num_kv_heads, C = p.chunk_len;
-  const int t = p.start_pos[a] + i;
+  const int t = p.start_pos[a] + p.pos_bias + i;
   const int lp = t / kPage, row = t % kPage;
   const int bpg = p.btab[size_t(a) * p.max_pages + lp];
   const int rpg = p.rtab[size_t(a) * p.max_pages + lp];

@@ -58,6 +58,11 @@ class DecodeArgs(C.Structure):
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
+class DecodeAppendArgs(C.Structure):
+    _fields_ = [("decode", DecodeArgs), ("k_new", C.c_void_p), ("v_new", C.c_void_p),
+                ("rk_new", C.c_void_p), ("rv_new", C.c_void_p)]
+
+
 class PrefillArgs(C.Structure):
     _fields_ = [("pool", C.c_void_p), ("n_agents", C.c_int32), ("chunk_len", C.c_int32),
                 ("num_q_heads", C.c_int32), ("q", C.c_void_p), ("k_new", C.c_void_p),
@@ -91,6 +96,7 @@ _SIGS = {
     "forkkv_plan_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
     "forkkv_plan_timing": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_double), _i32p]),
     "forkkv_residual_attn_decode": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
+    "forkkv_residual_attn_decode_append": (C.c_int, [C.POINTER(DecodeAppendArgs), C.c_void_p]),
     "forkkv_residual_attn_prefill": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
 }
 
@@ -324,6 +330,22 @@ def residual_attn_decode(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, wor
                       workspace.numel() * workspace.element_size() if workspace is not None else 0)
     _check(lib().forkkv_residual_attn_decode(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_decode")
+
+
+def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, workspace,
+                                lora_scale, sm_scale, rope_theta, k_new, v_new, rk_new, rv_new,
+                                stream=None):
+    """Store each agent's new token (k_new/v_new [N][Hkv][d], rk_new/rv_new [N][r]) at
+    position len - 1, then decode over keys 0 .. len - 1 (async)."""
+    d = DecodeArgs(pool.handle, plan.handle, q.data_ptr(), Bk.data_ptr(), Bv.data_ptr(),
+                   btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]), float(lora_scale),
+                   float(sm_scale), float(rope_theta), out.data_ptr(),
+                   workspace.data_ptr() if workspace is not None else None,
+                   workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    args = DecodeAppendArgs(d, k_new.data_ptr(), v_new.data_ptr(), rk_new.data_ptr(),
+                            rv_new.data_ptr())
+    _check(lib().forkkv_residual_attn_decode_append(C.byref(args), _stream(stream)),
+           "forkkv_residual_attn_decode_append")
 
 
 def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, btab, rtab,

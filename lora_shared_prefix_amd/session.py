@@ -80,6 +80,16 @@ class DeviceBatch:
                                 self.workspace, lora_scale, sm_scale, rope_theta, stream)
         return self.out if out is None else out
 
+    def decode_append(self, rows, lora_scale, sm_scale, rope_theta, stream=None, out=None):
+        """After reserve_chunk(1) and make_plan(): store every agent's new token (rows: dict
+        of device tensors k_new [N][Hkv][d], v_new, rk_new [N][r], rv_new), then decode."""
+        out = self.out if out is None else out
+        fk.residual_attn_decode_append(self.pool, self.plan, self.q, self.Bk, self.Bv, self.btab,
+                                       self.rtab, out, self.workspace, lora_scale, sm_scale,
+                                       rope_theta, rows["k_new"], rows["v_new"], rows["rk_new"],
+                                       rows["rv_new"], stream)
+        return out
+
     # ---- chunked prefill ---------------------------------------------------------------
     def reserve_chunk(self, chunk_len):
         """Append chunk_len rows to every agent (host bookkeeping) and re-upload the tables."""
