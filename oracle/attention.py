@@ -93,11 +93,11 @@ def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_sc
     return out
 
 
-def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk_new, rv_new):
-    """Pool contents after the prefill chunk rows are stored (copies; inputs untouched).
+def apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new, rv_new):
+    """Pool contents after rows are stored (copies; inputs untouched).
 
-    Row i of agent a goes to position ``start_pos[a] + i``: page
-    ``table[a][pos // P]``, row ``pos % P``, laid out as the pool layout says.
+    Row i of agent a goes to position ``positions[a][i]``: page ``table[a][pos // P]``,
+    row ``pos % P``, laid out as the pool layout says.
     """
     bp, rp = bpool.copy(), rpool.copy()
     N, C = k_new.shape[0], k_new.shape[1]
@@ -105,7 +105,7 @@ def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk
     dims, ranks = np.arange(d), np.arange(r)
     for a in range(N):
         for i in range(C):
-            t = int(start_pos[a]) + i
+            t = int(positions[a][i])
             page, row = int(btab[a][t // P]), t % P
             for h in range(geo.Hkv):
                 bp[page, 0, h, key_offset(row, dims)] = k_new[a, i, h]
@@ -114,6 +114,15 @@ def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk
             rp[page, 0, res_key_offset(row, ranks)] = rk_new[a, i]
             rp[page, 1, res_value_offset(row, ranks, r)] = rv_new[a, i]
     return bp, rp
+
+
+def apply_chunk_write(geo, bpool, rpool, btab, rtab, start_pos, k_new, v_new, rk_new, rv_new):
+    """Pool contents after the prefill chunk rows are stored: row i of agent a at position
+    ``start_pos[a] + i`` (copies; inputs untouched)."""
+    C = k_new.shape[1]
+    positions = [[int(start_pos[a]) + i for i in range(C)] for a in range(k_new.shape[0])]
+    return apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new,
+                            rv_new)
 
 
 def prefill_attention(geo, bpool, rpool, btab, rtab, start_pos, q, k_new, v_new, rk_new,
@@ -156,6 +165,43 @@ def prefill_attention(geo, bpool, rpool, btab, rtab, start_pos, q, k_new, v_new,
         k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
         for i, g in rows:
             n_keys = start + i + 1
+            p = _softmax_rows(sm_scale * (k[:n_keys] @ qv[a, i, g]))
+            out[a, i, g] = p @ v[:n_keys]
+    return out
+
+
+def prefill_attention_at(geo, bpool, rpool, btab, rtab, positions, q, k_new, v_new, rk_new,
+                         rv_new, Bk, Bv, lora_scale, sm_scale, theta, samples=None):
+    """Prefill over an arbitrary list of positions: row i of agent a sits at position
+    ``positions[a][i]`` (e.g. a hole in the middle of the history followed by the real
+    request's tail -- Penelope review, 部件二: the phantom request and the real request keep
+    their original positions and run in one batch).  All rows are written first; then query
+    i attends to keys ``0 .. positions[a][i]`` of the written pools (self included).
+
+    Returns fp64 [N, C, Hq, d]; with ``samples`` (a list of (a, i, g)) only those rows are
+    computed and the rest are NaN.
+    """
+    N, C = q.shape[0], q.shape[1]
+    bp, rp = apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new,
+                              rv_new)
+    qv = decode_values(q, geo.dtype)
+    Bkv, Bvv = decode_values(Bk, geo.dtype), decode_values(Bv, geo.dtype)
+    out = np.full((N, C, geo.Hq, geo.d), np.nan)
+    want = {}
+    if samples is None:
+        for a in range(N):
+            for g in range(geo.Hq):
+                want.setdefault((a, g // geo.G), []).extend((i, g) for i in range(C))
+    else:
+        for a, i, g in samples:
+            want.setdefault((int(a), int(g) // geo.G), []).append((int(i), int(g)))
+    for (a, h), rows in sorted(want.items()):
+        last = max(int(positions[a][i]) for i, _ in rows)
+        pos = np.arange(last + 1, dtype=np.int64)
+        bk, bv, rk, rv = _cached_rows(geo, bp, rp, btab, rtab, a, h, pos)
+        k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
+        for i, g in rows:
+            n_keys = int(positions[a][i]) + 1
             p = _softmax_rows(sm_scale * (k[:n_keys] @ qv[a, i, g]))
             out[a, i, g] = p @ v[:n_keys]
     return out

@@ -114,3 +114,36 @@ def brute_prefill(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, start_pos, 
             per_q.append(rows)
         out.append(per_q)
     return out
+
+
+def brute_prefill_at(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, positions, q, k_new,
+                     v_new, rk_new, rv_new, Bk, Bv, s, sm_scale, theta):
+    """Rows are written at positions[a][i] (all of them first), then query i attends to keys
+    0 .. positions[a][i]; positions strictly increase per agent."""
+    bpool, rpool, btab, rtab = map(_lists, (bpool, rpool, btab, rtab))
+    q, k_new, v_new, rk_new, rv_new, Bk, Bv = map(_lists, (q, k_new, v_new, rk_new, rv_new, Bk, Bv))
+    G = Hq // Hkv
+    out = []
+    for a in range(len(q)):
+        written = {int(t): j for j, t in enumerate(positions[a])}
+        per_q = []
+        for i in range(len(q[a])):
+            rows = []
+            for g in range(Hq):
+                h = g // G
+                kv = []
+                for t in range(int(positions[a][i]) + 1):
+                    ov = None
+                    if t in written:
+                        j = written[t]
+                        ov = ([_val(x, dtype) for x in k_new[a][j][h]],
+                              [_val(x, dtype) for x in v_new[a][j][h]],
+                              [_val(x, dtype) for x in rk_new[a][j]],
+                              [_val(x, dtype) for x in rv_new[a][j]])
+                    kv.append(_key_value(P, d, r, dtype, bpool, rpool, btab[a], rtab[a], Bk[a],
+                                         Bv[a], h, t, s, theta, row_override=ov))
+                qrow = [_val(x, dtype) for x in q[a][i][g]]
+                rows.append(_attend(qrow, kv, sm_scale, d))
+            per_q.append(rows)
+        out.append(per_q)
+    return out

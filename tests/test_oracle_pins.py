@@ -15,10 +15,11 @@ import torch
 import oracle
 import oracle.attention as oatt
 from oracle import PoolModel
-from oracle.attention import Geometry, decode_attention, merged_kv, prefill_attention
+from oracle.attention import (Geometry, apply_rows_write, decode_attention, merged_kv,
+                              prefill_attention, prefill_attention_at)
 from oracle.rope import inv_freq, rope_rotate, rope_unrotate
 from oracle.storage import base_key_rows, base_value_rows, decode_values
-from tests.bruteforce import brute_decode, brute_prefill
+from tests.bruteforce import brute_decode, brute_prefill, brute_prefill_at
 from tests.cases import tiny_case
 from tests.fused_model import fused_decode
 from workloads import CONFIGS, draw_inputs, pool_ops
@@ -115,6 +116,95 @@ def test_random_tiny_prefill_matches_brute_force(seed):
     os_ = prefill_attention(geo, *args, samples=samples)
     for a, i, g in samples:
         assert np.array_equal(os_[a, i, g], o[a, i, g])
+
+
+def _hole_case(seed, dtype="f32", Hq=2, Hkv=1, d=16, r=4):
+    """Agents with a history; a hole inside it is refilled and a tail is appended: rows at
+    strictly increasing positions [hole ..., tail ...] (Penelope review, 部件二)."""
+    rng = np.random.default_rng(seed)
+    case = tiny_case(seed, dtype, Hq=Hq, Hkv=Hkv, d=d, r=r, n_agents=2, max_prefix=60,
+                     max_suffix=30)
+    pm = PoolModel(64, 64, 16, case["perm_b"], case["perm_r"])
+    names = pm.replay(case["ops"])
+    hs = [names[a] for a in case["agents"]]
+    lens = [pm.length(h) for h in hs]
+    tail = 3
+    hole = 2 if min(lens) >= 2 else 1
+    positions = []
+    for h, L in zip(hs, lens):
+        h0 = int(rng.integers(0, L - hole + 1))
+        positions.append(list(range(h0, h0 + hole)) + list(range(L, L + tail)))
+        pm.append(h, tail)
+    C = hole + tail
+    bt, rt, _ = pm.tables(hs, 64)
+    from tests.cases import encode
+    n = len(hs)
+    rows = dict(q=encode(rng.standard_normal((n, C, Hq, d)), dtype),
+                k_new=encode(rng.standard_normal((n, C, Hkv, d)), dtype),
+                v_new=encode(rng.standard_normal((n, C, Hkv, d)), dtype),
+                rk_new=encode(rng.standard_normal((n, C, r)), dtype),
+                rv_new=encode(rng.standard_normal((n, C, r)), dtype))
+    return case, np.array(bt), np.array(rt), np.array(positions), rows
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_positions_prefill_matches_brute_force(seed):
+    """Rows at arbitrary increasing positions (a refilled hole + an appended tail): all rows
+    written first, each query attends to keys 0 .. its position."""
+    case, bt, rt, positions, rows = _hole_case(300 + seed)
+    assert all(p_[0] >= 0 for p_ in positions)
+    geo = _geo(case)
+    args = (case["bpool"], case["rpool"], bt, rt, positions, rows["q"], rows["k_new"],
+            rows["v_new"], rows["rk_new"], rows["rv_new"], case["Bk"], case["Bv"],
+            case["lora_scale"], case["sm_scale"], case["theta"])
+    o = prefill_attention_at(geo, *args)
+    b = np.array(brute_prefill_at(16, 2, 1, 16, 4, "f32", *args))
+    assert _nrel(o, b) < 1e-12
+
+
+def test_positions_prefill_is_decode_over_written_pools():
+    """Each query equals one decode query over the pools after the write, with its own
+    position + 1 keys (the plain definition, through the decode path of the oracle)."""
+    case, bt, rt, positions, rows = _hole_case(311, Hq=4, Hkv=2)
+    geo = _geo(case)
+    o = prefill_attention_at(geo, case["bpool"], case["rpool"], bt, rt, positions, rows["q"],
+                             rows["k_new"], rows["v_new"], rows["rk_new"], rows["rv_new"],
+                             case["Bk"], case["Bv"], case["lora_scale"], case["sm_scale"],
+                             case["theta"])
+    bp, rp = apply_rows_write(geo, case["bpool"], case["rpool"], bt, rt, positions,
+                              rows["k_new"], rows["v_new"], rows["rk_new"], rows["rv_new"])
+    for a in range(positions.shape[0]):
+        for i in range(positions.shape[1]):
+            lens = np.zeros(positions.shape[0], dtype=np.int64)
+            lens[a] = positions[a, i] + 1
+            qa = np.zeros_like(rows["q"][:, 0])
+            qa[a] = rows["q"][a, i]
+            d_ = decode_attention(geo, bp, rp, bt, rt, lens, qa, case["Bk"], case["Bv"],
+                                  case["lora_scale"], case["sm_scale"], case["theta"],
+                                  agents=[a])
+            assert _nrel(o[a, i], d_[a]) < 1e-12
+
+
+def test_positions_prefill_contiguous_equals_chunked_prefill():
+    """Contiguous positions start .. start + C - 1 reproduce the chunked prefill, which
+    concatenates the chunk rows instead of reading the written pools."""
+    C = 4
+    case = tiny_case(321, "f32", Hq=2, Hkv=1, d=16, r=4, n_agents=2, chunk=C)
+    pm = PoolModel(64, 64, 16, case["perm_b"], case["perm_r"])
+    names = pm.replay(case["ops"])
+    hs = [names[a] for a in case["agents"]]
+    start = np.array([pm.length(h) for h in hs])
+    for h in hs:
+        pm.append(h, C)
+    bt, rt, _ = pm.tables(hs, 64)
+    bt, rt = np.array(bt), np.array(rt)
+    geo = _geo(case)
+    tail = (case["q"], case["k_new"], case["v_new"], case["rk_new"], case["rv_new"], case["Bk"],
+            case["Bv"], case["lora_scale"], case["sm_scale"], case["theta"])
+    o1 = prefill_attention(geo, case["bpool"], case["rpool"], bt, rt, start, *tail)
+    positions = np.array([[int(s0) + i for i in range(C)] for s0 in start])
+    o2 = prefill_attention_at(geo, case["bpool"], case["rpool"], bt, rt, positions, *tail)
+    assert _nrel(o1, o2) < 1e-12
 
 
 # ---- C1: zero adapter reduces to plain attention (library routine) --------------------------
