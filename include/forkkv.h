@@ -266,6 +266,15 @@ int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* args,
  * The kernel first stores the chunk rows into the pools, then every chunk query
  * attends causally to keys 0 .. its own position (Penelope review, 部件二: each layer
  * writes the batch's K/V first, then attends).
+ *
+ * With a position list (positions != NULL) row i of agent a sits at positions[a][i]
+ * instead: e.g. the rows of a hole inside the history, recomputed by a prefill-only
+ * request, followed by the real request's new tail -- both keep their original positions
+ * and run in one launch (Penelope review, 部件二, the phantom request).  All rows are
+ * stored first; query i then attends to keys 0 .. positions[a][i], reading the rows just
+ * stored.  Positions must strictly increase per agent and lie inside the tables; every
+ * position must have been reserved (history rows of the hole, appended rows of the tail).
+ * start_pos / start_pos_host are then ignored and may be NULL.
  * --------------------------------------------------------------------------------- */
 typedef struct {
   const forkkv_pool* pool;
@@ -286,7 +295,14 @@ typedef struct {
   const int32_t* start_pos_host; /* host [N], same values (validation and launch shape) */
   float lora_scale, sm_scale, rope_theta;
   void* out;                /* device [N][C][Hq][d] */
+  const int32_t* positions;      /* nullable: device [N][C], row positions (see above) */
+  const int32_t* positions_host; /* host [N][C], same values; required with positions */
 } forkkv_prefill_args;
+
+/* Errors: FORKKV_EINVAL for null pointers, C < 1, a head count that is not a multiple of
+ * Hkv, rows outside the tables or positions that do not strictly increase;
+ * FORKKV_EUNSUPPORTED for a shape no kernel covers; FORKKV_ESTATE when the pool has no
+ * device storage; FORKKV_EHIP when a launch fails. */
 
 int forkkv_residual_attn_prefill(const forkkv_prefill_args* args, hipStream_t stream);
 

@@ -211,16 +211,27 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   if (a->n_agents < 0 || a->chunk_len < 1) return FORKKV_EINVAL;
   if (a->num_q_heads < g.num_kv_heads || a->num_q_heads % g.num_kv_heads) return FORKKV_EINVAL;
   if (a->n_agents == 0) return FORKKV_OK;
+  const bool listed = a->positions != nullptr;
   if (!a->q || !a->k_new || !a->v_new || !a->rk_new || !a->rv_new || !a->Bk || !a->Bv ||
-      !a->btab || !a->rtab || !a->start_pos || !a->start_pos_host || !a->out)
+      !a->btab || !a->rtab || !a->out)
     return FORKKV_EINVAL;
+  if (listed ? !a->positions_host : (!a->start_pos || !a->start_pos_host)) return FORKKV_EINVAL;
   if (a->max_pages < 1) return FORKKV_EINVAL;
   if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->rope_theta > 0.f) ||
       !finite(a->rope_theta))
     return FORKKV_EINVAL;
+  const int64_t cap = int64_t(a->max_pages) * kPage;
   for (int32_t i = 0; i < a->n_agents; ++i) {
-    const int64_t s = a->start_pos_host[i];
-    if (s < 0 || s + a->chunk_len > int64_t(a->max_pages) * kPage) return FORKKV_EINVAL;
+    if (listed) {
+      const int32_t* pos = a->positions_host + size_t(i) * a->chunk_len;
+      if (pos[0] < 0) return FORKKV_EINVAL;
+      for (int32_t c = 1; c < a->chunk_len; ++c)
+        if (pos[c] <= pos[c - 1]) return FORKKV_EINVAL;
+      if (pos[a->chunk_len - 1] >= cap) return FORKKV_EINVAL;
+    } else {
+      const int64_t s = a->start_pos_host[i];
+      if (s < 0 || s + a->chunk_len > cap) return FORKKV_EINVAL;
+    }
   }
   forkkv::PrefillParams p{};
   p.q = a->q;
@@ -235,6 +246,7 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   p.btab = a->btab;
   p.rtab = a->rtab;
   p.start_pos = a->start_pos;
+  p.positions = a->positions;
   p.out = a->out;
   p.n_agents = a->n_agents;
   p.chunk_len = a->chunk_len;

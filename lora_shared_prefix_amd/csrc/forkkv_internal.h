@@ -116,12 +116,19 @@ struct PrefillParams {
   const int32_t* btab;
   const int32_t* rtab;
   const int32_t* start_pos;
+  const int32_t* positions;  // nullable: [N][C] position of every row (strictly increasing
+                             // per agent); null: row i of agent a at start_pos[a] + i
   void* out;
   int32_t n_agents, chunk_len, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
   int32_t pos_bias;         // row i of agent a is stored at position start_pos[a] + pos_bias + i
   float lora_scale, sm_scale_log2, rope_theta;
 };
+
+// Position of row i of agent a (both kernels and the row write agree on it).
+__host__ __device__ inline int row_position(const PrefillParams& p, int a, int i) {
+  return p.positions ? p.positions[size_t(a) * p.chunk_len + i] : p.start_pos[a] + p.pos_bias + i;
+}
 
 // Kernel launchers (defined in the .hip translation units).  They return hipError_t
 // from the launch.

@@ -102,7 +102,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
   int agents[kItemAgents];
   int slot_of[kItemAgents];
   int limit[kItemAgents];  // decode: keys t < limit[j]
-  int a_pf = 0, q0 = 0, start = 0, C = 0, QB = 0;
+  int a_pf = 0, q0 = 0, last_pos = 0, C = 0, QB = 0;
   if constexpr (kPrefill) {
     a_pf = blockIdx.z;
     C = pp.chunk_len;
@@ -110,13 +110,13 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     if (QB * G * d > kGenericThreads * kGenericAccPerThread) QB = kGenericThreads * kGenericAccPerThread / (G * d);
     if (QB * G * r > kGenericThreads * kGenericAccrPerThread) QB = kGenericThreads * kGenericAccrPerThread / (G * r);
     q0 = blockIdx.x * QB;
-    start = pp.start_pos[a_pf];
     const int nq = min(QB, C - q0);
+    last_pos = row_position(pp, a_pf, q0 + nq - 1);  // positions increase along the chunk
     rows = nq * G;
     na = 1;
     agents[0] = a_pf;
     lp_begin = 0;
-    lp_end = (start + q0 + nq - 1) / kPage + 1;
+    lp_end = last_pos / kPage + 1;
   } else {
     const int32_t* it = dp.plan + dp.off_items + blockIdx.x * kItemInts;
     lp_begin = it[0];
@@ -169,7 +169,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     // arbitrary (even NaN) and a zero probability times NaN would still be NaN.
     int vrows;
     if constexpr (kPrefill) {
-      vrows = min(kPage, max(0, start + q0 + rows / G - lp * kPage));
+      vrows = min(kPage, max(0, last_pos + 1 - lp * kPage));
     } else {
       vrows = 0;
       for (int j = 0; j < na; ++j) vrows = max(vrows, min(kPage, limit[j] - lp * kPage));
@@ -230,7 +230,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
         if constexpr (kPrefill) {
           const int qi = q0 + row / G, g = row % G;
           qoff = ((size_t(a_pf) * C + qi) * Hq + h * G + g) * d;
-          valid = pos <= start + qi;
+          valid = pos <= row_position(pp, a_pf, qi);
         } else {
           const int g = row % G;
           qoff = (size_t(agents[j]) * Hq + h * G + g) * d;
@@ -476,7 +476,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) prefill_write_kernel(PrefillParams p) {
   const int i = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
   const int d = p.head_dim, r = p.rank, Hkv = p.num_kv_heads, C = p.chunk_len;
-  const int t = p.start_pos[a] + p.pos_bias + i;
+  const int t = row_position(p, a, i);
   const int lp = t / kPage, row = t % kPage;
   const int bpg = p.btab[size_t(a) * p.max_pages + lp];
   const int rpg = p.rtab[size_t(a) * p.max_pages + lp];

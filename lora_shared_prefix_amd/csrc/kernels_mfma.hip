@@ -607,11 +607,14 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pg = w >> 2, tp = w & 3;  // staging role: page of the pair, tile pair / quarter
   const int col = lane & 15, g4 = lane >> 4;
-  const int start = p.start_pos[a];
   const int total_rows = C * G;
   const int row0 = rb * kPfRows;
   const int last_row = min(total_rows, row0 + kPfRows) - 1;
-  const int lp_end = (start + last_row / G) / kPage + 1;  // pages any row of the block sees
+  // positions increase along the chunk: the block's queries span first_pos .. last_pos
+  const int first_pos = row_position(p, a, row0 / G);
+  const int last_pos = row_position(p, a, last_row / G);
+  const int end_pos = row_position(p, a, C - 1) + 1;  // rows at or past end_pos: unwritten
+  const int lp_end = last_pos / kPage + 1;  // pages any row of the block sees
   const int n_it = (lp_end + 1) / 2;
   const int n = Hkv * kD;
   const uint16_t* bcache = static_cast<const uint16_t*>(p.bcache);
@@ -628,7 +631,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     const int row = row0 + kPfRowsPerWave * w + 16 * rt + col;
     rok[rt] = row < total_rows;
     const int qi = rok[rt] ? row / G : 0, g = rok[rt] ? row % G : 0;
-    qpos[rt] = start + qi;
+    qpos[rt] = row_position(p, a, qi);
     const uint16_t* qrow = q + ((size_t(a) * C + qi) * Hq + h * G + g) * kD;
     for (int c = 0; c < 4; ++c) {
       U4 t;
@@ -756,7 +759,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // arbitrary bytes (even NaN); a zero probability times NaN is NaN, so they are zeroed.
     // The 16 bytes this lane stages are the operand pieces of reader lanes 2l and 2l+1
     // (tokens 4 g .. 4 g + 3, g = ((2l) mod 64) / 16); its value-residual piece is its own.
-    const int last = lp < lp_end ? start + C - lp * kPage : 0;
+    const int last = lp < lp_end ? end_pos - lp * kPage : 0;
     uint4 v = B.v;
     uint2 rv = B.rv;
     if (last < kPage) {  // wave-uniform: only the pages at the end of the sequence
@@ -782,10 +785,11 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       }
     }
     U4 pb[2];  // P^T operands, K = 32 keys: elements 0..3 page 0, 4..7 page 1
-    // Both pages exist and lie entirely before the chunk (every key precedes every query):
+    // Both pages exist and lie entirely before the block's first query position (every key
+    // precedes every query):
     // no mask at all.  Rows past the chunk have zero q and are never written, so they need
     // none either.  (Wave-uniform.)
-    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < start;
+    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < first_pos;
     for (int rt = 0; rt < 2; ++rt) {
       // raw scores (q.k); the softmax scale (> 0, log2 units) is applied inside the exp
       float sc[8], pmax = -INFINITY;

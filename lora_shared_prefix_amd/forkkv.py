@@ -70,7 +70,8 @@ class PrefillArgs(C.Structure):
                 ("Bk", C.c_void_p), ("Bv", C.c_void_p), ("btab", C.c_void_p),
                 ("rtab", C.c_void_p), ("max_pages", C.c_int32), ("start_pos", C.c_void_p),
                 ("start_pos_host", _i32p), ("lora_scale", C.c_float), ("sm_scale", C.c_float),
-                ("rope_theta", C.c_float), ("out", C.c_void_p)]
+                ("rope_theta", C.c_float), ("out", C.c_void_p), ("positions", C.c_void_p),
+                ("positions_host", _i32p)]
 
 
 _SIGS = {
@@ -350,14 +351,21 @@ def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, o
 
 def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, btab, rtab,
                           start_pos, start_pos_host, out, lora_scale, sm_scale, rope_theta,
-                          stream=None):
-    """Launch chunked prefill (async): store the chunk rows, then attend causally."""
+                          stream=None, positions=None, positions_host=None):
+    """Launch prefill (async): store the rows, then attend causally.  Rows sit at
+    start_pos[a] + i, or at positions[a][i] when a position list (device int32 [N][C] plus
+    the same values on the host) is given."""
     N, Cn, Hq = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
-    sp = _i32_array(start_pos_host)
+    sp = _i32_array(start_pos_host) if start_pos_host is not None else None
+    ph = (_i32_array([int(x) for row in positions_host for x in row])
+          if positions_host is not None else None)
     args = PrefillArgs(pool.handle, N, Cn, Hq, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                        rk_new.data_ptr(), rv_new.data_ptr(), Bk.data_ptr(), Bv.data_ptr(),
-                       btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]), start_pos.data_ptr(),
-                       C.cast(sp, _i32p), float(lora_scale), float(sm_scale), float(rope_theta),
-                       out.data_ptr())
+                       btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]),
+                       start_pos.data_ptr() if start_pos is not None else None,
+                       C.cast(sp, _i32p) if sp is not None else None, float(lora_scale),
+                       float(sm_scale), float(rope_theta), out.data_ptr(),
+                       positions.data_ptr() if positions is not None else None,
+                       C.cast(ph, _i32p) if ph is not None else None)
     _check(lib().forkkv_residual_attn_prefill(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_prefill")
