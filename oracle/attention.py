@@ -36,11 +36,12 @@ class Geometry:
                    dtype=cfg.dtype)
 
 
-def _cached_rows(geo, bpool, rpool, btab, rtab, a, h, positions):
-    bk = base_key_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype)
-    bv = base_value_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype)
-    rk = res_key_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype)
-    rv = res_value_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype)
+def _cached_rows(geo, bpool, rpool, btab, rtab, a, h, positions, starts=None):
+    st = None if starts is None else starts[a]
+    bk = base_key_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype, st)
+    bv = base_value_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype, st)
+    rk = res_key_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype, st)
+    rv = res_value_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype, st)
     return bk, bv, rk, rv
 
 
@@ -65,12 +66,14 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
 
 
 def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_scale,
-                     sm_scale, theta, agents=None, kv_heads=None):
+                     sm_scale, theta, agents=None, kv_heads=None, starts=None):
     """One decode query per agent over its cached keys 0 .. seq_len-1.
 
     q: [N, Hq, d] (post-RoPE, stored encoding).  Returns fp64 [N, Hq, d]; rows
     not requested through ``agents`` / ``kv_heads`` are NaN.  An agent with no
-    cached keys gets a zero output.
+    cached keys gets a zero output.  ``starts`` ([N][max_pages] page start
+    positions, -1 padded) is the slot map of sequences holding a frozen tail
+    (ForkServe README, "Design vs APC"); None means page lp starts at lp * P.
     """
     N = q.shape[0]
     qv = decode_values(q, geo.dtype)
@@ -85,7 +88,7 @@ def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_sc
             if L == 0:
                 out[a, list(gs)] = 0.0
                 continue
-            bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, pos)
+            bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, pos, starts)
             k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
             for g in gs:
                 p = _softmax_rows(sm_scale * (k @ qv[a, g]))
@@ -93,26 +96,40 @@ def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_sc
     return out
 
 
-def apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new, rv_new):
+def _slot(geo, starts, a, t):
+    """(logical page, row) of position t of agent a, under the slot map if given."""
+    if starts is None:
+        return t // geo.P, t % geo.P
+    st = [s for s in starts[a] if s >= 0]
+    j = max(i for i, s in enumerate(st) if s <= t)
+    return j, t - st[j]
+
+
+def apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new, rv_new,
+                     starts=None):
     """Pool contents after rows are stored (copies; inputs untouched).
 
     Row i of agent a goes to position ``positions[a][i]``: page ``table[a][pos // P]``,
-    row ``pos % P``, laid out as the pool layout says.
+    row ``pos % P`` (under a slot map: the page whose start is the last one <= pos, row
+    pos - start), laid out as the pool layout says.  With ``rk_new`` None only the base
+    pool is written.
     """
     bp, rp = bpool.copy(), rpool.copy()
     N, C = k_new.shape[0], k_new.shape[1]
-    P, d, r = geo.P, geo.d, geo.r
+    d, r = geo.d, geo.r
     dims, ranks = np.arange(d), np.arange(r)
     for a in range(N):
         for i in range(C):
             t = int(positions[a][i])
-            page, row = int(btab[a][t // P]), t % P
+            lp, row = _slot(geo, starts, a, t)
+            page = int(btab[a][lp])
             for h in range(geo.Hkv):
                 bp[page, 0, h, key_offset(row, dims)] = k_new[a, i, h]
                 bp[page, 1, h, value_offset(row, dims)] = v_new[a, i, h]
-            page = int(rtab[a][t // P])
-            rp[page, 0, res_key_offset(row, ranks)] = rk_new[a, i]
-            rp[page, 1, res_value_offset(row, ranks, r)] = rv_new[a, i]
+            if rk_new is not None:
+                page = int(rtab[a][lp])
+                rp[page, 0, res_key_offset(row, ranks)] = rk_new[a, i]
+                rp[page, 1, res_value_offset(row, ranks, r)] = rv_new[a, i]
     return bp, rp
 
 
@@ -171,7 +188,7 @@ def prefill_attention(geo, bpool, rpool, btab, rtab, start_pos, q, k_new, v_new,
 
 
 def prefill_attention_at(geo, bpool, rpool, btab, rtab, positions, q, k_new, v_new, rk_new,
-                         rv_new, Bk, Bv, lora_scale, sm_scale, theta, samples=None):
+                         rv_new, Bk, Bv, lora_scale, sm_scale, theta, samples=None, starts=None):
     """Prefill over an arbitrary list of positions: row i of agent a sits at position
     ``positions[a][i]`` (e.g. a hole in the middle of the history followed by the real
     request's tail -- Penelope review, 部件二: the phantom request and the real request keep
@@ -179,11 +196,11 @@ def prefill_attention_at(geo, bpool, rpool, btab, rtab, positions, q, k_new, v_n
     i attends to keys ``0 .. positions[a][i]`` of the written pools (self included).
 
     Returns fp64 [N, C, Hq, d]; with ``samples`` (a list of (a, i, g)) only those rows are
-    computed and the rest are NaN.
+    computed and the rest are NaN.  ``starts`` is the slot map, as for ``decode_attention``.
     """
     N, C = q.shape[0], q.shape[1]
     bp, rp = apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_new,
-                              rv_new)
+                              rv_new, starts)
     qv = decode_values(q, geo.dtype)
     Bkv, Bvv = decode_values(Bk, geo.dtype), decode_values(Bv, geo.dtype)
     out = np.full((N, C, geo.Hq, geo.d), np.nan)
@@ -198,7 +215,7 @@ def prefill_attention_at(geo, bpool, rpool, btab, rtab, positions, q, k_new, v_n
     for (a, h), rows in sorted(want.items()):
         last = max(int(positions[a][i]) for i, _ in rows)
         pos = np.arange(last + 1, dtype=np.int64)
-        bk, bv, rk, rv = _cached_rows(geo, bp, rp, btab, rtab, a, h, pos)
+        bk, bv, rk, rv = _cached_rows(geo, bp, rp, btab, rtab, a, h, pos, starts)
         k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
         for i, g in rows:
             n_keys = int(positions[a][i]) + 1

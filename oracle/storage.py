@@ -44,34 +44,42 @@ def res_value_offset(t, k, r):
     return (t // 4) * (4 * r) + k * 4 + t % 4
 
 
-def _pages_rows(tab_row: np.ndarray, positions: np.ndarray, P_: int):
-    lp = positions // P_
-    return tab_row[lp].astype(np.int64), (positions % P_).astype(np.int64)
+def _pages_rows(tab_row: np.ndarray, positions: np.ndarray, P_: int, starts_row=None):
+    """Physical page and row of each position.  Without a slot map page lp holds positions
+    lp*P .. lp*P + P-1; with one (``starts_row``: start position of each logical page, -1
+    padded) page lp holds the positions from its start up to the next page's start."""
+    positions = np.asarray(positions, dtype=np.int64)
+    if starts_row is None:
+        lp = positions // P_
+        return np.asarray(tab_row)[lp].astype(np.int64), (positions % P_).astype(np.int64)
+    st = np.asarray([s for s in starts_row if s >= 0], dtype=np.int64)
+    lp = np.searchsorted(st, positions, side="right") - 1
+    return np.asarray(tab_row)[lp].astype(np.int64), (positions - st[lp]).astype(np.int64)
 
 
-def base_key_rows(bpool, btab_row, positions, head, P_, d, dtype):
+def base_key_rows(bpool, btab_row, positions, head, P_, d, dtype, starts_row=None):
     """Stored (post-RoPE) base keys of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P_)
+    pages, rows = _pages_rows(btab_row, positions, P_, starts_row)
     idx = key_offset(rows[:, None], np.arange(d)[None, :])
     return decode_values(bpool[:, 0, head, :][pages[:, None], idx], dtype)
 
 
-def base_value_rows(bpool, btab_row, positions, head, P_, d, dtype):
+def base_value_rows(bpool, btab_row, positions, head, P_, d, dtype, starts_row=None):
     """Base values of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P_)
+    pages, rows = _pages_rows(btab_row, positions, P_, starts_row)
     idx = value_offset(rows[:, None], np.arange(d)[None, :])
     return decode_values(bpool[:, 1, head, :][pages[:, None], idx], dtype)
 
 
-def res_key_rows(rpool, rtab_row, positions, P_, r, dtype):
+def res_key_rows(rpool, rtab_row, positions, P_, r, dtype, starts_row=None):
     """Rank-r key residuals (no RoPE) at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P_)
+    pages, rows = _pages_rows(rtab_row, positions, P_, starts_row)
     idx = res_key_offset(rows[:, None], np.arange(r)[None, :])
     return decode_values(rpool[:, 0, :][pages[:, None], idx], dtype)
 
 
-def res_value_rows(rpool, rtab_row, positions, P_, r, dtype):
+def res_value_rows(rpool, rtab_row, positions, P_, r, dtype, starts_row=None):
     """Rank-r value residuals at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P_)
+    pages, rows = _pages_rows(rtab_row, positions, P_, starts_row)
     idx = res_value_offset(rows[:, None], np.arange(r)[None, :], r)
     return decode_values(rpool[:, 1, :][pages[:, None], idx], dtype)

@@ -23,13 +23,25 @@ def _lists(a):
     return a.tolist() if hasattr(a, "tolist") else a
 
 
+def _slot_of(P, starts_a, t):
+    """(logical page, row) of position t: page t // P, or under a slot map the last page
+    whose start is <= t (linear scan)."""
+    if starts_a is None:
+        return divmod(t, P)
+    j = 0
+    for i, st in enumerate(starts_a):
+        if 0 <= st <= t:
+            j = i
+    return j, t - starts_a[j]
+
+
 def _key_value(P, d, r, dtype, bpool, rpool, btab_a, rtab_a, Bk_a, Bv_a, h, t, s, theta,
-               row_override=None):
+               row_override=None, starts_a=None):
     """Merged key and value of one agent/head at position t (lists of d floats)."""
     if row_override is not None:
         bk, bv, rk, rv = row_override
     else:
-        lp, row = divmod(t, P)
+        lp, row = _slot_of(P, starts_a, t)
         bp, rp = btab_a[lp], rtab_a[lp]
         # tiles are stored in matrix-core operand order (see include/forkkv.h)
         bk = [_val(bpool[bp][0][h][(j // 8) * 128 + row * 8 + j % 8], dtype) for j in range(d)]
@@ -66,8 +78,9 @@ def _attend(qrow, kv, sm_scale, d):
 
 
 def brute_decode(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv,
-                 s, sm_scale, theta):
+                 s, sm_scale, theta, starts=None):
     bpool, rpool, btab, rtab = map(_lists, (bpool, rpool, btab, rtab))
+    starts = None if starts is None else _lists(starts)
     q, Bk, Bv = map(_lists, (q, Bk, Bv))
     G = Hq // Hkv
     out = []
@@ -76,7 +89,8 @@ def brute_decode(P, Hq, Hkv, d, r, dtype, bpool, rpool, btab, rtab, seq_lens, q,
         for g in range(Hq):
             h = g // G
             kv = [_key_value(P, d, r, dtype, bpool, rpool, btab[a], rtab[a], Bk[a], Bv[a], h, t,
-                             s, theta) for t in range(int(seq_lens[a]))]
+                             s, theta, starts_a=None if starts is None else starts[a])
+                  for t in range(int(seq_lens[a]))]
             qrow = [_val(x, dtype) for x in q[a][g]]
             rows.append(_attend(qrow, kv, sm_scale, d))
         out.append(rows)

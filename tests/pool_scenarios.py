@@ -24,11 +24,13 @@ def read_kv(name):
     return out
 
 
-def fanout_ops(L, k, ell):
-    """Snapshot the trunk (base-only), fork k children at L, each writes ell tokens."""
+def fanout_ops(L, k, ell, mode=None, hint=0):
+    """Snapshot the trunk (base-only), fork k children at L, each writes ell tokens.
+    ``mode`` (pool_model.PACK / FREEZE / AUTO, with ``hint``) selects the unaligned-tail
+    treatment; None is the default (pack)."""
     ops = [("create", "trunk", 0), ("append", "trunk", L)]
     for j in range(k):
-        ops.append(("fork", "trunk", L, f"c{j}"))
+        ops.append(("fork", "trunk", L, f"c{j}") + (() if mode is None else (mode, hint)))
     for j in range(k):
         ops.append(("append", f"c{j}", ell))
     return ops

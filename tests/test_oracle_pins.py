@@ -417,3 +417,100 @@ def test_tile_orders_are_permutations_with_lane_linear_operands():
         # residuals, r = 16: key as B operand (ranks 4g + e of row col), value as A operand
         assert [res_key_offset(col, 4 * g + e) for e in range(4)] == [4 * l + e for e in range(4)]
         assert [res_value_offset(4 * g + e, col, 16) for e in range(4)] == [4 * l + e for e in range(4)]
+
+
+# ---- the slot map of frozen tails (ForkServe README, "Design vs APC") ----------------------
+
+def _build_freeze(case):
+    pm = PoolModel(case["num_bpages"], case["num_rpages"], case["P"], case["perm_b"],
+                   case["perm_r"])
+    names = pm.replay(case["ops"])
+    hs = [names[a] for a in case["agents"]]
+    bt, rt, lens = pm.tables(hs, 16)
+    st = pm.starts_table(hs, 16)
+    return np.array(bt), np.array(rt), np.array(lens), np.array(st), pm, hs
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_frozen_tail_decode_matches_brute_force(seed, dtype):
+    """Decode over sequences holding frozen tails: the oracle's slot-map reading against the
+    scalar brute force, which finds each position's page by a linear scan of the starts."""
+    case = tiny_case(300 + seed, dtype, Hq=4, Hkv=2, d=16, r=4, n_agents=4, freeze=True)
+    bt, rt, lens, st, _, _ = _build_freeze(case)
+    assert (st[:, 1:] - st[:, :-1] < 16).any()  # there is a frozen tail somewhere
+    o = _oracle_decode(case, bt, rt, lens, starts=st)
+    b = np.array(brute_decode(case["P"], case["Hq"], case["Hkv"], case["d"], case["r"], dtype,
+                              case["bpool"], case["rpool"], bt, rt, lens, case["q"], case["Bk"],
+                              case["Bv"], case["lora_scale"], case["sm_scale"], case["theta"],
+                              starts=st))
+    assert _nrel(o, b) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_frozen_tail_decode_equals_aligned_relayout(seed):
+    """Moving every position's stored row into a fresh, aligned layout (page t // P, row
+    t % P) leaves the decode unchanged: the slot map only relocates rows."""
+    case = tiny_case(320 + seed, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=4, freeze=True)
+    bt, rt, lens, st, _, _ = _build_freeze(case)
+    geo = _geo(case)
+    N, P = len(lens), 16
+    n_pg = -(-int(lens.max()) // P)
+    nb = N * n_pg
+    bp2 = np.zeros((nb, 2, case["Hkv"], P * case["d"]), dtype=case["bpool"].dtype)
+    rp2 = np.zeros((nb, 2, P * case["r"]), dtype=case["rpool"].dtype)
+    bt2 = np.arange(nb).reshape(N, n_pg)
+    from oracle.storage import _pages_rows
+    for a in range(N):
+        pos = np.arange(int(lens[a]))
+        sp, sr = _pages_rows(bt[a], pos, P, st[a])
+        rpg, _ = _pages_rows(rt[a], pos, P, st[a])
+        dp, dr = bt2[a][pos // P], pos % P
+        for h in range(case["Hkv"]):
+            for x in range(case["d"]):
+                ko = (x // 8) * 128 + x % 8
+                bp2[dp, 0, h, ko + dr * 8] = case["bpool"][sp, 0, h, ko + sr * 8]
+                vo = (x // 16) * 256 + (x % 16) * 4
+                bp2[dp, 1, h, vo + (dr // 4) * 64 + dr % 4] = \
+                    case["bpool"][sp, 1, h, vo + (sr // 4) * 64 + sr % 4]
+        for k in range(case["r"]):
+            ko = (k // 4) * 64 + k % 4
+            rp2[dp, 0, ko + dr * 4] = case["rpool"][rpg, 0, ko + sr * 4]
+            rp2[dp, 1, (dr // 4) * 4 * case["r"] + k * 4 + dr % 4] = \
+                case["rpool"][rpg, 1, (sr // 4) * 4 * case["r"] + k * 4 + sr % 4]
+    o = _oracle_decode(case, bt, rt, lens, starts=st)
+    o2 = decode_attention(geo, bp2, rp2, bt2, bt2, lens, case["q"], case["Bk"], case["Bv"],
+                          case["lora_scale"], case["sm_scale"], case["theta"])
+    assert np.array_equal(o, o2)
+
+
+def test_slot_map_write_lands_on_the_models_slots():
+    """apply_rows_write under the slot map stores each appended row in the slot the pool
+    model's append reported for it (page * P + row)."""
+    rng = np.random.default_rng(5)
+    case = tiny_case(340, "f32", Hq=2, Hkv=1, d=16, r=4, n_agents=3, freeze=True)
+    pm = PoolModel(64, 64, 16, case["perm_b"], case["perm_r"])
+    names = pm.replay(case["ops"])
+    hs = [names[a] for a in case["agents"]]
+    lens0 = [pm.length(h) for h in hs]
+    n = 21
+    slots = [pm.append(h, n) for h in hs]
+    bt, rt, _ = pm.tables(hs, 16)
+    st = pm.starts_table(hs, 16)
+    pos = np.array([[L + i for i in range(n)] for L in lens0])
+    kn = rng.standard_normal((3, n, 1, 16)).astype(np.float32)
+    vn = rng.standard_normal((3, n, 1, 16)).astype(np.float32)
+    rkn = rng.standard_normal((3, n, 4)).astype(np.float32)
+    rvn = rng.standard_normal((3, n, 4)).astype(np.float32)
+    geo = _geo(case)
+    bp, rp = apply_rows_write(geo, case["bpool"], case["rpool"], bt, rt, pos, kn, vn, rkn, rvn,
+                              starts=st)
+    for a in range(3):
+        for i in range(n):
+            page, row = divmod(slots[a][0][i], 16)
+            rpage, rrow = divmod(slots[a][1][i], 16)
+            assert rrow == row
+            got = [bp[page, 0, 0, (x // 8) * 128 + row * 8 + x % 8] for x in range(16)]
+            assert np.array_equal(np.array(got), kn[a, i, 0])
+            got = [rp[rpage, 0, (k // 4) * 64 + row * 4 + k % 4] for k in range(4)]
+            assert np.array_equal(np.array(got), rkn[a, i])

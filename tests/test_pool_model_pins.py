@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import PoolError, PoolModel
+from oracle.pool_model import AUTO, FREEZE, PACK
 from tests.pool_scenarios import clone_ops, fanout_ops, read_kv, read_table
 
 TABLE = read_table("forkserve_results_table.txt")
@@ -158,3 +159,135 @@ def test_free_parent_keeps_trunk_and_order():
     assert pm.stats()["live_bpages"] == 4 and list(pm.free_b) == list(range(4, 16))
     pm.free(c)
     assert list(pm.free_b)[-4:] == [0, 1, 2, 3]
+
+
+# ---- freeze-tail (ForkServe README, "Design vs APC": the adaptive unaligned tail) ---------
+
+@pytest.mark.parametrize("L,k,ell", [(2050, 4, 48), (37, 3, 5), (100, 2, 60), (31, 5, 1),
+                                     (4097, 8, 128)])
+def test_freeze_formula_for_unaligned_tail(L, k, ell):
+    """pages_freeze = 1 + k * ceil(l / P): one read-only tail shared by the trunk and every
+    child, plus each child's own pages; the trunk's full pages are aliased as before."""
+    P = 16
+    pm = PoolModel(4096, 8192)
+    names = pm.replay(fanout_ops(L, k, ell, FREEZE))
+    assert pm.stats()["live_bpages"] == L // P + 1 + k * (-(-ell // P))
+    # the frozen tail is one page, mapped by the trunk and all k children
+    tail_page = pm.tables([names["trunk"]], -(-L // P))[0][0][L // P]
+    assert pm.ref_b[tail_page] == k + 1
+    # the same fan-out packed costs pages_pack instead (the printed scenario row: 145)
+    pk = PoolModel(4096, 8192)
+    pk.replay(fanout_ops(L, k, ell, PACK))
+    assert pk.stats()["live_bpages"] == -(-L // P) + k * (-(-((L % P) + ell) // P))
+    if (L, k, ell) == (2050, 4, 48):
+        assert pk.stats()["live_bpages"] == 145
+
+
+@pytest.mark.parametrize("L,k,ell", [(2050, 4, 10), (2050, 4, 14), (2050, 4, 15), (2061, 3, 6),
+                                     (2061, 3, 40), (2063, 6, 2)])
+def test_adaptive_tail_rule(L, k, ell):
+    """AUTO packs when the trunk tail and the child's suffix fit in one page (r + l <= P),
+    else freezes: the live page count follows the matching formula."""
+    P, r = 16, L % 16
+    pm = PoolModel(4096, 8192)
+    pm.replay(fanout_ops(L, k, ell, AUTO, ell))
+    # pack: the trunk keeps its partial page and each child copies r rows into its own;
+    # freeze: that partial page is the one shared read-only tail
+    want = (1 + k * (-(-(r + ell) // P)) if r + ell <= P else 1 + k * (-(-ell // P)))
+    assert pm.stats()["live_bpages"] == L // P + want
+
+
+def test_freeze_slot_map_covers_each_position_once():
+    """After a freeze fork, positions 0 .. len-1 of every sequence map one to one onto
+    (page, row) slots: the frozen tail holds r rows, later pages start at r-shifted
+    positions, and no slot is used by two positions of one sequence."""
+    P = 16
+    pm = PoolModel(256, 512)
+    names = pm.replay(fanout_ops(37, 3, 21, FREEZE))
+    names["gc"], _ = pm.fork(names["c1"], 37 + 21)  # a grandchild at the child's end (aligned? no)
+    pm.append(names["gc"], 9)
+    pm.append(names["trunk"], 5)  # the trunk continues after its own frozen tail
+    for nm in ("trunk", "c0", "c1", "c2", "gc"):
+        h = names[nm]
+        s = pm.seqs[h]
+        starts = pm.starts_table([h], 8)[0]
+        L = pm.length(h)
+        slots = set()
+        for t in range(L):
+            j = max(i for i, st in enumerate(starts) if 0 <= st <= t)
+            row = t - starts[j]
+            assert 0 <= row < s.rows(j) <= P
+            slots.add((s.bpages[j], row))
+        assert len(slots) == L
+        assert starts[:3] == [0, 16, 32]
+        if nm != "gc" and L > 37:
+            assert starts[3] == 37  # the row after the frozen 5-row tail opens a page
+    # the trunk's tail page is read-only: its own append opened a page at position 37
+    assert pm.seqs[names["trunk"]].rows(2) == 5
+
+
+def test_freeze_only_at_the_parents_end():
+    pm = PoolModel(64, 64)
+    names = pm.replay([("create", "t", 0), ("append", "t", 40)])
+    with pytest.raises(PoolError) as e:
+        pm.fork(names["t"], 37, FREEZE)
+    assert e.value.kind == "EINVAL"
+    c, cow = pm.fork(names["t"], 37, AUTO, 40)  # AUTO cannot freeze there: it packs
+    assert cow == (pm.seqs[names["t"]].bpages[2], pm.seqs[c].bpages[2], 5)
+
+
+# ---- decoupled eviction (ForkKV study note: "Error / eviction recovery", trick 1) --------
+
+def test_base_eviction_keeps_residuals_and_refill_restores_sharing():
+    """Evicting the trunk's base pages leaves every agent's residual pages live (the two
+    pools are evicted independently); the agents hold -1 there, cannot append or fork
+    until refilled, and a refill maps one fresh page per logical page into all of them."""
+    P = 16
+    pm = PoolModel(64, 128)
+    names = pm.replay(fanout_ops(64, 3, 20))
+    kids = [names[f"c{j}"] for j in range(3)]
+    before = pm.stats()
+    bt0, rt0, lens0 = pm.tables(kids, 8)
+    victims = bt0[0][1:3]  # two shared trunk pages
+    pm.evict_base(victims)
+    st = pm.stats()
+    assert st["live_rpages"] == before["live_rpages"] and st["rpage_refs"] == before["rpage_refs"]
+    assert st["live_bpages"] == before["live_bpages"] - 2
+    assert list(pm.free_b)[-2:] == list(victims)
+    bt1, rt1, lens1 = pm.tables(kids, 8)
+    assert rt1 == rt0 and lens1 == lens0
+    for row in bt1:
+        assert row[1:3] == [-1, -1]
+    for h in kids:
+        with pytest.raises(PoolError) as e:
+            pm.append(h, 1)
+        assert e.value.kind == "ESTATE"
+    with pytest.raises(PoolError) as e:
+        pm.fork(kids[0], 40)
+    assert e.value.kind == "ESTATE"
+    pm.fork(kids[0], 16)  # below the evicted range: fine
+    # the trunk (base-only snapshot) lost them too; refill the three agents and the trunk
+    new = pm.refill_base(kids + [names["trunk"]], 1, 3)
+    assert len(new) == 2 and all(pm.ref_b[pg] == 4 for pg in new)
+    bt2, _, _ = pm.tables(kids, 8)
+    for row, row0 in zip(bt2, bt0):
+        assert row[:1] + row[3:] == row0[:1] + row0[3:] and row[1:3] == new
+    pm.append(kids[1], 3)
+
+
+def test_eviction_errors():
+    pm = PoolModel(32, 32)
+    names = pm.replay(fanout_ops(32, 2, 4))
+    kids = [names["c0"], names["c1"]]
+    with pytest.raises(PoolError):
+        pm.evict_base([31 if pm.ref_b[31] == 0 else 30])  # a free page
+    pg = pm.tables([kids[0]], 4)[0][0][0]
+    with pytest.raises(PoolError):
+        pm.evict_base([pg, pg])
+    with pytest.raises(PoolError):
+        pm.refill_base(kids, 0, 1)  # nothing evicted there
+    pm.evict_base([pg])
+    with pytest.raises(PoolError):
+        pm.refill_base(kids, 0, 2)  # page 1 is still mapped
+    st = pm.stats()
+    assert pm.refill_base(kids, 0, 1) and pm.stats()["live_bpages"] == st["live_bpages"] + 1
