@@ -35,8 +35,11 @@
  *     value residual (t, k): (t / 4) * (4 * r) + k * 4 + t % 4
  *   Element type: FORKKV_DTYPE_BF16 (bfloat16) or FORKKV_DTYPE_F32.  P = 16,
  *   d a multiple of 16 (<= 256), r a multiple of 4 (<= 64).
- *   A slot is page * P + row; position t of a sequence lives in page
- *   table[t / P], row t % P.
+ *   A slot is page * P + row.  Position t of a sequence lives in page
+ *   table[t / P], row t % P -- unless a frozen tail (see forkkv_fork_ex) sits in
+ *   its history: then logical page j holds the rows from its start position
+ *   pstart[j] (forkkv_export_starts) up to the next page's start, and the kernels
+ *   take the start table as an extra argument.
  *
  * Fork bookkeeping (host side, bit-exact deterministic)
  * -----------------------------------------------------
@@ -81,6 +84,9 @@ enum {
 };
 
 enum { FORKKV_DTYPE_F32 = 0, FORKKV_DTYPE_BF16 = 1 };
+
+/* Treatment of an unaligned tail at a fork (forkkv_fork_ex). */
+enum { FORKKV_FORK_PACK = 0, FORKKV_FORK_FREEZE = 1, FORKKV_FORK_AUTO = 2 };
 
 /* Decode kernel selection (forkkv_plan_opts.kernel). */
 enum { FORKKV_KERNEL_AUTO = 0, FORKKV_KERNEL_GENERIC = 1, FORKKV_KERNEL_MFMA = 2 };
@@ -146,15 +152,56 @@ int forkkv_seq_append(forkkv_pool* pool, forkkv_seq seq, int32_t n, int32_t* bsl
 int forkkv_fork(forkkv_pool* pool, forkkv_seq parent, int32_t alias_len, forkkv_seq* child,
                 forkkv_cow_op* cow);
 
+/* Fork with a choice for the unaligned tail (ForkServe README, "Design vs APC": the
+ * adaptive tail, pages_pack = k * ceil((r + l) / P) versus pages_freeze = 1 + k * ceil(l / P)).
+ *   FORKKV_FORK_PACK   as forkkv_fork: the child copies the tail's rows into a private page.
+ *   FORKKV_FORK_FREEZE the parent's partial last page becomes read-only for the parent and the
+ *                      child (no copy); later rows of either go to fresh pages, so their pages
+ *                      no longer start at multiples of P (the slot map, forkkv_export_starts).
+ *                      Only at the parent's end (alias_len == len), else FORKKV_EINVAL.
+ *   FORKKV_FORK_AUTO   pack when tail rows + suffix_hint <= P (the child's expected suffix
+ *                      fits the tail page) or the cut is not at the parent's end, else freeze.
+ * Whole pages below alias_len -- full pages and frozen tails -- are aliased as by forkkv_fork.
+ * Errors: FORKKV_EINVAL (bad handle, alias_len, mode or suffix_hint < 0), FORKKV_ESTATE (an
+ * aliased page was evicted), FORKKV_ENOMEM. */
+int forkkv_fork_ex(forkkv_pool* pool, forkkv_seq parent, int32_t alias_len, int32_t mode,
+                   int32_t suffix_hint, forkkv_seq* child, forkkv_cow_op* cow);
+
 /* Release a sequence: each page's reference count drops; pages reaching 0 return to the
  * tail of their free list. */
 int forkkv_seq_free(forkkv_pool* pool, forkkv_seq seq);
 int forkkv_seq_len(const forkkv_pool* pool, forkkv_seq seq, int32_t* len);
+/* Number of logical pages of seq (ceil(len / P), plus one per frozen tail it holds). */
+int forkkv_seq_pages(const forkkv_pool* pool, forkkv_seq seq, int32_t* n_pages);
 
 /* Block tables of n sequences (host outputs): btab, rtab [n][max_pages] page ids padded
  * with -1 (rtab all -1 for base-only sequences); seq_lens [n] (nullable). */
 int forkkv_export_tables(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
                          int32_t max_pages, int32_t* btab, int32_t* rtab, int32_t* seq_lens);
+
+/* Start position of each logical page of n sequences (host output pstart [n][max_pages],
+ * -1 padded): page j holds rows pstart[j] .. pstart[j+1]-1 (the last page up to len-1).
+ * *aligned (host, nullable) = 1 when every page starts at j * P (no frozen tail), in which
+ * case the kernels need no start table. */
+int forkkv_export_starts(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
+                         int32_t max_pages, int32_t* pstart, int32_t* aligned);
+
+/* Decoupled eviction (ForkKV study note, "Error / eviction recovery"; implementation detail
+ * 1): evict base pages (host pages[n], distinct, live) from every sequence that maps them.
+ * Their table entries become -1 and they return to the tail of the base free list in the
+ * order given; residual pages are untouched (the rCache survives).  A sequence with a
+ * missing base page is a partial hit: appends, forks over the gap and decode plans return
+ * FORKKV_ESTATE until it is refilled.  Errors: FORKKV_EINVAL. */
+int forkkv_evict_bpages(forkkv_pool* pool, const int32_t* pages, int32_t n);
+
+/* Partial-hit refill: map fresh base pages into logical pages [lp0, lp1) of the n listed
+ * sequences (host seqs[n], distinct), each of which must miss exactly those pages and agree
+ * on their start positions and row counts.  One page per logical page is shared by all of
+ * them (reference count n); new_pages (host, nullable, lp1 - lp0 entries) receives them.
+ * The caller then stores the recomputed base rows (post-RoPE xW_k and xW_v) there, e.g. with
+ * forkkv_write_rows without residual rows.  Errors: FORKKV_EINVAL, FORKKV_ENOMEM. */
+int forkkv_refill_bpages(forkkv_pool* pool, const forkkv_seq* seqs, int32_t n, int32_t lp0,
+                         int32_t lp1, int32_t* new_pages);
 
 int forkkv_pool_stats(const forkkv_pool* pool, forkkv_stats* out);
 
@@ -231,8 +278,15 @@ typedef struct {
   void* out;                /* device [N][Hq][d], pool dtype; an agent with len 0 gets 0 */
   void* workspace;          /* device, workspace_bytes of the plan */
   size_t workspace_bytes;
+  const int32_t* pstart;    /* device [N][max_pages] page start positions (forkkv_export_starts);
+                               nullable when every page starts at a multiple of P.  Required
+                               when a batch sequence holds a frozen tail (ForkServe README,
+                               "Design vs APC": the fork-aware slot map) */
 } forkkv_decode_args;
 
+/* Errors: FORKKV_EINVAL (null pointers, a plan of another geometry, max_pages below the
+ * plan's, a small workspace, non-finite scales, no pstart for a plan over a frozen tail);
+ * FORKKV_ESTATE (pool without device storage, plan not uploaded); FORKKV_EHIP. */
 int forkkv_residual_attn_decode(const forkkv_decode_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
@@ -297,6 +351,9 @@ typedef struct {
   void* out;                /* device [N][C][Hq][d] */
   const int32_t* positions;      /* nullable: device [N][C], row positions (see above) */
   const int32_t* positions_host; /* host [N][C], same values; required with positions */
+  const int32_t* pstart;         /* nullable: device [N][max_pages] page start positions, for
+                                    sequences holding a frozen tail (the slot map); such calls
+                                    run the generic attention kernel */
 } forkkv_prefill_args;
 
 /* Errors: FORKKV_EINVAL for null pointers, C < 1, a head count that is not a multiple of
@@ -305,6 +362,36 @@ typedef struct {
  * device storage; FORKKV_EHIP when a launch fails. */
 
 int forkkv_residual_attn_prefill(const forkkv_prefill_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Row write without attention: store rows into the pools at given positions, bit exact.
+ * Used after a partial-hit refill (forkkv_refill_bpages; ForkKV study note, "Error /
+ * eviction recovery": only the base projection xW is recomputed and re-inserted, the
+ * surviving residual xA_i is reused) with rk_new = rv_new = NULL, which leaves the
+ * residual pool untouched; with residual rows it is the row-store half of a prefill.
+ * Row i of sequence a goes to position positions[a][i], in the page the tables (and the
+ * slot map, if given) name for it.
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  const forkkv_pool* pool;
+  int32_t n_seqs;                /* N */
+  int32_t n_rows;                /* R >= 1 rows per sequence */
+  const int32_t* btab;           /* device [N][max_pages] */
+  const int32_t* rtab;           /* device [N][max_pages]; may be NULL when rk_new is */
+  const int32_t* pstart;         /* nullable: device [N][max_pages] page start positions */
+  int32_t max_pages;
+  const int32_t* positions;      /* device [N][R], strictly increasing per sequence */
+  const int32_t* positions_host; /* host [N][R], same values (validation, launch shape) */
+  const void* k_new;             /* device [N][R][Hkv][d], post-RoPE base keys */
+  const void* v_new;             /* device [N][R][Hkv][d] */
+  const void* rk_new;            /* nullable: device [N][R][r] (NULL together with rv_new) */
+  const void* rv_new;
+} forkkv_write_args;
+
+/* Errors: FORKKV_EINVAL (null pointers, R < 1, positions not strictly increasing or outside
+ * the tables, only one of rk_new / rv_new given); FORKKV_ESTATE (no device storage);
+ * FORKKV_EHIP.  A row whose table entry is -1 (an evicted page) is not stored. */
+int forkkv_write_rows(const forkkv_write_args* args, hipStream_t stream);
 
 #ifdef __cplusplus
 }

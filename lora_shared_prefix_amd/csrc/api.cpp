@@ -78,6 +78,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   if (!pl->dev) return FORKKV_ESTATE;
   if (!a->q || !a->Bk || !a->Bv || !a->btab || !a->rtab || !a->out) return FORKKV_EINVAL;
   if (a->max_pages < pl->max_pages_needed) return FORKKV_EINVAL;
+  if (!pl->aligned && !a->pstart) return FORKKV_EINVAL;  // a frozen tail needs the slot map
   if (pl->n_slots > 0 && (!a->workspace || a->workspace_bytes < pl->workspace_bytes))
     return FORKKV_EINVAL;
   if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->rope_theta > 0.f) ||
@@ -94,6 +95,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   p.rcache = pool->rcache;
   p.btab = a->btab;
   p.rtab = a->rtab;
+  p.pstart = a->pstart;
   p.plan = static_cast<const int32_t*>(pl->dev);
   char* ws = static_cast<char*>(a->workspace);
   p.ws_ml = reinterpret_cast<float*>(ws);
@@ -186,6 +188,8 @@ int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipSt
   w.rcache = a->decode.pool->rcache;
   w.btab = a->decode.btab;
   w.rtab = a->decode.rtab;
+  w.pstart = a->decode.pstart;
+  w.write_res = true;
   w.start_pos = p.plan + off_lens;  // the plan's lengths, on the device
   w.pos_bias = -1;                  // the new token sits at position length - 1
   w.n_agents = pl->n_agents;
@@ -247,6 +251,8 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   p.rtab = a->rtab;
   p.start_pos = a->start_pos;
   p.positions = a->positions;
+  p.pstart = a->pstart;
+  p.write_res = true;
   p.out = a->out;
   p.n_agents = a->n_agents;
   p.chunk_len = a->chunk_len;
@@ -266,12 +272,57 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
 
   (void)hipGetLastError();
   if (forkkv::launch_prefill_write(p, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  // (the MFMA prefill kernel assumes pages at multiples of P: a slot map runs the generic one)
   const bool mfma = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, p.group) &&
-                    forkkv::prefill_mfma_enabled();
+                    forkkv::prefill_mfma_enabled() && !a->pstart;
   hipError_t err = mfma ? forkkv::launch_prefill_mfma(p, a->start_pos_host, stream)
                         : forkkv::launch_prefill_generic(p, g.dtype, stream);
   if (err != hipSuccess) return FORKKV_EHIP;
   if (hipGetLastError() != hipSuccess) return FORKKV_EHIP;
+  return FORKKV_OK;
+}
+
+int forkkv_write_rows(const forkkv_write_args* a, hipStream_t stream) {
+  if (!a || !a->pool) return FORKKV_EINVAL;
+  const forkkv_pool* pool = a->pool;
+  const forkkv_pool_desc& g = pool->desc;
+  if (!pool->bcache) return FORKKV_ESTATE;
+  if (a->n_seqs < 0 || a->n_rows < 1 || a->max_pages < 1) return FORKKV_EINVAL;
+  if (a->n_seqs == 0) return FORKKV_OK;
+  const bool res = a->rk_new != nullptr;
+  if ((a->rv_new != nullptr) != res) return FORKKV_EINVAL;
+  if (!a->btab || (res && !a->rtab) || !a->positions || !a->positions_host || !a->k_new ||
+      !a->v_new)
+    return FORKKV_EINVAL;
+  const int64_t cap = int64_t(a->max_pages) * kPage;
+  for (int32_t i = 0; i < a->n_seqs; ++i) {
+    const int32_t* pos = a->positions_host + size_t(i) * a->n_rows;
+    if (pos[0] < 0 || pos[a->n_rows - 1] >= cap) return FORKKV_EINVAL;
+    for (int32_t c = 1; c < a->n_rows; ++c)
+      if (pos[c] <= pos[c - 1]) return FORKKV_EINVAL;
+  }
+  forkkv::PrefillParams w{};
+  w.k_new = a->k_new;
+  w.v_new = a->v_new;
+  w.rk_new = a->rk_new;
+  w.rv_new = a->rv_new;
+  w.bcache = pool->bcache;
+  w.rcache = pool->rcache;
+  w.btab = a->btab;
+  w.rtab = a->rtab;
+  w.pstart = a->pstart;
+  w.write_res = res;
+  w.positions = a->positions;
+  w.n_agents = a->n_seqs;
+  w.chunk_len = a->n_rows;
+  w.num_kv_heads = g.num_kv_heads;
+  w.head_dim = g.head_dim;
+  w.rank = g.rank;
+  w.max_pages = a->max_pages;
+  w.num_bpages = g.num_bpages;
+  w.num_rpages = g.num_rpages;
+  (void)hipGetLastError();
+  if (forkkv::launch_prefill_write(w, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
   return FORKKV_OK;
 }
 

@@ -34,8 +34,31 @@ constexpr int32_t kPlanMagic = 0x464b5631;  // "FKV1"
 struct Seq {
   bool alive = true;
   bool has_res = false;
+  bool closed = false;            // the last page takes no more rows (a frozen tail)
   int32_t len = 0;
   std::vector<int32_t> bpages, rpages;
+  std::vector<int32_t> starts;    // position of row 0 of each logical page (the slot map)
+
+  // rows of logical page j that belong to this sequence
+  int32_t rows(size_t j) const {
+    const int32_t end = j + 1 < starts.size() ? starts[j + 1] : len;
+    return end - starts[j];
+  }
+  // rows that still fit in the last page
+  int32_t room() const {
+    if (bpages.empty() || closed) return 0;
+    return kPage - rows(bpages.size() - 1);
+  }
+  bool aligned() const {  // every page starts at a multiple of the page size
+    for (size_t j = 0; j < starts.size(); ++j)
+      if (starts[j] != static_cast<int32_t>(j) * kPage) return false;
+    return true;
+  }
+  bool missing_base() const {
+    for (int32_t pg : bpages)
+      if (pg < 0) return true;
+    return false;
+  }
 };
 
 }  // namespace forkkv
@@ -55,6 +78,7 @@ struct forkkv_plan {
   void* rcache = nullptr;
   int32_t n_agents = 0, n_items = 0, n_slots = 0, num_q_heads = 0, kernel = 0;
   int32_t group = 0;        // agents per item the kernel was planned for
+  bool aligned = true;      // every page of every agent starts at a multiple of P
   std::vector<int32_t> blob;
   void* dev = nullptr;      // caller's device copy
   size_t workspace_bytes = 0;
@@ -93,6 +117,7 @@ struct DecodeParams {
   const int32_t* btab;
   const int32_t* rtab;
   const int32_t* plan;      // device blob
+  const int32_t* pstart;    // nullable: [N][max_pages] start position of each page
   float* ws_ml;             // [slots][Hq][2]  (running max in log2 units, sum)
   float* ws_acc;            // [slots][Hq][d]
   float* ws_accr;           // [slots][Hq][r]
@@ -118,6 +143,8 @@ struct PrefillParams {
   const int32_t* start_pos;
   const int32_t* positions;  // nullable: [N][C] position of every row (strictly increasing
                              // per agent); null: row i of agent a at start_pos[a] + i
+  const int32_t* pstart;     // nullable: [N][max_pages] start position of each page
+  bool write_res;            // the row write stores the residual rows too
   void* out;
   int32_t n_agents, chunk_len, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
@@ -128,6 +155,37 @@ struct PrefillParams {
 // Position of row i of agent a (both kernels and the row write agree on it).
 __host__ __device__ inline int row_position(const PrefillParams& p, int a, int i) {
   return p.positions ? p.positions[size_t(a) * p.chunk_len + i] : p.start_pos[a] + p.pos_bias + i;
+}
+
+// The slot map.  Logical page lp of agent a holds the positions from its start up to the
+// next page's start (P rows for a full page, fewer for a frozen tail); without a start
+// table (null) page lp starts at lp * P.
+__host__ __device__ inline int page_start(const int32_t* pstart, int max_pages, int a, int lp) {
+  return pstart ? pstart[size_t(a) * max_pages + lp] : lp * kPage;
+}
+// Rows of page lp held by agent a of length len (<= P; <= 0 past the end).
+__host__ __device__ inline int page_rows(const int32_t* pstart, int max_pages, int a, int lp,
+                                         int len) {
+  int end = len, st = lp * kPage;
+  if (pstart) {
+    const int32_t* row = pstart + size_t(a) * max_pages;
+    st = row[lp];
+    if (lp + 1 < max_pages && row[lp + 1] >= 0 && row[lp + 1] < end) end = row[lp + 1];
+  }
+  return end - st < kPage ? end - st : kPage;
+}
+// Logical page of position t >= 0: the last page whose start is <= t (binary search; the
+// starts increase and are -1 past the last page).
+__host__ __device__ inline int page_of(const int32_t* pstart, int max_pages, int a, int t) {
+  if (!pstart) return t / kPage;
+  const int32_t* row = pstart + size_t(a) * max_pages;
+  int lo = 0, hi = max_pages - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (row[mid] >= 0 && row[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 // Kernel launchers (defined in the .hip translation units).  They return hipError_t

@@ -11,6 +11,7 @@
 // kernel, or in the epilogue of the prefill kernel).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 
 #include "forkkv_internal.h"
@@ -92,6 +93,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
   const T* rcache = static_cast<const T*>(kPrefill ? pp.rcache : dp.rcache);
   const int32_t* btab = kPrefill ? pp.btab : dp.btab;
   const int32_t* rtab = kPrefill ? pp.rtab : dp.rtab;
+  const int32_t* pstart = kPrefill ? pp.pstart : dp.pstart;  // slot map (nullable)
   const T* q = static_cast<const T*>(kPrefill ? pp.q : dp.q);
   const T* Bk = static_cast<const T*>(kPrefill ? pp.Bk : dp.Bk);
   const int half = d / 2;
@@ -116,7 +118,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     na = 1;
     agents[0] = a_pf;
     lp_begin = 0;
-    lp_end = last_pos / kPage + 1;
+    lp_end = page_of(pstart, max_pages, a_pf, last_pos) + 1;
   } else {
     const int32_t* it = dp.plan + dp.off_items + blockIdx.x * kItemInts;
     lp_begin = it[0];
@@ -166,13 +168,21 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     const size_t kbase = (size_t(bpg) * 2 * Hkv + h) * kPage * d;
     const size_t vbase = (size_t(bpg) * 2 * Hkv + Hkv + h) * kPage * d;
     // Rows no query of this workgroup may read are never loaded: their contents are
-    // arbitrary (even NaN) and a zero probability times NaN would still be NaN.
+    // arbitrary (even NaN) and a zero probability times NaN would still be NaN.  The page's
+    // first position (shared by the item's agents, which map the same page) and the rows
+    // each agent holds come from the slot map.
+    const int pos0 = page_start(pstart, max_pages, agents[0], lp);
     int vrows;
+    int prow[kItemAgents];  // rows of this page held by agent j
     if constexpr (kPrefill) {
-      vrows = min(kPage, max(0, last_pos + 1 - lp * kPage));
+      prow[0] = max(0, min(page_rows(pstart, max_pages, a_pf, lp, INT_MAX), last_pos + 1 - pos0));
+      vrows = prow[0];
     } else {
       vrows = 0;
-      for (int j = 0; j < na; ++j) vrows = max(vrows, min(kPage, limit[j] - lp * kPage));
+      for (int j = 0; j < na; ++j) {
+        prow[j] = max(0, page_rows(pstart, max_pages, agents[j], lp, limit[j]));
+        vrows = max(vrows, prow[j]);
+      }
     }
     for (int i = tid; i < kPage * d; i += kGenericThreads) {
       // stored tiles are in matrix-core operand order; see TileOrder
@@ -196,7 +206,7 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     }
     for (int i = tid; i < kPage * half; i += kGenericThreads) {
       const int row = i / half, jj = i % half;
-      double ang = static_cast<double>(lp * kPage + row) * inv[jj];
+      double ang = static_cast<double>(pos0 + row) * inv[jj];
       ang -= kTwoPi * floor(ang / kTwoPi);
       double sv, cv;
       sincos(ang, &sv, &cv);
@@ -224,17 +234,17 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
       const int nrows = kPrefill ? rows : G;
       for (int i = tid; i < nrows * kPage; i += kGenericThreads) {
         const int row = row0 + i / kPage, t = i % kPage;
-        const int pos = lp * kPage + t;
+        const int pos = pos0 + t;
         size_t qoff;
         bool valid;
         if constexpr (kPrefill) {
           const int qi = q0 + row / G, g = row % G;
           qoff = ((size_t(a_pf) * C + qi) * Hq + h * G + g) * d;
-          valid = pos <= row_position(pp, a_pf, qi);
+          valid = t < prow[0] && pos <= row_position(pp, a_pf, qi);
         } else {
           const int g = row % G;
           qoff = (size_t(agents[j]) * Hq + h * G + g) * d;
-          valid = pos < limit[j];
+          valid = t < prow[j];
         }
         valid = valid && rok[j];
         float sc = -INFINITY;
@@ -471,15 +481,19 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
   }
 }
 
-// Store the chunk rows at their slots (bit-exact copies in the pool layout).
+// Store the chunk rows at their slots (bit-exact copies in the pool layout).  The slot of
+// position t is its page under the slot map and its offset from the page's start; a row
+// whose slot falls outside a page (a malformed start table) is not stored.
 template <typename T>
 __global__ void __launch_bounds__(256) prefill_write_kernel(PrefillParams p) {
   const int i = blockIdx.x, a = blockIdx.y, tid = threadIdx.x;
   const int d = p.head_dim, r = p.rank, Hkv = p.num_kv_heads, C = p.chunk_len;
   const int t = row_position(p, a, i);
-  const int lp = t / kPage, row = t % kPage;
+  const int lp = page_of(p.pstart, p.max_pages, a, t);
+  const int row = t - page_start(p.pstart, p.max_pages, a, lp);
+  if (lp < 0 || lp >= p.max_pages || row < 0 || row >= kPage) return;
   const int bpg = p.btab[size_t(a) * p.max_pages + lp];
-  const int rpg = p.rtab[size_t(a) * p.max_pages + lp];
+  const int rpg = p.write_res ? p.rtab[size_t(a) * p.max_pages + lp] : -1;
   T* bc = static_cast<T*>(p.bcache);
   T* rc = static_cast<T*>(p.rcache);
   const T* kn = static_cast<const T*>(p.k_new) + (size_t(a) * C + i) * Hkv * d;

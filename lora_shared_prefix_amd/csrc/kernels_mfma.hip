@@ -145,7 +145,10 @@ __device__ __forceinline__ int perm_dim(int T, int m) {
   return 32 * (T >> 1) + 8 * (m >> 2) + 4 * (T & 1) + (m & 3);
 }
 
-template <int A>  // agents per group (columns = agents x G <= 16)
+// A: agents per group (columns = agents x G <= 16).  kMap: the batch holds a frozen tail and
+// page starts come from the start table (the slot map); without it page lp starts at lp * P
+// and none of that bookkeeping is compiled in.
+template <int A, bool kMap>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeParams p, int n_items) {
   __shared__ __align__(16) unsigned char lds[kLdsBytes];
@@ -227,7 +230,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int jc = col / G;                   // agent (within group) of this lane's column
   const bool col_ok = active && col < na_g * G;
   const int a_col = col_ok ? it[4 + j0 + jc] : 0;
-  const int len_col = col_ok ? p.plan[p.off_lens + a_col] : 0;
+  const int32_t* const pstart = kMap ? p.pstart : nullptr;  // the slot map (see above)
   bf8 qv[4];
   {
     const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
@@ -269,10 +272,14 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
   // cos/sin(t0 * w_j) for lane j = frequency j, at this wave's first page, with the angle
   // reduced in fp64; later pages follow by the rotation (cos, sin)(16 w_j).  Over the at
-  // most 64 pages of a wave the recurrence drifts by a few 1e-6 rad at most.
+  // most 64 pages of a wave the recurrence drifts by a few 1e-6 rad at most.  Pages start
+  // at lp * P unless a frozen tail precedes them (the slot map): a page whose start differs
+  // from the recurrence's position re-anchors it by the (at most P - 1 positions) gap.
   float pc, ps, step_c, step_s;
+  const float omega_f = static_cast<float>(omega);
+  int next_pos = (active && lpa < lpb) ? page_start(pstart, p.max_pages, agent[0], lpa) : 0;
   {
-    double ang = static_cast<double>(lpa * kPage) * omega;
+    double ang = static_cast<double>(next_pos) * omega;
     ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
     double sv, cv;
     sincos(ang, &sv, &cv);
@@ -351,11 +358,25 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     if (B.bp < 0) return;  // wave-uniform
     VBuf V;
     load_v(B, V, na_c);
+    // rows of this page held by each agent (the page's start is common to them all)
     int vrows = 0, minrows = kPage;
+    int prow[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      vrows = max(vrows, min(kPage, rlen[j] - lp * kPage));
-      minrows = min(minrows, rlen[j] - lp * kPage);
+      prow[j] = page_rows(pstart, p.max_pages, agent[j], lp, rlen[j]);
+      vrows = max(vrows, prow[j]);
+      minrows = min(minrows, prow[j]);
+    }
+    if constexpr (kMap) {
+      const int pos0 = page_start(pstart, p.max_pages, agent[0], lp);
+      if (pos0 != next_pos) {  // wave-uniform: re-anchor the rotation at this page's start
+        float sv, cv;
+        sincosf(static_cast<float>(pos0 - next_pos) * omega_f, &sv, &cv);
+        const float c = mul_sub(pc, cv, ps, sv);
+        ps = mul_add(ps, cv, pc, sv);
+        pc = c;
+      }
+      next_pos = pos0 + kPage;
     }
     // Rows no column may read are zeroed: their bytes are arbitrary (even NaN).
     const bool row_ok = col < vrows;  // this lane's key row (tok = col) in the A operands
@@ -468,9 +489,12 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         pmax = fmaxf(pmax, sc[i]);
       }
     } else {
+      int rows_col = prow[0];  // rows of the page held by this lane's column's agent
+#pragma unroll
+      for (int j = 1; j < NA; ++j)
+        if (jc == j) rows_col = prow[j];
       for (int i = 0; i < 4; ++i) {
-        const int pos = lp * kPage + 4 * g4 + i;
-        sc[i] = (col_ok && pos < len_col) ? ssel[i] * qscale : -INFINITY;
+        sc[i] = (col_ok && 4 * g4 + i < rows_col) ? ssel[i] * qscale : -INFINITY;
         pmax = fmaxf(pmax, sc[i]);
       }
     }
@@ -914,13 +938,21 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
   const int A = agents_per_group(p.group);
   const int n_items = p.n_items;
   const int blocks = 8 * p.num_kv_heads * ((n_items + 7) / 8);
-  switch (A) {
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<2>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<1>), dim3(blocks), dim3(kThreads), 0, s, p, n_items); break;
+#define FORKKV_DECODE_LAUNCH(NA, MAP) \
+  hipLaunchKernelGGL((decode_mfma_kernel<NA, MAP>), dim3(blocks), dim3(kThreads), 0, s, p, n_items)
+  const bool map = p.pstart != nullptr;
+  switch (A * 2 + (map ? 1 : 0)) {
+    case 8: FORKKV_DECODE_LAUNCH(4, false); break;
+    case 9: FORKKV_DECODE_LAUNCH(4, true); break;
+    case 6: FORKKV_DECODE_LAUNCH(3, false); break;
+    case 7: FORKKV_DECODE_LAUNCH(3, true); break;
+    case 4: FORKKV_DECODE_LAUNCH(2, false); break;
+    case 5: FORKKV_DECODE_LAUNCH(2, true); break;
+    case 2: FORKKV_DECODE_LAUNCH(1, false); break;
+    case 3: FORKKV_DECODE_LAUNCH(1, true); break;
     default: return hipErrorInvalidValue;
   }
+#undef FORKKV_DECODE_LAUNCH
   return hipGetLastError();
 }
 

@@ -44,6 +44,11 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
     if (!S[a]->alive || !S[a]->has_res) return FORKKV_EINVAL;
     max_np = std::max<int32_t>(max_np, static_cast<int32_t>(S[a]->bpages.size()));
   }
+  // a partial hit (an evicted base page) must be refilled before it can be attended to
+  for (int32_t a = 0; a < n; ++a)
+    if (S[a]->missing_base()) return FORKKV_ESTATE;
+  bool aligned = true;
+  for (int32_t a = 0; a < n; ++a) aligned = aligned && S[a]->aligned();
   forkkv_plan_opts o{};
   if (opts) o = *opts;
   int kernel = o.kernel;
@@ -184,6 +189,7 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   pl->num_q_heads = num_q_heads;
   pl->kernel = kernel;
   pl->group = cap;
+  pl->aligned = aligned;
   pl->max_pages_needed = max_np;
 
   std::vector<int32_t>& b = pl->blob;

@@ -3,8 +3,11 @@
 // ForkKV study note, "3. 架构 / 方法图" (Figure 6): a new agent maps the parent's
 // read-only base pages and allocates only its own residual pages.  ForkServe README,
 // "Design vs APC", "Methods" (CoW tree) and "Status": fork aliases the parent's frames,
-// writes allocate private pages, an unaligned tail is packed by copying its n_valid rows,
-// and reference counts keep a trunk alive after its parent is freed.
+// writes allocate private pages, an unaligned tail is packed by copying its n_valid rows
+// or frozen into one read-only page shared by the trunk and its children (the adaptive
+// tail), and reference counts keep a trunk alive after its parent is freed.  ForkKV study
+// note, "Error / eviction recovery": base pages can be evicted while the residual pages
+// survive, and refilled later (partial hit).
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -129,11 +132,15 @@ int forkkv_seq_append(forkkv_pool* p, forkkv_seq h, int32_t n, int32_t* bslots,
                       int32_t* rslots, forkkv_cow_op* cow) {
   Seq* s = get_seq(p, h);
   if (!s || n < 0) return FORKKV_EINVAL;
+  if (s->missing_base()) return FORKKV_ESTATE;
   const int64_t new_len = int64_t(s->len) + n;
   if (new_len > INT32_MAX / 2) return FORKKV_EINVAL;
-  const int32_t grow = ceil_div(new_len, kPage) - static_cast<int32_t>(s->bpages.size());
+  // rows fill the last page while it has room (a frozen tail has none), then fresh pages
+  const int32_t room = s->room();
+  const int32_t grow = ceil_div(std::max<int64_t>(0, int64_t(n) - room), kPage);
+  const size_t last = s->bpages.empty() ? 0 : s->bpages.size() - 1;
   // A write into a shared partial last page needs a private copy first.
-  const bool need_cow = n > 0 && (s->len % kPage) != 0 && p->ref_b[s->bpages.back()] > 1;
+  const bool need_cow = n > 0 && room > 0 && s->rows(last) > 0 && p->ref_b[s->bpages[last]] > 1;
   const int32_t need_b = grow + (need_cow ? 1 : 0);
   const int32_t need_r = s->has_res ? grow : 0;
   if (need_b > static_cast<int32_t>(p->free_b.size()) ||
@@ -141,46 +148,101 @@ int forkkv_seq_append(forkkv_pool* p, forkkv_seq h, int32_t n, int32_t* bslots,
     return FORKKV_ENOMEM;
   clear_cow(cow);
   if (need_cow) {
-    const int32_t old = s->bpages.back();
+    const int32_t old = s->bpages[last];
     const int32_t fresh = take(p->free_b, p->ref_b);
     p->ref_b[old] -= 1;
-    s->bpages.back() = fresh;
-    if (cow) *cow = forkkv_cow_op{old, fresh, s->len % kPage};
+    s->bpages[last] = fresh;
+    if (cow) *cow = forkkv_cow_op{old, fresh, s->rows(last)};
   }
+  const size_t first_new = s->bpages.size();
+  const int32_t nxt = s->len + room;  // start of the first fresh page
   for (int32_t i = 0; i < grow; ++i) {
     s->bpages.push_back(take(p->free_b, p->ref_b));
+    s->starts.push_back(nxt + i * kPage);
     if (s->has_res) s->rpages.push_back(take(p->free_r, p->ref_r));
   }
   for (int32_t i = 0; i < n; ++i) {
     const int32_t t = s->len + i;
-    if (bslots) bslots[i] = s->bpages[t / kPage] * kPage + t % kPage;
-    if (rslots) rslots[i] = s->has_res ? s->rpages[t / kPage] * kPage + t % kPage : -1;
+    size_t j;
+    int32_t row;
+    if (t < nxt) {
+      j = last;
+      row = t - s->starts[last];
+    } else {
+      j = first_new + (t - nxt) / kPage;
+      row = (t - nxt) % kPage;
+    }
+    if (bslots) bslots[i] = s->bpages[j] * kPage + row;
+    if (rslots) rslots[i] = s->has_res ? s->rpages[j] * kPage + row : -1;
   }
   s->len = static_cast<int32_t>(new_len);
+  if (grow) s->closed = false;
   return FORKKV_OK;
 }
 
 int forkkv_fork(forkkv_pool* p, forkkv_seq parent, int32_t alias_len, forkkv_seq* child,
                 forkkv_cow_op* cow) {
+  return forkkv_fork_ex(p, parent, alias_len, FORKKV_FORK_PACK, 0, child, cow);
+}
+
+int forkkv_fork_ex(forkkv_pool* p, forkkv_seq parent, int32_t alias_len, int32_t mode,
+                   int32_t suffix_hint, forkkv_seq* child, forkkv_cow_op* cow) {
   Seq* ps = get_seq(p, parent);
-  if (!ps || !child || alias_len < 0 || alias_len > ps->len) return FORKKV_EINVAL;
-  const int32_t full = alias_len / kPage;
-  const int32_t tail = alias_len % kPage;
-  const int32_t need_b = tail ? 1 : 0;
-  const int32_t need_r = ceil_div(alias_len, kPage);
+  if (!ps || !child || alias_len < 0 || alias_len > ps->len || suffix_hint < 0 ||
+      (mode != FORKKV_FORK_PACK && mode != FORKKV_FORK_FREEZE && mode != FORKKV_FORK_AUTO))
+    return FORKKV_EINVAL;
+  // whole pages (full, or frozen tails) below alias_len are aliased; the page cut by
+  // alias_len, or the parent's open partial last page, is the unaligned tail
+  const size_t n_pg = ps->bpages.size();
+  size_t whole = 0, tail_j = 0;
+  int32_t tail = 0;
+  for (size_t j = 0; j < n_pg; ++j) {
+    const int32_t st = ps->starts[j], nr = ps->rows(j);
+    if (st >= alias_len) break;
+    const bool open = j + 1 == n_pg && !ps->closed && nr < kPage;
+    if (st + nr <= alias_len && !open) {
+      ++whole;
+    } else {
+      tail_j = j;
+      tail = alias_len - st;
+      break;
+    }
+  }
+  for (size_t j = 0; j < whole + (tail ? 1 : 0); ++j)
+    if (ps->bpages[j] < 0) return FORKKV_ESTATE;
+  if (mode == FORKKV_FORK_AUTO)
+    mode = (tail + suffix_hint <= kPage || alias_len != ps->len) ? FORKKV_FORK_PACK
+                                                                  : FORKKV_FORK_FREEZE;
+  if (tail && mode == FORKKV_FORK_FREEZE && alias_len != ps->len) return FORKKV_EINVAL;
+  const bool freeze = tail && mode == FORKKV_FORK_FREEZE;
+  const int32_t need_b = (tail && !freeze) ? 1 : 0;
+  const int32_t need_r = static_cast<int32_t>(whole) + (tail ? 1 : 0);
   if (need_b > static_cast<int32_t>(p->free_b.size()) ||
       need_r > static_cast<int32_t>(p->free_r.size()))
     return FORKKV_ENOMEM;
   clear_cow(cow);
   Seq c;
   c.has_res = true;
-  c.bpages.assign(ps->bpages.begin(), ps->bpages.begin() + full);
+  c.bpages.assign(ps->bpages.begin(), ps->bpages.begin() + whole);
+  c.starts.assign(ps->starts.begin(), ps->starts.begin() + whole);
   for (int32_t pg : c.bpages) p->ref_b[pg] += 1;
   if (tail) {
-    const int32_t src = ps->bpages[full];
-    const int32_t fresh = take(p->free_b, p->ref_b);
-    c.bpages.push_back(fresh);
-    if (cow) *cow = forkkv_cow_op{src, fresh, tail};
+    c.starts.push_back(ps->starts[tail_j]);
+    if (freeze) {
+      const int32_t pg = ps->bpages[tail_j];
+      p->ref_b[pg] += 1;
+      c.bpages.push_back(pg);
+      ps->closed = true;
+      c.closed = true;
+    } else {
+      const int32_t src = ps->bpages[tail_j];
+      const int32_t fresh = take(p->free_b, p->ref_b);
+      c.bpages.push_back(fresh);
+      if (cow) *cow = forkkv_cow_op{src, fresh, tail};
+    }
+  } else if (whole && ps->rows(whole - 1) < kPage &&
+             ps->starts[whole - 1] + ps->rows(whole - 1) == alias_len) {
+    c.closed = true;  // ends on a frozen tail
   }
   for (int32_t i = 0; i < need_r; ++i) c.rpages.push_back(take(p->free_r, p->ref_r));
   c.len = alias_len;
@@ -193,13 +255,64 @@ int forkkv_seq_free(forkkv_pool* p, forkkv_seq h) {
   Seq* s = get_seq(p, h);
   if (!s) return FORKKV_EINVAL;
   for (int32_t pg : s->bpages)
-    if (--p->ref_b[pg] == 0) p->free_b.push_back(pg);
+    if (pg >= 0 && --p->ref_b[pg] == 0) p->free_b.push_back(pg);  // (-1: evicted)
   for (int32_t pg : s->rpages)
     if (--p->ref_r[pg] == 0) p->free_r.push_back(pg);
   s->alive = false;
+  s->closed = false;
   s->len = 0;
   s->bpages.clear();
   s->rpages.clear();
+  s->starts.clear();
+  return FORKKV_OK;
+}
+
+int forkkv_evict_bpages(forkkv_pool* p, const int32_t* pages, int32_t n) {
+  if (!p || n < 0 || (n > 0 && !pages)) return FORKKV_EINVAL;
+  std::vector<char> gone(p->desc.num_bpages, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pg = pages[i];
+    if (pg < 0 || pg >= p->desc.num_bpages || p->ref_b[pg] == 0 || gone[pg]) return FORKKV_EINVAL;
+    gone[pg] = 1;
+  }
+  for (Seq& s : p->seqs) {
+    if (!s.alive) continue;
+    for (int32_t& pg : s.bpages)
+      if (pg >= 0 && gone[pg]) pg = -1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    p->ref_b[pages[i]] = 0;
+    p->free_b.push_back(pages[i]);
+  }
+  return FORKKV_OK;
+}
+
+int forkkv_refill_bpages(forkkv_pool* p, const forkkv_seq* seqs, int32_t n, int32_t lp0,
+                         int32_t lp1, int32_t* new_pages) {
+  if (!p || n < 1 || !seqs || lp0 < 0 || lp1 <= lp0) return FORKKV_EINVAL;
+  std::vector<Seq*> ss;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* s = get_seq(p, seqs[i]);
+    if (!s) return FORKKV_EINVAL;
+    for (int32_t k = 0; k < i; ++k)
+      if (seqs[k] == seqs[i]) return FORKKV_EINVAL;
+    ss.push_back(s);
+  }
+  for (Seq* s : ss) {
+    if (static_cast<size_t>(lp1) > s->bpages.size()) return FORKKV_EINVAL;
+    for (int32_t j = lp0; j < lp1; ++j)
+      if (s->bpages[j] != -1) return FORKKV_EINVAL;
+  }
+  for (Seq* s : ss)
+    for (int32_t j = lp0; j < lp1; ++j)
+      if (s->starts[j] != ss[0]->starts[j] || s->rows(j) != ss[0]->rows(j)) return FORKKV_EINVAL;
+  if (lp1 - lp0 > static_cast<int32_t>(p->free_b.size())) return FORKKV_ENOMEM;
+  for (int32_t j = lp0; j < lp1; ++j) {
+    const int32_t pg = take(p->free_b, p->ref_b);
+    p->ref_b[pg] = n;
+    for (Seq* s : ss) s->bpages[j] = pg;
+    if (new_pages) new_pages[j - lp0] = pg;
+  }
   return FORKKV_OK;
 }
 
@@ -207,6 +320,13 @@ int forkkv_seq_len(const forkkv_pool* p, forkkv_seq h, int32_t* len) {
   const Seq* s = get_seq(p, h);
   if (!s || !len) return FORKKV_EINVAL;
   *len = s->len;
+  return FORKKV_OK;
+}
+
+int forkkv_seq_pages(const forkkv_pool* p, forkkv_seq h, int32_t* n_pages) {
+  const Seq* s = get_seq(p, h);
+  if (!s || !n_pages) return FORKKV_EINVAL;
+  *n_pages = static_cast<int32_t>(s->bpages.size());
   return FORKKV_OK;
 }
 
@@ -228,6 +348,25 @@ int forkkv_export_tables(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n
     std::copy(s->rpages.begin(), s->rpages.end(), rt);
     if (seq_lens) seq_lens[i] = s->len;
   }
+  return FORKKV_OK;
+}
+
+int forkkv_export_starts(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
+                         int32_t max_pages, int32_t* pstart, int32_t* aligned) {
+  if (!p || n < 0 || (n > 0 && (!seqs || !pstart)) || max_pages < 0) return FORKKV_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get_seq(p, seqs[i]);
+    if (!s || static_cast<int32_t>(s->starts.size()) > max_pages) return FORKKV_EINVAL;
+  }
+  int32_t all = 1;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get_seq(p, seqs[i]);
+    int32_t* row = pstart + size_t(i) * max_pages;
+    std::fill(row, row + max_pages, -1);
+    std::copy(s->starts.begin(), s->starts.end(), row);
+    if (!s->aligned()) all = 0;
+  }
+  if (aligned) *aligned = all;
   return FORKKV_OK;
 }
 

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libforkkv.so")
 OK, EINVAL, ENOMEM, EHIP, ESTATE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16 = 0, 1
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
+FORK_PACK, FORK_FREEZE, FORK_AUTO = 0, 1, 2
 PAGE = 16
 
 _i32p = C.POINTER(C.c_int32)
@@ -55,7 +56,8 @@ class DecodeArgs(C.Structure):
                 ("Bk", C.c_void_p), ("Bv", C.c_void_p), ("btab", C.c_void_p),
                 ("rtab", C.c_void_p), ("max_pages", C.c_int32), ("lora_scale", C.c_float),
                 ("sm_scale", C.c_float), ("rope_theta", C.c_float), ("out", C.c_void_p),
-                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("pstart", C.c_void_p)]
 
 
 class DecodeAppendArgs(C.Structure):
@@ -71,7 +73,15 @@ class PrefillArgs(C.Structure):
                 ("rtab", C.c_void_p), ("max_pages", C.c_int32), ("start_pos", C.c_void_p),
                 ("start_pos_host", _i32p), ("lora_scale", C.c_float), ("sm_scale", C.c_float),
                 ("rope_theta", C.c_float), ("out", C.c_void_p), ("positions", C.c_void_p),
-                ("positions_host", _i32p)]
+                ("positions_host", _i32p), ("pstart", C.c_void_p)]
+
+
+class WriteArgs(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("n_seqs", C.c_int32), ("n_rows", C.c_int32),
+                ("btab", C.c_void_p), ("rtab", C.c_void_p), ("pstart", C.c_void_p),
+                ("max_pages", C.c_int32), ("positions", C.c_void_p), ("positions_host", _i32p),
+                ("k_new", C.c_void_p), ("v_new", C.c_void_p), ("rk_new", C.c_void_p),
+                ("rv_new", C.c_void_p)]
 
 
 _SIGS = {
@@ -82,8 +92,13 @@ _SIGS = {
     "forkkv_seq_create": (C.c_int, [C.c_void_p, C.c_int32, _i32p]),
     "forkkv_seq_append": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, _i32p, _i32p, C.POINTER(CowOp)]),
     "forkkv_fork": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, _i32p, C.POINTER(CowOp)]),
+    "forkkv_fork_ex": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _i32p, C.POINTER(CowOp)]),
+    "forkkv_export_starts": (C.c_int, [C.c_void_p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p]),
+    "forkkv_evict_bpages": (C.c_int, [C.c_void_p, _i32p, C.c_int32]),
+    "forkkv_refill_bpages": (C.c_int, [C.c_void_p, _i32p, C.c_int32, C.c_int32, C.c_int32, _i32p]),
     "forkkv_seq_free": (C.c_int, [C.c_void_p, C.c_int32]),
     "forkkv_seq_len": (C.c_int, [C.c_void_p, C.c_int32, _i32p]),
+    "forkkv_seq_pages": (C.c_int, [C.c_void_p, C.c_int32, _i32p]),
     "forkkv_export_tables": (C.c_int, [C.c_void_p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, _i32p]),
     "forkkv_pool_stats": (C.c_int, [C.c_void_p, C.POINTER(Stats)]),
     "forkkv_free_list": (C.c_int, [C.c_void_p, C.c_int32, _i32p, C.c_int32, _i32p]),
@@ -99,6 +114,7 @@ _SIGS = {
     "forkkv_residual_attn_decode": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "forkkv_residual_attn_decode_append": (C.c_int, [C.POINTER(DecodeAppendArgs), C.c_void_p]),
     "forkkv_residual_attn_prefill": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
+    "forkkv_write_rows": (C.c_int, [C.POINTER(WriteArgs), C.c_void_p]),
 }
 
 _lib = None
@@ -200,11 +216,37 @@ class Pool:
             return None, None, cow_t
         return list(bs)[:n], list(rs)[:n], cow_t
 
-    def fork(self, parent, alias_len):
+    def fork(self, parent, alias_len, mode=None, suffix_hint=0):
+        """Fork (mode None: forkkv_fork, i.e. pack; else forkkv_fork_ex with FORK_*)."""
         child, cow = C.c_int32(), CowOp()
-        _check(lib().forkkv_fork(self.handle, parent, alias_len, C.byref(child), C.byref(cow)),
-               "forkkv_fork")
+        if mode is None:
+            _check(lib().forkkv_fork(self.handle, parent, alias_len, C.byref(child),
+                                     C.byref(cow)), "forkkv_fork")
+        else:
+            _check(lib().forkkv_fork_ex(self.handle, parent, alias_len, int(mode),
+                                        int(suffix_hint), C.byref(child), C.byref(cow)),
+                   "forkkv_fork_ex")
         return child.value, ((cow.src_bpage, cow.dst_bpage, cow.n_rows) if cow.n_rows else None)
+
+    def starts(self, seqs, max_pages):
+        """Page start positions [n][max_pages] (-1 padded) and whether all are aligned."""
+        n = len(seqs)
+        out = (C.c_int32 * max(n * max_pages, 1))()
+        al = C.c_int32()
+        _check(lib().forkkv_export_starts(self.handle, _i32_array(seqs), n, max_pages, out,
+                                          C.byref(al)), "forkkv_export_starts")
+        out = list(out)
+        return [out[i * max_pages:(i + 1) * max_pages] for i in range(n)], bool(al.value)
+
+    def evict_base(self, pages):
+        _check(lib().forkkv_evict_bpages(self.handle, _i32_array(pages), len(pages)),
+               "forkkv_evict_bpages")
+
+    def refill_base(self, seqs, lp0, lp1):
+        out = (C.c_int32 * max(lp1 - lp0, 1))()
+        _check(lib().forkkv_refill_bpages(self.handle, _i32_array(seqs), len(seqs), lp0, lp1,
+                                          out), "forkkv_refill_bpages")
+        return list(out)[:max(lp1 - lp0, 0)]
 
     def free(self, seq):
         _check(lib().forkkv_seq_free(self.handle, seq), "forkkv_seq_free")
@@ -212,6 +254,11 @@ class Pool:
     def length(self, seq):
         out = C.c_int32()
         _check(lib().forkkv_seq_len(self.handle, seq, C.byref(out)), "forkkv_seq_len")
+        return out.value
+
+    def pages(self, seq):
+        out = C.c_int32()
+        _check(lib().forkkv_seq_pages(self.handle, seq, C.byref(out)), "forkkv_seq_pages")
         return out.value
 
     def tables(self, seqs, max_pages):
@@ -260,7 +307,7 @@ class Pool:
                 if cow:
                     cows.append(cow)
             elif op[0] == "fork":
-                names[op[3]], cow = self.fork(names[op[1]], op[2])
+                names[op[3]], cow = self.fork(names[op[1]], op[2], *op[4:])
                 if cow:
                     cows.append(cow)
             else:
@@ -322,27 +369,30 @@ class Plan:
 
 
 def residual_attn_decode(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, workspace,
-                         lora_scale, sm_scale, rope_theta, stream=None):
-    """Launch decode (async).  All tensors on the device; btab/rtab int32 [N][max_pages]."""
+                         lora_scale, sm_scale, rope_theta, stream=None, pstart=None):
+    """Launch decode (async).  All tensors on the device; btab/rtab int32 [N][max_pages];
+    pstart (int32 [N][max_pages]) is the page start table of batches with a frozen tail."""
     args = DecodeArgs(pool.handle, plan.handle, q.data_ptr(), Bk.data_ptr(), Bv.data_ptr(),
                       btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]), float(lora_scale),
                       float(sm_scale), float(rope_theta), out.data_ptr(),
                       workspace.data_ptr() if workspace is not None else None,
-                      workspace.numel() * workspace.element_size() if workspace is not None else 0)
+                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                      _ptr(pstart))
     _check(lib().forkkv_residual_attn_decode(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_decode")
 
 
 def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, workspace,
                                 lora_scale, sm_scale, rope_theta, k_new, v_new, rk_new, rv_new,
-                                stream=None):
+                                stream=None, pstart=None):
     """Store each agent's new token (k_new/v_new [N][Hkv][d], rk_new/rv_new [N][r]) at
     position len - 1, then decode over keys 0 .. len - 1 (async)."""
     d = DecodeArgs(pool.handle, plan.handle, q.data_ptr(), Bk.data_ptr(), Bv.data_ptr(),
                    btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]), float(lora_scale),
                    float(sm_scale), float(rope_theta), out.data_ptr(),
                    workspace.data_ptr() if workspace is not None else None,
-                   workspace.numel() * workspace.element_size() if workspace is not None else 0)
+                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                   _ptr(pstart))
     args = DecodeAppendArgs(d, k_new.data_ptr(), v_new.data_ptr(), rk_new.data_ptr(),
                             rv_new.data_ptr())
     _check(lib().forkkv_residual_attn_decode_append(C.byref(args), _stream(stream)),
@@ -351,7 +401,7 @@ def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, o
 
 def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, btab, rtab,
                           start_pos, start_pos_host, out, lora_scale, sm_scale, rope_theta,
-                          stream=None, positions=None, positions_host=None):
+                          stream=None, positions=None, positions_host=None, pstart=None):
     """Launch prefill (async): store the rows, then attend causally.  Rows sit at
     start_pos[a] + i, or at positions[a][i] when a position list (device int32 [N][C] plus
     the same values on the host) is given."""
@@ -366,6 +416,18 @@ def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, b
                        C.cast(sp, _i32p) if sp is not None else None, float(lora_scale),
                        float(sm_scale), float(rope_theta), out.data_ptr(),
                        positions.data_ptr() if positions is not None else None,
-                       C.cast(ph, _i32p) if ph is not None else None)
+                       C.cast(ph, _i32p) if ph is not None else None, _ptr(pstart))
     _check(lib().forkkv_residual_attn_prefill(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_prefill")
+
+
+def write_rows(pool: Pool, btab, rtab, positions, positions_host, k_new, v_new, rk_new=None,
+               rv_new=None, pstart=None, stream=None):
+    """Store rows at positions[a][i] without attention (async); with rk_new = rv_new = None
+    only the base pool is written (a partial-hit refill)."""
+    N, R = int(k_new.shape[0]), int(k_new.shape[1])
+    ph = _i32_array([int(x) for row in positions_host for x in row])
+    args = WriteArgs(pool.handle, N, R, btab.data_ptr(), _ptr(rtab) if rtab is not None else None,
+                     _ptr(pstart), int(btab.shape[1]), positions.data_ptr(), C.cast(ph, _i32p),
+                     k_new.data_ptr(), v_new.data_ptr(), _ptr(rk_new), _ptr(rv_new))
+    _check(lib().forkkv_write_rows(C.byref(args), _stream(stream)), "forkkv_write_rows")

@@ -59,13 +59,18 @@ class DeviceBatch:
             self.make_plan(kernel, pages_per_item, max_agents_per_item, stream)
 
     def refresh_tables(self, extra_pages=0):
-        lens = [self.pool.length(h) for h in self.handles]
-        self.max_pages = max(1, max((-(-L // fk.PAGE) for L in lens), default=1) + extra_pages)
+        """Upload the block tables and, when a sequence holds a frozen tail, the page start
+        table (the slot map; ``pstart`` is None for aligned batches)."""
+        pages = [self.pool.pages(h) for h in self.handles]
+        self.max_pages = max(1, max(pages, default=1) + extra_pages)
         bt, rt, self.lens = self.pool.tables(self.handles, self.max_pages)
         self.btab_host = np.array(bt, dtype=np.int32).reshape(len(self.handles), self.max_pages)
         self.rtab_host = np.array(rt, dtype=np.int32).reshape(len(self.handles), self.max_pages)
         self.btab = torch.from_numpy(self.btab_host).to(self.device)
         self.rtab = torch.from_numpy(self.rtab_host).to(self.device)
+        st, aligned = self.pool.starts(self.handles, self.max_pages)
+        self.pstart_host = np.array(st, dtype=np.int32).reshape(len(self.handles), self.max_pages)
+        self.pstart = None if aligned else torch.from_numpy(self.pstart_host).to(self.device)
 
     def make_plan(self, kernel=fk.KERNEL_AUTO, pages_per_item=0, max_agents_per_item=0,
                   stream=None):
@@ -77,7 +82,8 @@ class DeviceBatch:
     def decode(self, lora_scale, sm_scale, rope_theta, stream=None, q=None, out=None):
         fk.residual_attn_decode(self.pool, self.plan, self.q if q is None else q, self.Bk,
                                 self.Bv, self.btab, self.rtab, self.out if out is None else out,
-                                self.workspace, lora_scale, sm_scale, rope_theta, stream)
+                                self.workspace, lora_scale, sm_scale, rope_theta, stream,
+                                pstart=self.pstart)
         return self.out if out is None else out
 
     def decode_append(self, rows, lora_scale, sm_scale, rope_theta, stream=None, out=None):
@@ -87,7 +93,7 @@ class DeviceBatch:
         fk.residual_attn_decode_append(self.pool, self.plan, self.q, self.Bk, self.Bv, self.btab,
                                        self.rtab, out, self.workspace, lora_scale, sm_scale,
                                        rope_theta, rows["k_new"], rows["v_new"], rows["rk_new"],
-                                       rows["rv_new"], stream)
+                                       rows["rv_new"], stream, pstart=self.pstart)
         return out
 
     # ---- chunked prefill ---------------------------------------------------------------
@@ -109,7 +115,7 @@ class DeviceBatch:
         fk.residual_attn_prefill(self.pool, chunk["q"], chunk["k_new"], chunk["v_new"],
                                  chunk["rk_new"], chunk["rv_new"], self.Bk, self.Bv, self.btab,
                                  self.rtab, self.start_dev, self.start, out, lora_scale,
-                                 sm_scale, rope_theta, stream)
+                                 sm_scale, rope_theta, stream, pstart=self.pstart)
         return out
 
 

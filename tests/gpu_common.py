@@ -64,13 +64,18 @@ def apply_cows_host(bpool, cows, Hkv, d):
     return out
 
 
-def used_rows(bt, rt, lens):
-    """Sets of (page, row) slots read by the batch."""
+def used_rows(bt, rt, lens, starts=None):
+    """Sets of (page, row) slots read by the batch (``starts``: the slot map, if any)."""
     b, r = set(), set()
     for a in range(len(lens)):
         for t in range(int(lens[a])):
-            b.add((int(bt[a][t // 16]), t % 16))
-            r.add((int(rt[a][t // 16]), t % 16))
+            if starts is None:
+                j, row = t // 16, t % 16
+            else:
+                j = max(i for i, s in enumerate(starts[a]) if 0 <= s <= t)
+                row = t - int(starts[a][j])
+            b.add((int(bt[a][j]), row))
+            r.add((int(rt[a][j]), row))
     return b, r
 
 

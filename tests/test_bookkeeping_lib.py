@@ -241,3 +241,126 @@ def test_plan_rejects_base_only_and_bad_heads():
         fk.Plan(lp, [c], 3)
     p = fk.Plan(lp, [], 4)
     assert p.info["n_items"] == 0
+
+
+# ---- freeze-tail forks, the slot map, base eviction and refill --------------------------
+
+_KIND = {"EINVAL": fk.EINVAL, "ENOMEM": fk.ENOMEM, "ESTATE": fk.ESTATE}
+
+
+def _both(lp_call, pm_call):
+    """Run the same operation on the library and the model: same result or same error."""
+    try:
+        exp = pm_call()
+    except PoolError as e:
+        with pytest.raises(fk.ForkKVError) as ei:
+            lp_call()
+        assert ei.value.code == _KIND[e.kind], (e.kind, ei.value.code)
+        return None, False
+    got = lp_call()
+    return (got, exp), True
+
+
+def _same_starts(lp, pm, handles):
+    if handles:
+        mp = max(1, max(len(pm.seqs[h].bpages) for h in handles))
+        got, aligned = lp.starts(handles, mp)
+        exp = pm.starts_table(handles, mp)
+        assert got == exp
+        assert aligned == all(row[j] == 16 * j for row in exp for j in range(mp) if row[j] >= 0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_freeze_evict_refill_match_model(seed):
+    """Random scripts mixing pack / freeze / auto forks, appends, frees, base evictions and
+    refills: the library's free lists, reference counts, tables, slot maps, copies and
+    error codes equal the model's after every step."""
+    rng = np.random.default_rng(7000 + seed)
+    nb, nr = 48, 64
+    lp, pm = _pair(nb, nr, rng.permutation(nb), rng.permutation(nr))
+    live = []
+    for step in range(300):
+        op = int(rng.integers(0, 8))
+        if op == 0 or not live:
+            res = bool(rng.integers(0, 2))
+            assert lp.create(res) == pm.create(res)
+            live.append(pm.seqs.__len__() - 1)
+        elif op in (1, 2):
+            h = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 30))
+            r, ok = _both(lambda: lp.append(h, n), lambda: pm.append(h, n))
+            if ok:
+                assert r[0] == r[1]
+        elif op in (3, 4):
+            h = live[int(rng.integers(len(live)))]
+            L = pm.length(h)
+            alias = L if rng.integers(0, 2) else int(rng.integers(0, L + 1))
+            mode = int(rng.integers(0, 3))
+            hint = int(rng.integers(0, 24))
+            r, ok = _both(lambda: lp.fork(h, alias, mode, hint), lambda: pm.fork(h, alias, mode, hint))
+            if ok:
+                assert r[0] == r[1]
+                live.append(r[1][0])
+        elif op == 5:
+            h = live.pop(int(rng.integers(len(live))))
+            lp.free(h)
+            pm.free(h)
+        elif op == 6:  # evict one or two live base pages (or an invalid list)
+            pages = [p for p in range(nb) if pm.ref_b[p] > 0]
+            if rng.integers(0, 4) == 0 or not pages:
+                pages = [int(rng.integers(0, nb))] * 2
+            else:
+                pages = [int(x) for x in rng.choice(pages, size=min(2, len(pages)), replace=False)]
+            _both(lambda: lp.evict_base(pages), lambda: pm.evict_base(pages))
+        else:  # refill a missing run for every live sequence that misses it
+            miss = [(h, j) for h in live for j, pg in enumerate(pm.seqs[h].bpages) if pg < 0]
+            if miss:
+                h0, j0 = miss[int(rng.integers(len(miss)))]
+                hs = [h for h in live if j0 < len(pm.seqs[h].bpages) and pm.seqs[h].bpages[j0] < 0
+                      and pm.seqs[h].starts[:j0 + 1] == pm.seqs[h0].starts[:j0 + 1]]
+                r, ok = _both(lambda: lp.refill_base(hs, j0, j0 + 1),
+                              lambda: pm.refill_base(hs, j0, j0 + 1))
+                if ok:
+                    assert r[0] == r[1]
+        _same_state(lp, pm, live)
+        _same_starts(lp, pm, live)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_freeze_scenarios_match_model(mode):
+    """The six printed fan-out scenarios under each tail mode (hint = the child's suffix)."""
+    for row in read_table("forkserve_results_table.txt"):
+        L, k, ell = int(row[1]), int(row[2]), int(row[3])
+        lp, pm = _pair(1 << 15, 1 << 16)
+        names = _replay_both_modes(lp, pm, fanout_ops(L, k, ell, mode, ell))
+        _same_state(lp, pm, list(names.values()))
+        _same_starts(lp, pm, list(names.values()))
+
+
+def _replay_both_modes(lp, pm, ops):
+    names_l, cows_l = lp.replay(ops)
+    names_m = pm.replay(ops)
+    assert names_l == names_m
+    return names_l
+
+
+def test_plan_rejects_partial_hit_and_flags_frozen_tail():
+    """A plan over a sequence with an evicted base page fails with FORKKV_ESTATE; a batch
+    holding a frozen tail needs the slot map (checked at decode time, see the GPU tests)."""
+    lp = fk.Pool(64, 64, 1, 16, 4, "f32")
+    names, _ = lp.replay([("create", "t", 0), ("append", "t", 37),
+                          ("fork", "t", 37, "a", fk.FORK_FREEZE, 0),
+                          ("fork", "t", 37, "b", fk.FORK_FREEZE, 0),
+                          ("append", "a", 5), ("append", "b", 20)])
+    hs = [names["a"], names["b"]]
+    st, aligned = lp.starts(hs, 5)
+    assert not aligned and st[0] == [0, 16, 32, 37, -1] and st[1] == [0, 16, 32, 37, 53]
+    fk.Plan(lp, hs, 2, kernel=fk.KERNEL_GENERIC)
+    bt, _, _ = lp.tables(hs, 5)
+    lp.evict_base([bt[0][1]])
+    with pytest.raises(fk.ForkKVError) as e:
+        fk.Plan(lp, hs, 2, kernel=fk.KERNEL_GENERIC)
+    assert e.value.code == fk.ESTATE
+    new = lp.refill_base(hs + [names["t"]], 1, 2)
+    assert lp.tables(hs, 5)[0][0][1] == new[0]
+    fk.Plan(lp, hs, 2, kernel=fk.KERNEL_GENERIC)
