@@ -50,7 +50,7 @@ constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 constexpr int kBkBytes = kItemAgents * 8 * 64 * 8;      // [agent][tile][lane][4 bf16]
 constexpr int kTrigBytes = 2 * kPage * kTrigPad * 2;    // cos, sin: [c][j] (scaled by s)
 constexpr int kPageTrigBytes = kWaves * 2 * 64 * 2;     // per wave: cos[64], sin[64]
-constexpr int kQhBytes = kWaves * 4 * 64 * 16;          // per wave: fp16 q, [chunk][lane]
+constexpr int kQhBytes = kWaves * 4 * 64 * 16;          // per wave: bf16 q, [chunk][lane]
 constexpr int kMergeFloats = 4 + 32 + 4;                // m, l, pad, pad | acc[32] | accr[4]
 constexpr int kMergeBytes = kWaves * 64 * kMergeFloats * 4;
 constexpr int kBkRawBytes = kItemAgents * kR * kD * 2;  // B_k rows before the permutation
@@ -185,7 +185,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   _Float16* trig_c = reinterpret_cast<_Float16*>(lds + kBkBytes);      // [c][kTrigPad]
   _Float16* trig_s = trig_c + kPage * kTrigPad;
   _Float16* ptrig = reinterpret_cast<_Float16*>(lds + kBkBytes + kTrigBytes) + w * 128;
-  uint4* qh_lds =
+  uint4* qb_lds =
       reinterpret_cast<uint4*>(lds + kBkBytes + kTrigBytes + kPageTrigBytes) + w * 4 * 64;
 
   // ---- stage B_k slices (A-operand order) and the in-page trig table ----------------------
@@ -231,27 +231,21 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const bool col_ok = active && col < na_g * G;
   const int a_col = col_ok ? it[4 + j0 + jc] : 0;
   const int32_t* const pstart = kMap ? p.pstart : nullptr;  // the slot map (see above)
-  bf8 qv[4];
+  // The rotated residual keys are formed in fp16 (packed arithmetic) and scored against an
+  // fp16 copy of q, kept in registers (it is read by every agent's score of every page);
+  // the shared base tile is scored in bf16 against the bf16 q, kept in LDS (this wave's
+  // slot, lane-linear) and read once per page.
+  H8 qhr[4];
   {
     const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
     for (int c = 0; c < 4; ++c) {
       U4 t;
       t.u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
-      qv[c] = t.b;
+      qb_lds[c * 64 + lane] = t.u;
+      const uint32_t wds[4] = {t.u.x, t.u.y, t.u.z, t.u.w};
+      for (int e = 0; e < 4; ++e)
+        qhr[c].p[e] = pack_f16x2(__uint_as_float(wds[e] << 16), __uint_as_float(wds[e] & 0xffff0000u));
     }
-  }
-  // the rotated residual keys are formed in fp16 (packed arithmetic) and scored against
-  // an fp16 copy of q; the shared base tile is scored in bf16
-  // an fp16 copy of q; the shared base tile is scored in bf16.  The fp16 copy lives in
-  // LDS (this wave's slot, lane-linear) and is read where it is used.
-  for (int c = 0; c < 4; ++c) {
-    U4 t;
-    t.b = qv[c];
-    const uint32_t wds[4] = {t.u.x, t.u.y, t.u.z, t.u.w};
-    H8 hq;
-    for (int e = 0; e < 4; ++e)
-      hq.p[e] = pack_f16x2(__uint_as_float(wds[e] << 16), __uint_as_float(wds[e] & 0xffff0000u));
-    qh_lds[c * 64 + lane] = hq.u;
   }
   int agent[A], rlen[A];
   for (int j = 0; j < A; ++j) {
@@ -416,7 +410,11 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
     // -- scores: shared base tile, plus for each agent its rotated residual key --
     f4 sb = f4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < 4; ++c) sb = mfma32(B.kt[c].b, qv[c], sb);
+    for (int c = 0; c < 4; ++c) {
+      U4 qb;
+      qb.u = qb_lds[c * 64 + lane];
+      sb = mfma32(B.kt[c].b, qb.b, sb);
+    }
     // Work units u = (half, agent): half h covers score chunks h and h + 2, i.e. the
     // reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.  The units are
     // software-pipelined: the reconstruction MFMAs of unit u + 1 are issued before the
@@ -449,11 +447,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
           k2.p[2 * k + q2] = mul_add2(y, c, x, sn);
         }
       }
-      H8 q0, q2v;
-      q0.u = qh_lds[half * 64 + lane];
-      q2v.u = qh_lds[(half + 2) * 64 + lane];
-      sj[j] = mfma32h(k0.v, q0.v, sj[j]);
-      sj[j] = mfma32h(k2.v, q2v.v, sj[j]);
+      sj[j] = mfma32h(k0.v, qhr[half].v, sj[j]);
+      sj[j] = mfma32h(k2.v, qhr[half + 2].v, sj[j]);
     };
     f4 dA[4], dB[4];
     U2 oA[4], oB[4];
