@@ -188,69 +188,75 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   uint4* qb_lds =
       reinterpret_cast<uint4*>(lds + kBkBytes + kTrigBytes + kPageTrigBytes) + w * 4 * 64;
 
-  // ---- stage B_k slices (A-operand order) and the in-page trig table ----------------------
-  // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
-  // trig-table area (filled only afterwards), then permute into the MFMA A-operand order.
-  {
-    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + kBkBytes);
-    for (int x = tid; x < na * kR * (kD / 8); x += kThreads) {  // 16-byte pieces
-      const int jj = x / (kR * 16), k = (x / 16) % kR, piece = x % 16;
-      const int a = it[4 + jj];
-      *reinterpret_cast<uint4*>(raw + (jj * kR + k) * kD + 8 * piece) =
-          *reinterpret_cast<const uint4*>(Bk + (size_t(a) * kR + k) * n + h * kD + 8 * piece);
-    }
-    __syncthreads();
-    for (int x = tid; x < na * 8 * 64; x += kThreads) {
-      const int jj = x / (8 * 64), T = (x / 64) % 8, l = x % 64;
-      const int dim = perm_dim(T, l & 15);
-      const uint16_t* src = raw + jj * kR * kD + dim;
-      const int k0 = 4 * (l >> 4);
-      uint2 v;
-      v.x = uint32_t(src[k0 * kD]) | (uint32_t(src[(k0 + 1) * kD]) << 16);
-      v.y = uint32_t(src[(k0 + 2) * kD]) | (uint32_t(src[(k0 + 3) * kD]) << 16);
-      bkl[x] = v;
-    }
-    __syncthreads();
-  }
-  // w_j = theta^(-2j/d) = 2^(-(2j/d) log2 theta); lane j keeps w_j in fp64 (j = lane)
-  const double log2_theta = log2(static_cast<double>(p.rope_theta));
-  const double omega = exp2(-2.0 * lane / kD * log2_theta);
-  for (int x = tid; x < kPage * 64; x += kThreads) {
-    const int c = x / 64, j = x % 64;
-    // in-page offsets c < 16: the angle c * w_j is small and sincosf is accurate there
-    const float ang = static_cast<float>(c * exp2(-2.0 * j / kD * log2_theta));
-    float sv, cv;
-    sincosf(ang, &sv, &cv);
-    trig_c[c * kTrigPad + j] = static_cast<_Float16>(cv * p.lora_scale);
-    trig_s[c * kTrigPad + j] = static_cast<_Float16>(sv * p.lora_scale);
-  }
-  __syncthreads();
+  // ---- prologue ---------------------------------------------------------------------------
+  // Every load that depends on nothing else is issued first (this wave's query columns, the
+  // group's agents and lengths, the page ids of the sub-range, the B_k rows), so that their
+  // latencies overlap; the first page's key tiles follow as soon as its ids are in, and the
+  // on-chip set-up (B_k permutation, trig tables) runs while they are in flight.
+  const int pps = (np + n_sub - 1) / n_sub;
+  const int lpa = active ? lp0 + si * pps : 0;
+  const int lpb = active ? min(lp0 + np, lpa + pps) : 0;
+  const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
 
-  // ---- this wave's query columns ----------------------------------------------------------
-  const int jc = col / G;                   // agent (within group) of this lane's column
-  const bool col_ok = active && col < na_g * G;
-  const int a_col = col_ok ? it[4 + j0 + jc] : 0;
-  const int32_t* const pstart = kMap ? p.pstart : nullptr;  // the slot map (see above)
-  // The rotated residual keys are formed in fp16 (packed arithmetic) and scored against an
-  // fp16 copy of q, kept in registers (it is read by every agent's score of every page);
-  // the shared base tile is scored in bf16 against the bf16 q, kept in LDS (this wave's
-  // slot, lane-linear) and read once per page.
-  H8 qhr[4];
-  {
-    const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
-    for (int c = 0; c < 4; ++c) {
-      U4 t;
-      t.u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
-      qb_lds[c * 64 + lane] = t.u;
-      const uint32_t wds[4] = {t.u.x, t.u.y, t.u.z, t.u.w};
-      for (int e = 0; e < 4; ++e)
-        qhr[c].p[e] = pack_f16x2(__uint_as_float(wds[e] << 16), __uint_as_float(wds[e] & 0xffff0000u));
-    }
-  }
-  int agent[A], rlen[A];
+  // ---- this wave's agents and query columns ------------------------------------------------
+  int agent[A], slot[A], rlen[A];  // wave-uniform
+#pragma unroll
   for (int j = 0; j < A; ++j) {
     agent[j] = (active && j < na_g) ? it[4 + j0 + j] : 0;
+    slot[j] = (active && j < na_g) ? it[4 + kItemAgents + j0 + j] : 0;
     rlen[j] = (active && j < na_g) ? p.plan[p.off_lens + agent[j]] : 0;
+  }
+  const int jc = col / G;                   // agent (within group) of this lane's column
+  const bool col_ok = active && col < na_g * G;
+  int a_col = agent[0];
+#pragma unroll
+  for (int j = 1; j < A; ++j)
+    if (jc == j) a_col = agent[j];
+  if (!col_ok) a_col = 0;
+  const int32_t* const pstart = kMap ? p.pstart : nullptr;  // the slot map (see above)
+  U4 qraw[4];
+  {
+    const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
+    for (int c = 0; c < 4; ++c)
+      qraw[c].u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
+  }
+  // Page ids of this wave's sub-range (at most 64 pages: the plan sizes items so that no
+  // wave gets more): lane i holds the ids of page lpa + i, so a page's ids come from a
+  // readlane instead of a memory round trip.  Ids are checked here, once: out-of-pool ids
+  // become -1 (page skipped / zero residual).
+  const int id_base = lpa;
+  int vb = -1;
+  int vr[A];
+  {
+    const int lpi = id_base + lane;
+    const bool in = lpa < lpb && lpi < lpb;
+    vb = in ? p.btab[size_t(agent[0]) * p.max_pages + lpi] : -1;
+    if (vb >= p.num_bpages) vb = -1;
+    for (int j = 0; j < A; ++j) {
+      vr[j] = (in && j < na_g) ? p.rtab[size_t(agent[j]) * p.max_pages + lpi] : -1;
+      if (vr[j] >= p.num_rpages) vr[j] = -1;
+    }
+  }
+  // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
+  // trig-table area (filled only after the permutation below), to be permuted into the MFMA
+  // A-operand order.
+  // (a compile-time trip count, so that all pieces are in flight at once: piece i of this
+  // thread belongs to agent i)
+  constexpr int kBkPieces = kItemAgents * kR * (kD / 8) / kThreads;
+  static_assert(kR * (kD / 8) == kThreads, "one agent's B_k rows are one piece per thread");
+  // (branch-free: slots past the item's agents re-read its last agent's rows into staging
+  // space the permutation never reads)
+  {
+    const int k = tid / 16, piece = tid % 16;
+    uint4 rows[kBkPieces];
+#pragma unroll
+    for (int i = 0; i < kBkPieces; ++i)
+      rows[i] = *reinterpret_cast<const uint4*>(Bk + (size_t(it[4 + min(i, na - 1)]) * kR + k) * n +
+                                                h * kD + 8 * piece);
+#pragma unroll
+    for (int i = 0; i < kBkPieces; ++i)
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(lds + kBkBytes) + (i * kR + k) * kD +
+                                8 * piece) = rows[i];
   }
   const float qscale = p.sm_scale_log2;
 
@@ -258,31 +264,6 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   for (int t = 0; t < 8; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
   f4 accr = f4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-
-  const int pps = (np + n_sub - 1) / n_sub;
-  const int lpa = active ? lp0 + si * pps : 0;
-  const int lpb = active ? min(lp0 + np, lpa + pps) : 0;
-  const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
-
-  // cos/sin(t0 * w_j) for lane j = frequency j, at this wave's first page, with the angle
-  // reduced in fp64; later pages follow by the rotation (cos, sin)(16 w_j).  Over the at
-  // most 64 pages of a wave the recurrence drifts by a few 1e-6 rad at most.  Pages start
-  // at lp * P unless a frozen tail precedes them (the slot map): a page whose start differs
-  // from the recurrence's position re-anchors it by the (at most P - 1 positions) gap.
-  float pc, ps, step_c, step_s;
-  const float omega_f = static_cast<float>(omega);
-  int next_pos = (active && lpa < lpb) ? page_start(pstart, p.max_pages, agent[0], lpa) : 0;
-  {
-    double ang = static_cast<double>(next_pos) * omega;
-    ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
-    double sv, cv;
-    sincos(ang, &sv, &cv);
-    pc = static_cast<float>(cv);
-    ps = static_cast<float>(sv);
-    sincos(kPage * omega, &sv, &cv);
-    step_c = static_cast<float>(cv);
-    step_s = static_cast<float>(sv);
-  }
 
   // Page buffers.  The key-side operands of page lp + 1 (base key tile, residual keys) are
   // loaded while page lp is computed (two register buffers, used alternately); the
@@ -297,25 +278,16 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     U2 vt[8];
     U2 rv[A];
   };
-  // Page ids of this wave's sub-range (at most 64 pages: the plan sizes items so that no
-  // wave gets more): lane i holds the ids of page lpa + i, so a page's ids come from a
-  // readlane instead of a memory round trip.
-  const int id_base = lpa;
-  int vb = -1;
-  int vr[A];
-  // Ids are checked here, once: out-of-pool ids become -1 (page skipped / zero residual).
-  auto fetch_ids = [&]() {
-    const int lpi = id_base + lane;
-    const bool in = lpi < lpb;
-    vb = in ? p.btab[size_t(agent[0]) * p.max_pages + lpi] : -1;
-    if (vb >= p.num_bpages) vb = -1;
-    for (int j = 0; j < A; ++j) {
-      vr[j] = (in && j < na_g) ? p.rtab[size_t(agent[j]) * p.max_pages + lpi] : -1;
-      if (vr[j] >= p.num_rpages) vr[j] = -1;
-    }
-  };
-  if (lpa < lpb) fetch_ids();
   const uint16_t* const zero_res = g_zero_res;
+  // RoPE state of the page loop, set up below: cos/sin of the current page's angle (lane j =
+  // frequency j), the per-page step, the position the recurrence stands at, and w_j
+  float pc = 1.f, ps = 0.f, step_c = 1.f, step_s = 0.f, omega_f = 0.f;
+  int next_pos = 0;
+  // The rotated residual keys are formed in fp16 (packed arithmetic) and scored against an
+  // fp16 copy of q, kept in registers (it is read by every agent's score of every page);
+  // the shared base tile is scored in bf16 against the bf16 q, kept in LDS (this wave's
+  // slot, lane-linear) and read once per page.  Both are filled in the set-up below.
+  H8 qhr[4];
 
   // residual page of agent j at page lp (the zero page where the sequence has none)
   auto res_page = [&](int lp, int j) -> const uint16_t* {
@@ -535,11 +507,88 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     }
   };
 
-  auto run_pages = [&](auto na_c) {
+  // the group's agent count as a compile-time constant for the page routines
+  auto with_na = [&](auto f) __attribute__((always_inline)) {  // na_g is wave-uniform
+    if (na_g >= A) f(std::integral_constant<int, A>{});
+    if constexpr (A > 3) if (na_g == 3) f(std::integral_constant<int, 3>{});
+    if constexpr (A > 2) if (na_g == 2) f(std::integral_constant<int, 2>{});
+    if constexpr (A > 1) if (na_g == 1) f(std::integral_constant<int, 1>{});
+  };
+  // the first page's key-side operands (all A agents' residual rows: a missing one reads
+  // the zero page), before the set-up below
+  KBuf first;
+  if (lpa < lpb) load_k(lpa, first, std::integral_constant<int, A>{});
+
+  // ---- on-chip set-up, while the loads above are in flight ----------------------------
+  // w_j = theta^(-2j/d) = 2^(-(2j/d) log2 theta); lane j keeps w_j in fp64 (j = lane).  Every
+  // thread's trig-table entries are for its own lane's frequency: (c, j) = (w + 4i, lane).
+  const double log2_theta = log2(static_cast<double>(p.rope_theta));
+  const double omega = exp2(-2.0 * lane / kD * log2_theta);
+  omega_f = static_cast<float>(omega);
+  constexpr int kTrigPer = kPage * 64 / kThreads;
+  float tcv[kTrigPer], tsv[kTrigPer];
+  const float rev_f = static_cast<float>(omega * kInvTwoPi);  // w_j in revolutions
+#pragma unroll
+  for (int i = 0; i < kTrigPer; ++i) {
+    // in-page offsets c < 16: the angle c * w_j is at most 15 rad (2.4 revolutions), well
+    // inside the hardware sine/cosine's domain; their error is far below the fp16 the table
+    // is stored in
+    const float x = static_cast<float>(w + kWaves * i) * rev_f;
+    tsv[i] = __builtin_amdgcn_sinf(x);
+    tcv[i] = __builtin_amdgcn_cosf(x);
+  }
+  {
+    const uint16_t* raw = reinterpret_cast<const uint16_t*>(lds + kBkBytes);
+    __syncthreads();  // the B_k rows are staged
+    // (unrolled, with a compile-time trip count, so that its LDS reads are in flight together)
+#pragma unroll
+    for (int i = 0; i < kItemAgents * 8 * 64 / kThreads; ++i) {
+      const int x = tid + kThreads * i;
+      const int jj = x / (8 * 64), T = (x / 64) % 8, l = x % 64;
+      if (jj < na) {
+        const int dim = perm_dim(T, l & 15);
+        const uint16_t* src = raw + jj * kR * kD + dim;
+        const int k0 = 4 * (l >> 4);
+        uint2 v;
+        v.x = uint32_t(src[k0 * kD]) | (uint32_t(src[(k0 + 1) * kD]) << 16);
+        v.y = uint32_t(src[(k0 + 2) * kD]) | (uint32_t(src[(k0 + 3) * kD]) << 16);
+        bkl[x] = v;
+      }
+    }
+    __syncthreads();  // the staging area is free again
+  }
+#pragma unroll
+  for (int i = 0; i < kTrigPer; ++i) {
+    const int c = w + kWaves * i;
+    trig_c[c * kTrigPad + lane] = static_cast<_Float16>(tcv[i] * p.lora_scale);
+    trig_s[c * kTrigPad + lane] = static_cast<_Float16>(tsv[i] * p.lora_scale);
+  }
+  for (int c = 0; c < 4; ++c) {
+    qb_lds[c * 64 + lane] = qraw[c].u;
+    const uint32_t wds[4] = {qraw[c].u.x, qraw[c].u.y, qraw[c].u.z, qraw[c].u.w};
+    for (int e = 0; e < 4; ++e)
+      qhr[c].p[e] = pack_f16x2(__uint_as_float(wds[e] << 16), __uint_as_float(wds[e] & 0xffff0000u));
+  }
+  __syncthreads();
+
+  // cos/sin(t0 * w_j) for lane j = frequency j, at this wave's first page, with the angle
+  // t0 * w_j formed and reduced to [-pi, pi] in fp64; later pages follow by the rotation
+  // (cos, sin)(16 w_j).  Over the at most 64 pages of a wave the recurrence drifts by a few
+  // 1e-6 rad at most.  Pages start at lp * P unless a frozen tail precedes them (the slot
+  // map): a page whose start differs from the recurrence's position re-anchors it by the
+  // (at most P - 1 positions) gap.
+  next_pos = (active && lpa < lpb) ? page_start(pstart, p.max_pages, agent[0], lpa) : 0;
+  {
+    double ang = static_cast<double>(next_pos) * omega;
+    ang = fma(-kTwoPi, rint(ang * kInvTwoPi), ang);
+    sincosf(static_cast<float>(ang), &ps, &pc);
+    sincosf(static_cast<float>(kPage * omega), &step_s, &step_c);
+  }
+
+  auto run_pages = [&](auto na_c) __attribute__((always_inline)) {
     // The prefetch is issued unconditionally (past the end it re-reads the last page, an
     // L2 hit) so that every wait below only covers the older buffer's loads.
-    KBuf buf0, buf1;
-    load_k(lpa, buf0, na_c);
+    KBuf buf0 = first, buf1;
     for (int lp = lpa; lp < lpb; lp += 2) {
       load_k(min(lp + 1, lpb - 1), buf1, na_c);
       compute_page(lp, buf0, na_c);
@@ -548,13 +597,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       compute_page(lp + 1, buf1, na_c);
     }
   };
-  if (lpa < lpb) {
-    // na_g is wave-uniform: one branch selects the straight-line variant
-    if (na_g >= A) run_pages(std::integral_constant<int, A>{});
-    if constexpr (A > 3) if (na_g == 3) run_pages(std::integral_constant<int, 3>{});
-    if constexpr (A > 2) if (na_g == 2) run_pages(std::integral_constant<int, 2>{});
-    if constexpr (A > 1) if (na_g == 1) run_pages(std::integral_constant<int, 1>{});
-  }
+  if (lpa < lpb) with_na(run_pages);
 
   // ---- merge the sub-range partials of each group (LSE rule), write split-K partials ----
   l_run += shfl_xor(l_run, 16);
@@ -581,7 +624,11 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     m_run = M;
   }
   if (!col_ok) return;
-  const size_t row = size_t(it[4 + kItemAgents + j0 + jc]) * Hq + h * G + col % G;
+  int s_col = slot[0];
+#pragma unroll
+  for (int j = 1; j < A; ++j)
+    if (jc == j) s_col = slot[j];
+  const size_t row = size_t(s_col) * Hq + h * G + col % G;
   for (int t = 0; t < 8; ++t)
     *reinterpret_cast<float4*>(p.ws_acc + row * kD + 16 * t + 4 * g4) =
         make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
