@@ -199,12 +199,28 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
 
   // ---- this wave's agents and query columns ------------------------------------------------
+  // the item's agent and slot entries, read with constant indices (a few wide scalar loads
+  // instead of a chain of dependent ones), then picked by wave-uniform selects
+  int ia[kItemAgents], is[kItemAgents];
+#pragma unroll
+  for (int k = 0; k < kItemAgents; ++k) {
+    ia[k] = it[4 + k];
+    is[k] = it[4 + kItemAgents + k];
+  }
   int agent[A], slot[A], rlen[A];  // wave-uniform
 #pragma unroll
   for (int j = 0; j < A; ++j) {
-    agent[j] = (active && j < na_g) ? it[4 + j0 + j] : 0;
-    slot[j] = (active && j < na_g) ? it[4 + kItemAgents + j0 + j] : 0;
-    rlen[j] = (active && j < na_g) ? p.plan[p.off_lens + agent[j]] : 0;
+    int av = ia[0], sv = is[0];
+#pragma unroll
+    for (int k = 1; k < kItemAgents; ++k)
+      if (j0 + j == k) {
+        av = ia[k];
+        sv = is[k];
+      }
+    const bool ok = active && j < na_g;
+    agent[j] = ok ? av : 0;
+    slot[j] = ok ? sv : 0;
+    rlen[j] = ok ? p.plan[p.off_lens + agent[j]] : 0;
   }
   const int jc = col / G;                   // agent (within group) of this lane's column
   const bool col_ok = active && col < na_g * G;
@@ -217,8 +233,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   U4 qraw[4];
   {
     const uint16_t* qrow = q + (size_t(a_col) * Hq + h * G + col % G) * kD;
-    for (int c = 0; c < 4; ++c)
-      qraw[c].u = col_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < 4; ++c)  // (a_col is a valid agent; unused columns are zeroed later)
+      qraw[c].u = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g4);
   }
   // Page ids of this wave's sub-range (at most 64 pages: the plan sizes items so that no
   // wave gets more): lane i holds the ids of page lpa + i, so a page's ids come from a
@@ -251,7 +267,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     uint4 rows[kBkPieces];
 #pragma unroll
     for (int i = 0; i < kBkPieces; ++i)
-      rows[i] = *reinterpret_cast<const uint4*>(Bk + (size_t(it[4 + min(i, na - 1)]) * kR + k) * n +
+      rows[i] = *reinterpret_cast<const uint4*>(Bk + (size_t(i < na ? ia[i] : ia[0]) * kR + k) * n +
                                                 h * kD + 8 * piece);
 #pragma unroll
     for (int i = 0; i < kBkPieces; ++i)
@@ -564,6 +580,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     trig_s[c * kTrigPad + lane] = static_cast<_Float16>(tsv[i] * p.lora_scale);
   }
   for (int c = 0; c < 4; ++c) {
+    if (!col_ok) qraw[c].u = make_uint4(0, 0, 0, 0);  // columns without an agent score zero
     qb_lds[c * 64 + lane] = qraw[c].u;
     const uint32_t wds[4] = {qraw[c].u.x, qraw[c].u.y, qraw[c].u.z, qraw[c].u.w};
     for (int e = 0; e < 4; ++e)
