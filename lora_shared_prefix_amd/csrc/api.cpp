@@ -116,6 +116,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   p.off_lens = pl->blob[forkkv::kHdrOffLens];
   p.off_slot_ptr = pl->blob[forkkv::kHdrOffSlotPtr];
   p.off_slot_list = pl->blob[forkkv::kHdrOffSlotList];
+  p.max_agent_slots = pl->max_agent_slots;
   p.lora_scale = a->lora_scale;
   p.sm_scale_log2 = a->sm_scale * kLog2e;
   p.rope_theta = a->rope_theta;

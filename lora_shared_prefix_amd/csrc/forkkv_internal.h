@@ -84,6 +84,7 @@ struct forkkv_plan {
   size_t workspace_bytes = 0;
   size_t ws_off_acc = 0, ws_off_accr = 0;
   int32_t max_pages_needed = 0;
+  int32_t max_agent_slots = 0;  // the largest number of partials of one agent
   // timing: (kind, begin, end) per timed launch, kind 0 = split, 1 = combine
   bool timing = false;
   struct Timed { int kind; hipEvent_t b, e; };
@@ -125,6 +126,7 @@ struct DecodeParams {
   int32_t n_agents, n_items, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
   int32_t off_items, off_lens, off_slot_ptr, off_slot_list;
+  int32_t max_agent_slots;  // the largest number of split-K partials of one agent
   float lora_scale, sm_scale_log2, rope_theta;
 };
 

@@ -361,9 +361,10 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
 // before any is used, so a row costs about one memory round trip; each thread merges its
 // partials online and the eight groups are merged through LDS with the same rule.
 constexpr int kCombineGroups = 8;
-constexpr int kCombinePer = 12;   // partials per thread per chunk
+// partials per thread per chunk: a template parameter, the smallest of 2, 4, 8, 12 that
+// covers the plan's largest per-agent partial count in one chunk (fewer wasted loads)
 
-template <typename T, int kDG>
+template <typename T, int kDG, int kCombinePer>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
   // kDG = float4 dim groups per thread: the 32 lanes of a group cover 128 dims each
   using E = Elem<T>;
@@ -565,16 +566,29 @@ hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agent
   return hipGetLastError();
 }
 
+template <typename T, int kDG>
+void launch_combine_per(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  const int need = (p.max_agent_slots + kCombineGroups - 1) / kCombineGroups;
+  if (need <= 2)
+    hipLaunchKernelGGL((combine_kernel<T, kDG, 2>), grid, dim3(256), 0, s, p);
+  else if (need <= 4)
+    hipLaunchKernelGGL((combine_kernel<T, kDG, 4>), grid, dim3(256), 0, s, p);
+  else if (need <= 8)
+    hipLaunchKernelGGL((combine_kernel<T, kDG, 8>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, kDG, 12>), grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s) {
   if (p.head_dim > 256 || p.rank > 64) return hipErrorInvalidValue;
   dim3 grid(p.n_agents * p.num_q_heads);
   const bool wide = p.head_dim > 128;
   if (dtype == FORKKV_DTYPE_F32) {
-    if (wide) hipLaunchKernelGGL((combine_kernel<float, 2>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<float, 1>), grid, dim3(256), 0, s, p);
+    if (wide) launch_combine_per<float, 2>(p, grid, s);
+    else launch_combine_per<float, 1>(p, grid, s);
   } else {
-    if (wide) hipLaunchKernelGGL((combine_kernel<uint16_t, 2>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<uint16_t, 1>), grid, dim3(256), 0, s, p);
+    if (wide) launch_combine_per<uint16_t, 2>(p, grid, s);
+    else launch_combine_per<uint16_t, 1>(p, grid, s);
   }
   return hipGetLastError();
 }

@@ -172,7 +172,11 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   const int32_t n_items = static_cast<int32_t>(items.size() / kItemInts);
   // slots of agent a: slot_ptr[a] + (its index), consecutive per agent
   std::vector<int32_t> slot_ptr(n + 1, 0);
-  for (int32_t a = 0; a < n; ++a) slot_ptr[a + 1] = slot_ptr[a] + per_agent[a];
+  int32_t max_agent_slots = 0;
+  for (int32_t a = 0; a < n; ++a) {
+    slot_ptr[a + 1] = slot_ptr[a] + per_agent[a];
+    max_agent_slots = std::max(max_agent_slots, per_agent[a]);
+  }
   for (int32_t i = 0; i < n_items; ++i) {
     int32_t* it = items.data() + size_t(i) * kItemInts;
     for (int32_t j = 0; j < it[2]; ++j) it[4 + kItemAgents + j] += slot_ptr[it[4 + j]];
@@ -190,6 +194,7 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   pl->kernel = kernel;
   pl->group = cap;
   pl->aligned = aligned;
+  pl->max_agent_slots = max_agent_slots;
   pl->max_pages_needed = max_np;
 
   std::vector<int32_t>& b = pl->blob;
