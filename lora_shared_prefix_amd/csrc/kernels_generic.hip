@@ -482,6 +482,128 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
   }
 }
 
+// The same merge for d = 128, r = 16, one wave per output row and no LDS: quarter qd of the
+// wave (16 lanes) takes partials qd, qd + 4, ...; lane l of a quarter holds dims 8l .. 8l+7
+// of acc and entry l of acc_r.  The quarters are merged with cross-lane swaps (same rule),
+// after which every lane holds the whole merged state; quarter qd then applies B_v rows
+// 4qd .. 4qd+3 to its dims and the four products are summed across quarters.  B_v is read
+// before the partials, so one memory round trip covers a row.
+template <typename T> struct Row8;
+template <> struct Row8<uint16_t> {  // 8 bf16 values (16 bytes)
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <> struct Row8<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const float4*>(p);
+    hi = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const float4 v = e < 4 ? lo : hi;
+    const int k = e & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+
+template <typename T, int kPer>
+__global__ void __launch_bounds__(64) combine_row_kernel(DecodeParams p) {
+  constexpr int kDim = 128, kRank = 16;
+  using E = Elem<T>;
+  const int row_out = blockIdx.x, lane = threadIdx.x;
+  const int qd = lane >> 4, l16 = lane & 15;
+  const int Hq = p.num_q_heads;
+  const int a = row_out / Hq, g = row_out % Hq, h = g / p.group;
+  const size_t n = size_t(p.num_kv_heads) * kDim;
+  const int s0 = p.plan[p.off_slot_ptr + a], s1 = p.plan[p.off_slot_ptr + a + 1];
+  const T* bv = static_cast<const T*>(p.Bv) + size_t(a) * kRank * n + size_t(h) * kDim + 8 * l16;
+  Row8<T> bvr[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bvr[k].load(bv + size_t(4 * qd + k) * n);
+
+  float m_t = -INFINITY, l_t = 0.f, ar = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int c0 = s0; c0 < s1; c0 += 4 * kPer) {
+    float mv[kPer], lv[kPer], arv[kPer];
+    float4 a0[kPer], a1[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {  // every load of the chunk before any use
+      const int i = c0 + qd + 4 * u;
+      const size_t row = size_t(min(i, s1 - 1)) * Hq + g;
+      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + row * 2);
+      mv[u] = i < s1 ? ml.x : -INFINITY;
+      lv[u] = ml.y;
+      a0[u] = *reinterpret_cast<const float4*>(p.ws_acc + row * kDim + 8 * l16);
+      a1[u] = *reinterpret_cast<const float4*>(p.ws_acc + row * kDim + 8 * l16 + 4);
+      arv[u] = p.ws_accr[row * kRank + l16];
+    }
+    float mc = m_t;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) mc = fmaxf(mc, mv[u]);
+    if (mc == -INFINITY) continue;  // nothing merged yet (uniform per quarter)
+    const float sc = exp2f(m_t - mc);  // 0 while nothing merged yet
+    l_t *= sc;
+    ar *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    m_t = mc;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const float wgt = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - mc);
+      l_t += wgt * lv[u];
+      ar += wgt * arv[u];
+      acc[0] += wgt * a0[u].x; acc[1] += wgt * a0[u].y;
+      acc[2] += wgt * a0[u].z; acc[3] += wgt * a0[u].w;
+      acc[4] += wgt * a1[u].x; acc[5] += wgt * a1[u].y;
+      acc[6] += wgt * a1[u].z; acc[7] += wgt * a1[u].w;
+    }
+  }
+  // merge the quarters: partner quarter qd ^ 1, then qd ^ 2
+#pragma unroll
+  for (int mask = 16; mask <= 32; mask *= 2) {
+    const float mo = __shfl_xor(m_t, mask, 64);
+    const float lo = __shfl_xor(l_t, mask, 64);
+    const float aro = __shfl_xor(ar, mask, 64);
+    float acco[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acco[e] = __shfl_xor(acc[e], mask, 64);
+    const float M = fmaxf(m_t, mo);
+    const float w1 = m_t == -INFINITY ? 0.f : exp2f(m_t - M);
+    const float w2 = mo == -INFINITY ? 0.f : exp2f(mo - M);
+    l_t = l_t * w1 + lo * w2;
+    ar = ar * w1 + aro * w2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * w1 + acco[e] * w2;
+    m_t = M;
+  }
+  // B_v, once: quarter qd sums ranks 4qd .. 4qd+3 (acc_r entry k sits in lane k)
+  float res[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) res[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float rk = __shfl(ar, 4 * qd + k, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] += rk * bvr[k].get(e);
+  }
+#pragma unroll
+  for (int mask = 16; mask <= 32; mask *= 2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] += __shfl_xor(res[e], mask, 64);
+  if (qd == 0) {
+    T* o = static_cast<T*>(p.out) + (size_t(a) * Hq + g) * kDim + 8 * l16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      E::st(o, e, l_t > 0.f ? (acc[e] + p.lora_scale * res[e]) / l_t : 0.f);
+  }
+}
+
 // Store the chunk rows at their slots (bit-exact copies in the pool layout).  The slot of
 // position t is its page under the slot map and its offset from the page's start; a row
 // whose slot falls outside a page (a malformed start table) is not stored.
@@ -579,9 +701,28 @@ void launch_combine_per(const DecodeParams& p, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((combine_kernel<T, kDG, 12>), grid, dim3(256), 0, s, p);
 }
 
+template <typename T>
+void launch_combine_rows(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  // partials per lane per chunk: the smallest of 2, 4, 8, 16 covering the largest agent's
+  const int need = (p.max_agent_slots + 3) / 4;
+  if (need <= 2)
+    hipLaunchKernelGGL((combine_row_kernel<T, 2>), grid, dim3(64), 0, s, p);
+  else if (need <= 4)
+    hipLaunchKernelGGL((combine_row_kernel<T, 4>), grid, dim3(64), 0, s, p);
+  else if (need <= 8)
+    hipLaunchKernelGGL((combine_row_kernel<T, 8>), grid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((combine_row_kernel<T, 16>), grid, dim3(64), 0, s, p);
+}
+
 hipError_t launch_combine(const DecodeParams& p, int dtype, hipStream_t s) {
   if (p.head_dim > 256 || p.rank > 64) return hipErrorInvalidValue;
   dim3 grid(p.n_agents * p.num_q_heads);
+  if (p.head_dim == 128 && p.rank == 16) {
+    if (dtype == FORKKV_DTYPE_F32) launch_combine_rows<float>(p, grid, s);
+    else launch_combine_rows<uint16_t>(p, grid, s);
+    return hipGetLastError();
+  }
   const bool wide = p.head_dim > 128;
   if (dtype == FORKKV_DTYPE_F32) {
     if (wide) launch_combine_per<float, 2>(p, grid, s);
