@@ -117,15 +117,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
+// max(a, b) for values that are finite or -inf: one median-of-three against the largest
+// finite float (fmaxf would first quiet possible signalling NaNs, one extra instruction per
+// operand, and a bound of +inf is folded back into fmaxf by the compiler)
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, 3.402823466e38f);
+}
 // max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column's rows): two
 // butterfly steps with the cross-row lane swaps (no LDS round trip)
 __device__ __forceinline__ float max_over_rows(float v) {
   const uint32_t x = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t y = __float_as_uint(v);
   const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 union U4 {
@@ -496,7 +502,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     }
     // arguments are <= 8; v_exp_f32 flushes results below 2^-126 to zero, which only drops
     // probabilities negligible next to the reference's 1.0
-    const float m_ref = fmaxf(m_run, -1e30f);  // no -inf - -inf for columns without keys
+    const float m_ref = max2(m_run, -1e30f);  // no -inf - -inf for columns without keys
     float pr[4];
     for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_ref);
     l_run += (pr[0] + pr[1] + pr[2] + pr[3]);
@@ -676,8 +682,10 @@ constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // rows per workgroup
 __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __shared__ __align__(16) uint4 s_k[2][2][4 * 64];   // [buf][page][chunk * 64 + lane]
-  __shared__ __align__(16) uint4 s_v[2][2][4 * 64];   // [buf][page][quarter * 64 + lane]
-  __shared__ __align__(16) uint2 s_rv[2][2][64];      // [buf][page][lane]
+  // value operands in PV-MFMA order: [buf][tile t * 64 + reader lane], the 16 bytes a lane
+  // feeds one K = 32 MFMA (8 bytes of page 0, then 8 of page 1)
+  __shared__ __align__(16) uint4 s_v[2][8 * 64];
+  __shared__ __align__(16) uint4 s_rv[2][64];         // [buf][lane], same page halves
   const int Hkv = p.num_kv_heads, G = p.group, Hq = p.num_q_heads, C = p.chunk_len;
   // the workgroups of one KV head share an XCD (block ids are dealt round robin over the
   // 8 XCDs), so the shared prefix of that head streams through one L2
@@ -851,8 +859,15 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       m2(tvv, v.z, v.w);
       m2(last - 4 * g4, rv.x, rv.y);
     }
-    s_v[buf][pg][tp * 64 + lane] = v;
-    if (tp == 0) s_rv[buf][pg][lane] = rv;
+    // v holds reader lanes 2l and 2l + 1 of tile t = 2 tp + l / 32 (l = lane mod 32): each
+    // 8-byte piece goes to this page's half of that reader's slot
+    {
+      uint2* sv = reinterpret_cast<uint2*>(&s_v[buf][0]);
+      const int slot = (2 * tp + (lane >> 5)) * 64 + ((2 * lane) & 63);
+      sv[2 * slot + pg] = make_uint2(v.x, v.y);
+      sv[2 * (slot + 1) + pg] = make_uint2(v.z, v.w);
+    }
+    if (tp == 0) reinterpret_cast<uint2*>(&s_rv[buf][0])[2 * lane + pg] = rv;
   };
 
   auto compute = [&](int it) {
@@ -897,28 +912,21 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
         accr[rt] *= alpha;
         m_run[rt] = m_new;
       }
-      const float m_ref = fmaxf(m_run[rt], -1e30f);
-      float pr[8], sum = 0.f;
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref));
-        sum += pr[e];
-      }
-      l_run[rt] += sum;
+      const float m_ref = max2(m_run[rt], -1e30f);
+      float pr[8];
+      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref));
+      l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       pb[rt].u = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
     }
-    const uint2* v0 = reinterpret_cast<const uint2*>(&s_v[buf][0][0]);
-    const uint2* v1 = reinterpret_cast<const uint2*>(&s_v[buf][1][0]);
     for (int t = 0; t < 8; ++t) {
-      const uint2 x0 = v0[t * 64 + lane], x1 = v1[t * 64 + lane];
       U4 vop;
-      vop.u = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      vop.u = s_v[buf][t * 64 + lane];
       for (int rt = 0; rt < 2; ++rt) acc[rt][t] = mfma32(vop.b, pb[rt].b, acc[rt][t]);
     }
     {
-      const uint2 x0 = s_rv[buf][0][lane], x1 = s_rv[buf][1][lane];
       U4 rvop;
-      rvop.u = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      rvop.u = s_rv[buf][lane];
       for (int rt = 0; rt < 2; ++rt) accr[rt] = mfma32(rvop.b, pb[rt].b, accr[rt]);
     }
   };
@@ -939,7 +947,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
 
   // ---- epilogue: o = (acc + s * acc_r B_v) / l, B_v applied once ------------------------
   __syncthreads();  // the staging buffers are reused below
-  float* s_accr = reinterpret_cast<float*>(&s_v[0][0][0]);       // [wave][16 ranks][32 rows]
+  float* s_accr = reinterpret_cast<float*>(&s_v[0][0]);          // [wave][16 ranks][32 rows]
   float* s_bv = reinterpret_cast<float*>(&s_k[0][0][0]);         // [16 ranks][128 dims]
   const uint16_t* Bv = static_cast<const uint16_t*>(p.Bv);
   for (int x = tid; x < kR * kD; x += kPfThreads) {
