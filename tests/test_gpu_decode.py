@@ -13,7 +13,7 @@ if not torch.cuda.is_available():
 from lora_shared_prefix_amd import forkkv as fk  # noqa: E402
 from lora_shared_prefix_amd.session import DeviceBatch, workload_geom  # noqa: E402
 from oracle.attention import Geometry, decode_attention  # noqa: E402
-from tests.cases import tiny_case  # noqa: E402
+from tests.cases import encode, tiny_case  # noqa: E402
 from tests.gpu_common import (apply_cows_host, assert_close, errors, gpu_values,  # noqa: E402
                               model_tables, poison_unused, used_rows)
 from workloads import CONFIGS, draw_inputs, pool_ops  # noqa: E402
@@ -282,6 +282,60 @@ def test_graph_replay_matches_eager(kernel):
         same = torch.equal(b.out.view(torch.int16), eager.view(torch.int16))
         print(f"[parity] graph replay {rep} kernel={kernel}: bitwise equal={same}", flush=True)
         assert same
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_many_partials_per_agent(kernel):
+    """One page per split item: every agent's row merges well over 64 split-K partials, so
+    the combine takes several chunks per row (workload 1, heads 0 and 5 checked)."""
+    cfg, x = _workload(1)
+    ops, agents = pool_ops(cfg)
+    b = DeviceBatch(workload_geom(cfg), x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel,
+                    pages_per_item=1)
+    assert b.plan.info["n_slots"] > 64 * len(agents)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    _poison(b.out)
+    out = b.decode(cfg.lora_scale, sm, cfg.rope_theta)
+    torch.cuda.synchronize()
+    _, _, bt, rt, lens = model_tables(cfg.num_bpages, cfg.num_rpages, x["perm_b"], x["perm_r"],
+                                      ops, agents, b.max_pages)
+    ref = decode_attention(Geometry.of(cfg), x["bpool"], x["rpool"], bt, rt, lens, x["q"], x["Bk"],
+                           x["Bv"], cfg.lora_scale, sm, cfg.rope_theta, kv_heads=[0, 5])
+    mask = ~np.isnan(ref[..., 0])
+    g = gpu_values(out, cfg.dtype)
+    assert_close(g[mask], ref[mask], f"{cfg.name} one page per item kernel={kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_empty_agent_bf16_d128(kernel):
+    """An agent with no keys next to short ones at the bf16, d = 128, r = 16 shape: its
+    output is exactly zero, the others match the oracle."""
+    rng = np.random.default_rng(11)
+    Hkv, Hq, d, r, npg = 2, 8, 128, 16, 32
+    geom = dict(num_bpages=npg, num_rpages=npg, num_kv_heads=Hkv, num_q_heads=Hq, head_dim=d,
+                rank=r, dtype="bf16")
+    arrays = dict(bpool=encode(rng.standard_normal((npg, 2, Hkv, 16 * d)), "bf16"),
+                  rpool=encode(rng.standard_normal((npg, 2, 16 * r)), "bf16"),
+                  q=encode(rng.standard_normal((3, Hq, d)), "bf16"),
+                  Bk=encode(0.02 * rng.standard_normal((3, r, Hkv * d)), "bf16"),
+                  Bv=encode(0.02 * rng.standard_normal((3, r, Hkv * d)), "bf16"))
+    ops = [("create", "root", 0), ("append", "root", 37), ("fork", "root", 0, "a0"),
+           ("fork", "root", 16, "a1"), ("append", "a1", 5), ("fork", "root", 37, "a2"),
+           ("append", "a2", 40)]
+    agents = ["a0", "a1", "a2"]
+    b = DeviceBatch(geom, arrays, ops, agents, kernel=kernel)
+    assert b.plan.info["kernel"] == kernel
+    _poison(b.out)
+    out = b.decode(2.0, 1.0 / np.sqrt(d), 5e5)
+    torch.cuda.synchronize()
+    g = gpu_values(out, "bf16")
+    assert np.all(g[0] == 0.0)
+    _, _, bt, rt, lens = model_tables(npg, npg, None, None, ops, agents, b.max_pages)
+    host = apply_cows_host(arrays["bpool"], b.cows, Hkv, d)
+    ref = decode_attention(Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                                    rank=r, dtype="bf16"), host, arrays["rpool"], bt, rt, lens,
+                           arrays["q"], arrays["Bk"], arrays["Bv"], 2.0, 1.0 / np.sqrt(d), 5e5)
+    assert_close(g[1:], ref[1:], f"empty agent bf16 d=128 kernel={kernel}", scale_abs=True)
 
 
 def test_empty_agent_and_errors():
