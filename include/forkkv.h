@@ -61,7 +61,10 @@
  * device memory.  Arguments are validated before any launch; launches are
  * asynchronous on the given stream and the caller keeps every buffer alive until
  * the stream has finished.  A pool or plan handle must not be used from two
- * threads at once.
+ * threads at once.  Device buffers of elements (pools, q, B_k, B_v, new rows,
+ * outputs, workspaces) start on a 16-byte boundary (hipMalloc and PyTorch
+ * allocations do); calls given another address return FORKKV_EINVAL.  Integer
+ * tables (block tables, start tables, positions) need only their natural alignment.
  */
 #ifndef FORKKV_H
 #define FORKKV_H

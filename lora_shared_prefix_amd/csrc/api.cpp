@@ -28,6 +28,11 @@ hipEvent_t get_event(forkkv_plan* pl) {
 
 bool finite(float x) { return std::isfinite(x); }
 
+// Device buffers are read and written with 8- and 16-byte vector accesses.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+template <typename... P>
+bool all_aligned16(const P*... ps) { return (aligned16(ps) && ...); }
+
 }  // namespace
 
 extern "C" {
@@ -77,6 +82,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   if (pl->n_agents == 0) return FORKKV_OK;
   if (!pl->dev) return FORKKV_ESTATE;
   if (!a->q || !a->Bk || !a->Bv || !a->btab || !a->rtab || !a->out) return FORKKV_EINVAL;
+  if (!all_aligned16(a->q, a->Bk, a->Bv, a->out, a->workspace)) return FORKKV_EINVAL;
   if (a->max_pages < pl->max_pages_needed) return FORKKV_EINVAL;
   if (!pl->aligned && !a->pstart) return FORKKV_EINVAL;  // a frozen tail needs the slot map
   if (pl->n_slots > 0 && (!a->workspace || a->workspace_bytes < pl->workspace_bytes))
@@ -175,6 +181,7 @@ int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipSt
   const forkkv_plan* pl = a->decode.plan;
   if (rc != FORKKV_OK || pl->n_agents == 0) return rc;
   if (!a->k_new || !a->v_new || !a->rk_new || !a->rv_new) return FORKKV_EINVAL;
+  if (!all_aligned16(a->k_new, a->v_new, a->rk_new, a->rv_new)) return FORKKV_EINVAL;
   // every agent's captured length counts its new token
   const int32_t off_lens = pl->blob[forkkv::kHdrOffLens];
   for (int32_t i = 0; i < pl->n_agents; ++i)
@@ -219,6 +226,8 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   const bool listed = a->positions != nullptr;
   if (!a->q || !a->k_new || !a->v_new || !a->rk_new || !a->rv_new || !a->Bk || !a->Bv ||
       !a->btab || !a->rtab || !a->out)
+    return FORKKV_EINVAL;
+  if (!all_aligned16(a->q, a->k_new, a->v_new, a->rk_new, a->rv_new, a->Bk, a->Bv, a->out))
     return FORKKV_EINVAL;
   if (listed ? !a->positions_host : (!a->start_pos || !a->start_pos_host)) return FORKKV_EINVAL;
   if (a->max_pages < 1) return FORKKV_EINVAL;
@@ -295,6 +304,7 @@ int forkkv_write_rows(const forkkv_write_args* a, hipStream_t stream) {
   if (!a->btab || (res && !a->rtab) || !a->positions || !a->positions_host || !a->k_new ||
       !a->v_new)
     return FORKKV_EINVAL;
+  if (!all_aligned16(a->k_new, a->v_new, a->rk_new, a->rv_new)) return FORKKV_EINVAL;
   const int64_t cap = int64_t(a->max_pages) * kPage;
   for (int32_t i = 0; i < a->n_seqs; ++i) {
     const int32_t* pos = a->positions_host + size_t(i) * a->n_rows;

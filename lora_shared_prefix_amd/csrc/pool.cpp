@@ -96,6 +96,9 @@ int forkkv_pool_create(const forkkv_pool_desc* d, void* bcache, void* rcache,
   if (!valid_order(d->bpage_order, d->num_bpages) || !valid_order(d->rpage_order, d->num_rpages))
     return FORKKV_EINVAL;
   if ((bcache == nullptr) != (rcache == nullptr)) return FORKKV_EINVAL;
+  // (the kernels read pool tiles with 16-byte vector loads)
+  if ((reinterpret_cast<uintptr_t>(bcache) | reinterpret_cast<uintptr_t>(rcache)) & 15u)
+    return FORKKV_EINVAL;
   forkkv_pool* p = new (std::nothrow) forkkv_pool();
   if (!p) return FORKKV_ENOMEM;
   p->desc = *d;

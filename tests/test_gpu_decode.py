@@ -363,6 +363,16 @@ def test_empty_agent_and_errors():
         fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab[:, :0].contiguous(),
                                 b.rtab, b.out, b.workspace, 1.0, 0.3, 1e4)
     assert e.value.code == fk.EINVAL
+    # device buffers off a 16-byte boundary
+    qm = torch.empty(b.q.numel() + 1, dtype=b.q.dtype, device="cuda")[1:].view_as(b.q)
+    with pytest.raises(fk.ForkKVError) as e:
+        fk.residual_attn_decode(b.pool, b.plan, qm, b.Bk, b.Bv, b.btab, b.rtab, b.out,
+                                b.workspace, 1.0, 0.3, 1e4)
+    assert e.value.code == fk.EINVAL
+    bm = torch.empty(b.bcache.numel() + 1, dtype=b.bcache.dtype, device="cuda")[1:]
+    with pytest.raises(fk.ForkKVError) as e:
+        fk.Pool(16, 16, 1, 16, 4, "f32", bcache=bm, rcache=b.rcache)
+    assert e.value.code == fk.EINVAL
     # plan not uploaded
     p2 = fk.Plan(b.pool, b.handles, 2)
     with pytest.raises(fk.ForkKVError) as e:
