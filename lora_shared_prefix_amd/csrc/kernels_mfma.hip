@@ -872,17 +872,21 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
 
   auto compute = [&](int it) {
     const int buf = it & 1;
-    f4 sc4[2][2];  // [page][row tile]
-    for (int pgi = 0; pgi < 2; ++pgi) {
-      U4 kop[4];
-      for (int c = 0; c < 4; ++c) kop[c].u = s_k[buf][pgi][c * 64 + lane];
-      for (int rt = 0; rt < 2; ++rt) {
-        f4 sv = f4{0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < 4; ++c) sv = mfma32(kop[c].b, qv[rt][c], sv);
-        sc4[pgi][rt] = sv;
-      }
+    // Row tile 0's scores first, then row tile 1's; then per row tile its softmax and its
+    // PV products, so that the vector work of one row tile is issued while the matrix
+    // cores run the other's products.
+    f4 sc4[2][2];  // [row tile][page]
+    {
+      U4 kop[2][4];
+      for (int pgi = 0; pgi < 2; ++pgi)
+        for (int c = 0; c < 4; ++c) kop[pgi][c].u = s_k[buf][pgi][c * 64 + lane];
+      for (int rt = 0; rt < 2; ++rt)
+        for (int pgi = 0; pgi < 2; ++pgi) {
+          f4 sv = f4{0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < 4; ++c) sv = mfma32(kop[pgi][c].b, qv[rt][c], sv);
+          sc4[rt][pgi] = sv;
+        }
     }
-    U4 pb[2];  // P^T operands, K = 32 keys: elements 0..3 page 0, 4..7 page 1
     // Both pages exist and lie entirely before the block's first query position (every key
     // precedes every query):
     // no mask at all.  Rows past the chunk have zero q and are never written, so they need
@@ -893,12 +897,12 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       float sc[8], pmax = -INFINITY;
       if (unmasked) {
         for (int pgi = 0; pgi < 2; ++pgi)
-          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[pgi][rt][i];
+          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[rt][pgi][i];
       } else {
         for (int pgi = 0; pgi < 2; ++pgi) {
           const int lp = 2 * it + pgi;
           const int lim = lp < lp_end ? qpos[rt] - lp * kPage - 4 * g4 : -1;  // keys i <= lim
-          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[pgi][rt][i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[rt][pgi][i] : -INFINITY;
         }
       }
       for (int e = 0; e < 8; ++e) pmax = fmaxf(pmax, sc[e]);
@@ -916,18 +920,17 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       float pr[8];
       for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref));
       l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      pb[rt].u = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
-    }
-    for (int t = 0; t < 8; ++t) {
-      U4 vop;
-      vop.u = s_v[buf][t * 64 + lane];
-      for (int rt = 0; rt < 2; ++rt) acc[rt][t] = mfma32(vop.b, pb[rt].b, acc[rt][t]);
-    }
-    {
+      U4 pb;  // P^T operand, K = 32 keys: elements 0..3 page 0, 4..7 page 1
+      pb.u = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+      for (int t = 0; t < 8; ++t) {
+        U4 vop;
+        vop.u = s_v[buf][t * 64 + lane];
+        acc[rt][t] = mfma32(vop.b, pb.b, acc[rt][t]);
+      }
       U4 rvop;
       rvop.u = s_rv[buf][lane];
-      for (int rt = 0; rt < 2; ++rt) accr[rt] = mfma32(rvop.b, pb[rt].b, accr[rt]);
+      accr[rt] = mfma32(rvop.b, pb.b, accr[rt]);
     }
   };
 
