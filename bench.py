@@ -135,10 +135,45 @@ def bench_prefill(steps, warmup):
     fl = prefill_flops(cfg)
     tflops = fl / (ms * 1e-3) / 1e12
     log(f"prefill {ms:.3f} ms per call, {tflops:.1f} TFLOP/s")
-    return {"workload": cfg.name, "calls": n, "ms_per_call": ms,
-            "chunk_tokens_per_s": cfg.n_agents * cfg.chunk_len / (ms * 1e-3),
-            "dense_flops_per_call": fl, "tflops": tflops,
-            "mfma_frac": tflops / MFMA_PEAK_BF16_TFLOPS, "peak_tflops": MFMA_PEAK_BF16_TFLOPS}
+    res = {"workload": cfg.name, "calls": n, "ms_per_call": ms,
+           "chunk_tokens_per_s": cfg.n_agents * cfg.chunk_len / (ms * 1e-3),
+           "dense_flops_per_call": fl, "tflops": tflops,
+           "mfma_frac": tflops / MFMA_PEAK_BF16_TFLOPS, "peak_tflops": MFMA_PEAK_BF16_TFLOPS}
+
+    # Hole refill with a position list, same shape: every agent refills 256 rows inside its
+    # private rows (positions prefix + 128 .. prefix + 383) and appends a 256-row tail, in
+    # one call of the same 512 rows.
+    from lora_shared_prefix_amd import forkkv as fk
+    half = cfg.chunk_len // 2
+    lens = [b.pool.length(h) for h in b.handles]
+    for h in b.handles:
+        b.pool.append(h, half, want_slots=False)
+    b.refresh_tables()
+    h0 = cfg.prefix_len + cfg.chunk_len // 4
+    pos = [list(range(h0, h0 + half)) + list(range(L, L + half)) for L in lens]
+    pos_dev = torch.tensor(pos, dtype=torch.int32, device="cuda")
+
+    def refill():
+        fk.residual_attn_prefill(b.pool, chunk["q"], chunk["k_new"], chunk["v_new"],
+                                 chunk["rk_new"], chunk["rv_new"], b.Bk, b.Bv, b.btab, b.rtab,
+                                 None, None, out, cfg.lora_scale, sm, cfg.rope_theta,
+                                 positions=pos_dev, positions_host=pos)
+    refill()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(n):
+        refill()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_r = t0.elapsed_time(t1) / n
+    per_key = 2 * cfg.head_dim * 2 + 2 * cfg.rank
+    fl_r = cfg.num_q_heads * per_key * sum(p + 1 for row in pos for p in row)
+    log(f"hole-refill prefill {ms_r:.3f} ms per call, {fl_r / (ms_r * 1e-3) / 1e12:.1f} TFLOP/s")
+    res["hole_refill"] = {
+        "rows_per_agent": f"{half} refilled at {h0}..{h0 + half - 1} + {half} appended",
+        "ms_per_call": ms_r, "dense_flops_per_call": fl_r,
+        "tflops": fl_r / (ms_r * 1e-3) / 1e12}
+    return res
 
 
 def bench_decode(idx, steps, warmup, kernel, pages_per_item, copies_arg):
@@ -268,6 +303,122 @@ def bench_decode(idx, steps, warmup, kernel, pages_per_item, copies_arg):
     }
 
 
+def _graph_ms(fn, steps):
+    """Per-call ms of `steps` calls of fn captured as one HIP graph (after one untimed replay)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def _split_us(plan, fn, steps):
+    """Average split-kernel and combine launch durations (library events), in us."""
+    import torch
+    plan.timing()
+    plan.set_timing(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    plan.set_timing(False)
+    s, c, n = plan.timing()
+    return s / max(n, 1) * 1e3, c / max(n, 1) * 1e3
+
+
+def bench_next_rows(cfg, x, ops, agents, steps):
+    """Decode with append, decode over a frozen tail (the slot map), and eviction / refill /
+    base-only row write, at the decode workload's shape with ONE input copy: its 185 MB
+    working set fits the 256 MB Infinity Cache, so every figure stands beside plain decode
+    timed the same way on the same box, not beside the rotated-copy headline."""
+    import numpy as np
+    import torch
+
+    from lora_shared_prefix_amd import forkkv as fk
+    from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
+
+    geom = workload_geom(cfg)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    N, Hkv, d, r = cfg.n_agents, cfg.num_kv_heads, cfg.head_dim, cfg.rank
+    out = {}
+
+    # plain decode, the reference for this section
+    ab = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"])
+    dec = lambda: ab.decode(cfg.lora_scale, sm, cfg.rope_theta)
+    plain_ms = _graph_ms(dec, steps)
+    plain_split, _ = _split_us(ab.plan, dec, steps)
+    out["plain_decode"] = {"ms_per_call": plain_ms, "split_avg_us": plain_split}
+
+    # decode with append: every agent's new token is stored, then attended (one call)
+    pb = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], plan=False)
+    pb.reserve_chunk(1)
+    pb.make_plan()
+    bf = torch.bfloat16
+    rows = {"k_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
+            "v_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
+            "rk_new": torch.randn(N, r, dtype=bf, device="cuda"),
+            "rv_new": torch.randn(N, r, dtype=bf, device="cuda")}
+    app = lambda: pb.decode_append(rows, cfg.lora_scale, sm, cfg.rope_theta)
+    app_ms = _graph_ms(app, steps)
+    out["decode_append"] = {"ms_per_call": app_ms, "agent_tokens_per_s": N / (app_ms * 1e-3),
+                            "over_plain_decode_us": (app_ms - plain_ms) * 1e3}
+    del pb
+
+    # decode over a frozen tail: the trunk ends 7 rows into a page that every agent shares
+    # read-only (fork mode freeze); the agents' own rows start on fresh pages
+    L0 = cfg.prefix_len + 7
+    fops = [("create", "root", 0), ("append", "root", L0)]
+    for a in agents:
+        fops += [("fork", "root", L0, a, fk.FORK_FREEZE, 0), ("append", a, cfg.suffix_len)]
+    fb = DeviceBatch(geom, x, fops, agents, x["perm_b"], x["perm_r"])
+    assert fb.pstart is not None
+    fdec = lambda: fb.decode(cfg.lora_scale, sm, cfg.rope_theta)
+    f_ms = _graph_ms(fdec, steps)
+    f_split, _ = _split_us(fb.plan, fdec, steps)
+    f_bytes, _ = algorithmic_bytes(cfg, L0 + N * cfg.suffix_len)
+    out["frozen_tail_decode"] = {
+        "ms_per_call": f_ms, "split_avg_us": f_split,
+        "split_hbm_gbs": f_bytes / (f_split * 1e-6) / 1e9,
+        "trunk": f"{L0} tokens, the last 7 in a shared read-only page"}
+    del fb
+
+    # decoupled eviction: 64 shared trunk pages leave every holder, fresh pages are mapped
+    # back into the agents (host bookkeeping), and the recomputed base rows are stored
+    # through one holder (base pool only; the residual pages never left)
+    lp0, lp1 = 1000, 1064
+    pages = [int(v) for v in ab.btab_host[0][lp0:lp1]]
+    t = time.perf_counter()
+    ab.pool.evict_base(pages)
+    ab.pool.refill_base(ab.handles, lp0, lp1)
+    host_us = (time.perf_counter() - t) * 1e6
+    ab.refresh_tables()
+    n_rows = (lp1 - lp0) * 16
+    wpos = [list(range(lp0 * 16, lp1 * 16))]
+    wpos_dev = torch.tensor(wpos, dtype=torch.int32, device="cuda")
+    kw = torch.randn(1, n_rows, Hkv, d, dtype=bf, device="cuda")
+    vw = torch.randn(1, n_rows, Hkv, d, dtype=bf, device="cuda")
+    btab0 = ab.btab[:1].contiguous()
+    wr = lambda: fk.write_rows(ab.pool, btab0, None, wpos_dev, wpos, kw, vw)
+    w_ms = _graph_ms(wr, steps)
+    w_bytes = n_rows * Hkv * d * 2 * cfg.elem_bytes
+    out["evict_refill"] = {"pages": lp1 - lp0, "holders": len(ab.handles) + 1,
+                           "evict_refill_host_us": host_us, "write_rows_us": w_ms * 1e3,
+                           "write_rows_bytes": w_bytes,
+                           "write_rows_gbs": 2 * w_bytes / (w_ms * 1e-3) / 1e9}
+    log("next rows: " + json.dumps(out))
+    return out
+
+
 def copy_bandwidth_gbs():
     """Read + write bytes per second of a plain 1 GiB device-to-device copy (practical ceiling)."""
     import torch
@@ -302,6 +453,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=2, help="agents timed on the oracle (0 = skip)")
     ap.add_argument("--no-more-workloads", action="store_true",
                     help="skip the extra decode figures of workloads 1 and 3")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip decode-with-append, frozen-tail decode and eviction/refill timing")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing chunked prefill on the Qwen3-8B 131072-prefix workload")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -374,6 +527,9 @@ def main():
                 "algorithmic_bytes_per_launch": o["roofline"]["algorithmic_bytes_per_launch"],
                 "combine_avg_us": o["combine_avg_us"], "config": o["config"]}
         result["other_decode_workloads"] = others
+    if not args.no_next and args.workload == 2:
+        torch.cuda.empty_cache()
+        result["next_rows"] = bench_next_rows(cfg, x, ops, agents, max(10, args.steps // 2))
     if not args.no_prefill:
         torch.cuda.empty_cache()  # the decode inputs are freed by now
         result["prefill"] = bench_prefill(args.steps, args.warmup)

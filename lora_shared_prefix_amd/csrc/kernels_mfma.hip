@@ -259,6 +259,19 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       if (vr[j] >= p.num_rpages) vr[j] = -1;
     }
   }
+  // With the slot map, lane i also holds page lpa + i's start and the position its rows end
+  // at, from the first agent's start table: a base page that several agents map holds the
+  // same rows for each of them (a shared page is full or a frozen tail), so only an agent's
+  // own length can cut it shorter.
+  int vst = 0, vend = 0;
+  if constexpr (kMap) {
+    const int lpi = id_base + lane;
+    const bool in = lpa < lpb && lpi < lpb;
+    const int32_t* row = p.pstart + size_t(agent[0]) * p.max_pages;
+    vst = in ? row[lpi] : 0;
+    const int nx = (in && lpi + 1 < p.max_pages) ? row[lpi + 1] : -1;
+    vend = nx >= 0 ? nx : rlen[0];
+  }
   // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
   // trig-table area (filled only after the permutation below), to be permuted into the MFMA
   // A-operand order.
@@ -349,14 +362,19 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     // rows of this page held by each agent (the page's start is common to them all)
     int vrows = 0, minrows = kPage;
     int prow[NA];
+    int pos0 = 0, pend = 0;
+    if constexpr (kMap) {
+      pos0 = __builtin_amdgcn_readlane(vst, lp - id_base);
+      pend = __builtin_amdgcn_readlane(vend, lp - id_base);
+    }
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      prow[j] = page_rows(pstart, p.max_pages, agent[j], lp, rlen[j]);
+      prow[j] = kMap ? min(min(rlen[j], pend) - pos0, kPage)
+                     : page_rows(nullptr, p.max_pages, agent[j], lp, rlen[j]);
       vrows = max(vrows, prow[j]);
       minrows = min(minrows, prow[j]);
     }
     if constexpr (kMap) {
-      const int pos0 = page_start(pstart, p.max_pages, agent[0], lp);
       if (pos0 != next_pos) {  // wave-uniform: re-anchor the rotation at this page's start
         float sv, cv;
         sincosf(static_cast<float>(pos0 - next_pos) * omega_f, &sv, &cv);
