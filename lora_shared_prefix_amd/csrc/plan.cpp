@@ -79,6 +79,17 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
     // order groups by their first agent for determinism
     std::vector<std::vector<int32_t>> groups;
     for (auto& kv : by_page) groups.push_back(kv.second);
+    // Under a slot map the kernels take a shared page's start and row count from one of its
+    // holders: every holder must see the page at the same start with the same last row (the
+    // pool only ever shares full pages and frozen tails, so this always holds).
+    if (!aligned)
+      for (const auto& ag : groups) {
+        const forkkv::Seq& s0 = *S[ag[0]];
+        for (int32_t a : ag) {
+          const forkkv::Seq& s = *S[a];
+          if (s.starts[lp] != s0.starts[lp] || s.rows(lp) != s0.rows(lp)) return FORKKV_ESTATE;
+        }
+      }
     std::sort(groups.begin(), groups.end(),
               [](const std::vector<int32_t>& x, const std::vector<int32_t>& y) { return x[0] < y[0]; });
     for (auto& ag : groups) {
