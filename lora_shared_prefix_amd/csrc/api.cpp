@@ -122,6 +122,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   p.off_lens = pl->blob[forkkv::kHdrOffLens];
   p.off_slot_ptr = pl->blob[forkkv::kHdrOffSlotPtr];
   p.off_slot_list = pl->blob[forkkv::kHdrOffSlotList];
+  p.off_append = pl->blob[forkkv::kHdrOffAppend];
   p.max_agent_slots = pl->max_agent_slots;
   p.lora_scale = a->lora_scale;
   p.sm_scale_log2 = a->sm_scale * kLog2e;
@@ -211,7 +212,15 @@ int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipSt
   w.num_bpages = g.num_bpages;
   w.num_rpages = g.num_rpages;
   (void)hipGetLastError();
-  if (forkkv::launch_prefill_write(w, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
+  if (pl->kernel == FORKKV_KERNEL_MFMA) {
+    // the split kernel stores the new rows itself, ahead of the pages that hold them
+    p.k_new = a->k_new;
+    p.v_new = a->v_new;
+    p.rk_new = a->rk_new;
+    p.rv_new = a->rv_new;
+  } else if (forkkv::launch_prefill_write(w, g.dtype, stream) != hipSuccess) {
+    return FORKKV_EHIP;
+  }
   return launch_decode(const_cast<forkkv_plan*>(pl), p, g.dtype, stream);
 }
 

@@ -16,7 +16,8 @@ constexpr int kPage = 16;
 
 // One decode work item: a run of logical pages that every listed agent maps to the same
 // physical base pages, processed by one workgroup per KV head.
-//   [0] first logical page   [1] number of pages   [2] number of agents   [3] unused
+//   [0] first logical page   [1] number of pages   [2] number of agents
+//   [3] bit j set: agent j's last row lies in this item's pages (decode with append)
 //   [4 .. 4+kItemAgents) agent indices
 //   [4+kItemAgents .. 4+2*kItemAgents) partial slot of each agent; the slots of one agent
 //   are consecutive (slot_ptr[a] .. slot_ptr[a+1]), so the combine needs no slot list
@@ -27,6 +28,7 @@ constexpr int kItemInts = 4 + 2 * kItemAgents;
 enum : int {
   kHdrMagic = 0, kHdrAgents, kHdrItems, kHdrSlots, kHdrItemInts, kHdrQHeads,
   kHdrOffItems, kHdrOffLens, kHdrOffSlotPtr, kHdrOffSlotList, kHdrKernel, kHdrGroup,
+  kHdrOffAppend,  // per agent: base slot, residual slot of its last row (page * P + row)
   kHdrWords = 16
 };
 constexpr int32_t kPlanMagic = 0x464b5631;  // "FKV1"
@@ -123,9 +125,15 @@ struct DecodeParams {
   float* ws_acc;            // [slots][Hq][d]
   float* ws_accr;           // [slots][Hq][r]
   void* out;
+  // decode with append (MFMA kernel): each agent's new rows, stored by the workgroups of the
+  // item holding its last row before any page is read; null for a plain decode
+  const void* k_new;   // [N][Hkv][d]
+  const void* v_new;   // [N][Hkv][d]
+  const void* rk_new;  // [N][r]
+  const void* rv_new;  // [N][r]
   int32_t n_agents, n_items, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
-  int32_t off_items, off_lens, off_slot_ptr, off_slot_list;
+  int32_t off_items, off_lens, off_slot_ptr, off_slot_list, off_append;
   int32_t max_agent_slots;  // the largest number of split-K partials of one agent
   float lora_scale, sm_scale_log2, rope_theta;
 };

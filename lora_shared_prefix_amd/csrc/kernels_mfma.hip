@@ -554,6 +554,44 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     if constexpr (A > 2) if (na_g == 2) f(std::integral_constant<int, 2>{});
     if constexpr (A > 1) if (na_g == 1) f(std::integral_constant<int, 1>{});
   };
+  // Decode with append: the new token of every item agent whose last row lies in this item's
+  // pages is stored first -- this KV head's key and value rows, and the residual rows (the
+  // same bytes from every head's workgroup) -- and the workgroup waits for the stores before
+  // any page is read.  Only this item's workgroups read those pages: a row just appended sits
+  // in a page private to its agent.
+  static_assert(kThreads == 2 * kD, "one thread per key and per value element of a row");
+  if (p.k_new != nullptr) {  // uniform over the grid
+    const int mask = it[3];
+    uint16_t* const bw = const_cast<uint16_t*>(bcache);
+    uint16_t* const rw = const_cast<uint16_t*>(rcache);
+#pragma unroll
+    for (int j = 0; j < kItemAgents; ++j) {
+      if (!((mask >> j) & 1)) continue;  // uniform
+      const int a = ia[j];
+      const int bs = p.plan[p.off_append + 2 * a], rs = p.plan[p.off_append + 2 * a + 1];
+      const int bpg = bs / kPage, rpg = rs / kPage;
+      if (bs < 0 || rs < 0 || bpg >= p.num_bpages || rpg >= p.num_rpages) continue;
+      const int brow = bs % kPage, rrow = rs % kPage;
+      if (tid < kD) {
+        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t(a) * Hkv + h) * kD;
+        bw[(size_t(bpg) * 2 * Hkv + h) * tile + TileOrder::key(brow, tid)] = kn[tid];
+      } else {
+        const int x = tid - kD;
+        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (size_t(a) * Hkv + h) * kD;
+        bw[(size_t(bpg) * 2 * Hkv + Hkv + h) * tile + TileOrder::value(brow, x)] = vn[x];
+      }
+      if (tid < kR) {
+        const uint16_t* rkn = static_cast<const uint16_t*>(p.rk_new) + size_t(a) * kR;
+        rw[size_t(rpg) * 2 * kPage * kR + TileOrder::res_key(rrow, tid)] = rkn[tid];
+      } else if (tid < 2 * kR) {
+        const int k = tid - kR;
+        const uint16_t* rvn = static_cast<const uint16_t*>(p.rv_new) + size_t(a) * kR;
+        rw[size_t(rpg) * 2 * kPage * kR + kPage * kR + TileOrder::res_value(rrow, k, kR)] = rvn[k];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores have completed
+    __syncthreads();
+  }
   // the first page's key-side operands (all A agents' residual rows: a missing one reads
   // the zero page), before the set-up below
   KBuf first;

@@ -174,6 +174,8 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
           const int32_t a = r.agents[a0 + j];
           it[4 + j] = a;
           it[4 + kItemAgents + j] = per_agent[a]++;  // index within the agent, for now
+          const int32_t last = static_cast<int32_t>(S[a]->bpages.size()) - 1;
+          if (S[a]->len > 0 && last >= lp && last < lp + np) it[3] |= 1 << j;
         }
         n_slots += na;
         items.insert(items.end(), it, it + kItemInts);
@@ -225,6 +227,20 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   b[forkkv::kHdrOffSlotPtr] = static_cast<int32_t>(b.size());
   b.insert(b.end(), slot_ptr.begin(), slot_ptr.end());
   b[forkkv::kHdrOffSlotList] = static_cast<int32_t>(b.size());  // empty: slots are ranges
+  // slots of each agent's last row: where decode with append stores the new token
+  b[forkkv::kHdrOffAppend] = static_cast<int32_t>(b.size());
+  for (int32_t a = 0; a < n; ++a) {
+    const forkkv::Seq& sq = *S[a];
+    int32_t bs = -1, rs = -1;
+    if (sq.len > 0) {
+      const size_t last = sq.bpages.size() - 1;
+      const int32_t row = sq.len - 1 - sq.starts[last];
+      bs = sq.bpages[last] * forkkv::kPage + row;
+      rs = sq.rpages[last] * forkkv::kPage + row;
+    }
+    b.push_back(bs);
+    b.push_back(rs);
+  }
 
   const size_t rows = size_t(n_slots) * num_q_heads;
   pl->ws_off_acc = align256(rows * 2 * sizeof(float));

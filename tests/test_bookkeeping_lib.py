@@ -179,6 +179,23 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
                 covered[(a, lpg)] = i
     want = {(a, lpg) for a in range(n_agents) for lpg in range(-(-lens[a] // 16))}
     assert set(covered) == want
+    # decode with append: item bit j marks agent j's last page; the append section holds the
+    # base and residual slot (page * 16 + row) of every agent's last row
+    off_app = blob[12]
+    for i in range(n_items):
+        it = blob[off_items + i * ITEM_INTS: off_items + (i + 1) * ITEM_INTS]
+        lp0, npg, na = it[:3]
+        for j, a in enumerate(it[4:4 + na]):
+            last = -(-lens[a] // 16) - 1
+            assert bool((it[3] >> j) & 1) == (lens[a] > 0 and lp0 <= last < lp0 + npg)
+        assert it[3] >> na == 0
+    for a in range(n_agents):
+        bs, rs = blob[off_app + 2 * a], blob[off_app + 2 * a + 1]
+        if lens[a] == 0:
+            assert bs == rs == -1
+        else:
+            t = lens[a] - 1
+            assert bs == bt[a][t // 16] * 16 + t % 16 and rs == rt[a][t // 16] * 16 + t % 16
     # the partial slots of each agent are exactly the range slot_ptr[a] .. slot_ptr[a+1]
     assert blob[off_ptr] == 0 and off_list == off_ptr + n_agents + 1
     for a in range(n_agents):
