@@ -312,8 +312,11 @@ typedef struct {
 } forkkv_decode_append_args;
 
 /* Same errors as forkkv_residual_attn_decode; FORKKV_EINVAL also for a null row pointer or
- * a plan length below 1.  The new rows land at position len - 1 of each agent, in the
- * pages the tables name for it. */
+ * a plan length below 1.  The new rows land at position len - 1 of each agent, in the slot
+ * the pool holds for it when the plan is built (the tables passed are the ones exported for
+ * that plan).  A sequence appears at most once in the batch.  On the MFMA kernel the split
+ * kernel stores the rows itself, ahead of the pages that hold them; the generic kernel runs
+ * a row-write kernel first. */
 int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* args,
                                        hipStream_t stream);
 
