@@ -79,6 +79,7 @@ def cpu_baseline(cfg, x, ops, agents, n_sample):
     pm = PoolModel(cfg.num_bpages, cfg.num_rpages, 16, x["perm_b"], x["perm_r"])
     names = pm.replay(ops)
     bt, rt, lens = pm.tables([names[a] for a in agents], -(-cfg.seq_len // 16))
+    n_sample = min(n_sample, cfg.n_agents)
     sample = list(range(n_sample))
     t0 = time.perf_counter()
     decode_attention(Geometry.of(cfg), x["bpool"], x["rpool"], np.array(bt), np.array(rt), lens,
@@ -450,7 +451,8 @@ def main():
     ap.add_argument("--kernel", choices=["auto", "generic", "mfma"], default="auto")
     ap.add_argument("--pages-per-item", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--cpu-sample", type=int, default=2, help="agents timed on the oracle (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=8,
+                    help="agents timed on the oracle (0 = skip; 8 = the whole batch, about 10 s)")
     ap.add_argument("--no-more-workloads", action="store_true",
                     help="skip the extra decode figures of workloads 1 and 3")
     ap.add_argument("--no-next", action="store_true",
