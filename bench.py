@@ -9,6 +9,10 @@ from the K calls captured as one HIP graph and replayed (no host launch cost ins
 split kernel's launch duration (for the roofline figure) from a further pass of K eager
 calls with per-launch events recorded by the library on the launch stream.
 
+Also reported (skippable): the other two decode workloads, decode with append, decode over
+a frozen tail, eviction / refill / base-only row write (`next_rows`), chunked prefill on the
+Qwen3-8B workload with a hole-refill variant, and the fp64 oracle timed on the host.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
