@@ -125,6 +125,75 @@ def test_decode_append_tiny(seed, dtype, kernel, d, r, Hq, Hkv):
     assert_close(g, ref, f"append seed={seed} {dtype} kernel={kernel}", scale_abs=True)
 
 
+STEP_CASES = [(fk.KERNEL_MFMA, False), (fk.KERNEL_MFMA, True), (fk.KERNEL_GENERIC, True)]
+
+
+@pytest.mark.parametrize("kernel,freeze", STEP_CASES)
+def test_decode_append_steps(kernel, freeze):
+    """A serving loop: 20 decode-with-append steps in a row, so the new tokens cross page
+    boundaries and open fresh pages; with ``freeze`` the agents share the root's frozen
+    unaligned tail (the slot map is in use).  Every step's output, and the pools at the end,
+    are checked against the oracle replaying the same writes."""
+    from oracle.attention import apply_rows_write
+    rng = np.random.default_rng(4321 + int(freeze))
+    dtype, d, r, Hq, Hkv = "bf16", 128, 16, 8, 2
+    n_agents, num_pages, L0, steps = 3, 64, 37, 20
+    ops = [("create", "root", 0), ("append", "root", L0)]
+    points = [L0, 32, 21]
+    for j in range(n_agents):
+        ops.append(("fork", "root", L0, f"a{j}", fk.FORK_FREEZE, 0) if freeze
+                   else ("fork", "root", points[j], f"a{j}"))
+    agents = [f"a{j}" for j in range(n_agents)]
+    perm_b = rng.permutation(num_pages).astype(np.int32)
+    perm_r = rng.permutation(num_pages).astype(np.int32)
+    bpool = encode(rng.standard_normal((num_pages, 2, Hkv, 16 * d)), dtype)
+    rpool = encode(rng.standard_normal((num_pages, 2, 16 * r)), dtype)
+    Bk = encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype)
+    Bv = encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype)
+    q0 = encode(rng.standard_normal((n_agents, Hq, d)), dtype)
+    geom = dict(num_bpages=num_pages, num_rpages=num_pages, num_kv_heads=Hkv, num_q_heads=Hq,
+                head_dim=d, rank=r, dtype=dtype)
+    b = DeviceBatch(geom, dict(bpool=bpool, rpool=rpool, q=q0, Bk=Bk, Bv=Bv), ops, agents,
+                    perm_b, perm_r, plan=False)
+    geo = Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, rank=r,
+                   dtype=dtype)
+    host_b, host_r = apply_cows_host(bpool, b.cows, Hkv, d), rpool.copy()
+    lora_scale, theta, sm = 2.0, 5e5, 1.0 / np.sqrt(d)
+    for step in range(steps):
+        start = [b.pool.length(h) for h in b.handles]
+        for h in b.handles:
+            _, _, cow = b.pool.append(h, 1, want_slots=False)
+            if cow:
+                b.pool.cow_copy([cow])
+                host_b = apply_cows_host(host_b, [cow], Hkv, d)
+        b.refresh_tables()
+        b.make_plan(kernel)
+        assert b.plan.info["kernel"] == kernel
+        assert (b.pstart is not None) == freeze
+        q = encode(rng.standard_normal((n_agents, Hq, d)), dtype)
+        rows = dict(k_new=encode(rng.standard_normal((n_agents, Hkv, d)), dtype),
+                    v_new=encode(rng.standard_normal((n_agents, Hkv, d)), dtype),
+                    rk_new=encode(rng.standard_normal((n_agents, r)), dtype),
+                    rv_new=encode(rng.standard_normal((n_agents, r)), dtype))
+        b.q = to_device(q)
+        b.out.fill_(0x7FC0)
+        out = b.decode_append({k: to_device(v) for k, v in rows.items()}, lora_scale, sm, theta)
+        torch.cuda.synchronize()
+        starts = b.pstart_host if freeze else None
+        host_b, host_r = apply_rows_write(geo, host_b, host_r, b.btab_host, b.rtab_host,
+                                          [[t] for t in start], rows["k_new"][:, None],
+                                          rows["v_new"][:, None], rows["rk_new"][:, None],
+                                          rows["rv_new"][:, None], starts=starts)
+        ref = decode_attention(geo, host_b, host_r, b.btab_host, b.rtab_host, np.array(b.lens),
+                               q, Bk, Bv, lora_scale, sm, theta, starts=starts)
+        assert_close(gpu_values(out, dtype), ref,
+                     f"append step {step} kernel={kernel} freeze={freeze}", scale_abs=True)
+    got_b = b.bcache.cpu().numpy().view(np.uint16)
+    got_r = b.rcache.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_b, host_b), "pool bytes (base) after the loop"
+    assert np.array_equal(got_r, host_r), "pool bytes (residual) after the loop"
+
+
 def test_decode_append_llama3_react_shape():
     """Workload 1 (4 agents, 8192 shared + 512 private tokens, Llama3-8B attention shape):
     one appended token per agent at position 8704, MFMA kernel, sampled heads."""
