@@ -53,9 +53,7 @@ constexpr int kPageTrigBytes = kWaves * 2 * 64 * 2;     // per wave: cos[64], si
 constexpr int kQhBytes = kWaves * 4 * 64 * 16;          // per wave: bf16 q, [chunk][lane]
 constexpr int kMergeFloats = 4 + 32 + 4;                // m, l, pad, pad | acc[32] | accr[4]
 constexpr int kMergeBytes = kWaves * 64 * kMergeFloats * 4;
-constexpr int kBkRawBytes = kItemAgents * kR * kD * 2;  // B_k rows before the permutation
-constexpr int kLdsMain = kBkBytes + (kTrigBytes + kPageTrigBytes + kQhBytes > kBkRawBytes
-                                         ? kTrigBytes + kPageTrigBytes + kQhBytes : kBkRawBytes);
+constexpr int kLdsMain = kBkBytes + kTrigBytes + kPageTrigBytes + kQhBytes;
 constexpr int kLdsBytes = kLdsMain > kMergeBytes ? kLdsMain : kMergeBytes;
 
 __device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
@@ -198,7 +196,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   // Every load that depends on nothing else is issued first (this wave's query columns, the
   // group's agents and lengths, the page ids of the sub-range, the B_k rows), so that their
   // latencies overlap; the first page's key tiles follow as soon as its ids are in, and the
-  // on-chip set-up (B_k permutation, trig tables) runs while they are in flight.
+  // on-chip set-up (B_k packed into operand order, trig tables) runs while they are in flight.
   const int pps = (np + n_sub - 1) / n_sub;
   const int lpa = active ? lp0 + si * pps : 0;
   const int lpb = active ? min(lp0 + np, lpa + pps) : 0;
@@ -272,26 +270,26 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     const int nx = (in && lpi + 1 < p.max_pages) ? row[lpi + 1] : -1;
     vend = nx >= 0 ? nx : rlen[0];
   }
-  // Rows of B_k,a[:, h*d:(h+1)*d] are 256 contiguous bytes: read them coalesced into the
-  // trig-table area (filled only after the permutation below), to be permuted into the MFMA
-  // A-operand order.
-  // (a compile-time trip count, so that all pieces are in flight at once: piece i of this
-  // thread belongs to agent i)
-  constexpr int kBkPieces = kItemAgents * kR * (kD / 8) / kThreads;
-  static_assert(kR * (kD / 8) == kThreads, "one agent's B_k rows are one piece per thread");
-  // (branch-free: slots past the item's agents re-read its last agent's rows into staging
-  // space the permutation never reads)
-  {
-    const int k = tid / 16, piece = tid % 16;
-    uint4 rows[kBkPieces];
+  // B_k,a[:, h*d:(h+1)*d] goes to LDS in MFMA A-operand order without a staging pass: a
+  // work unit (agent jj, rank group g, dims 8pc .. 8pc+7) loads the four rank rows 4g .. 4g+3
+  // of its eight dims (16 contiguous bytes each, coalesced over pc) and later packs, per
+  // dim, the four ranks into the operand piece of the lane that consumes them.  Unit
+  // u = tid + kThreads * i, so jj = wave + kWaves * i is wave-uniform; all loads are issued
+  // here (units past the item's agents re-read its first agent and are not stored).
+  constexpr int kBkUnits = kItemAgents * 4 * (kD / 8) / kThreads;
+  static_assert(4 * (kD / 8) == 64, "a wave's units are one agent's");
+  uint4 bkr[kBkUnits][4];
 #pragma unroll
-    for (int i = 0; i < kBkPieces; ++i)
-      rows[i] = *reinterpret_cast<const uint4*>(Bk + (size_t(i < na ? ia[i] : ia[0]) * kR + k) * n +
-                                                h * kD + 8 * piece);
+  for (int i = 0; i < kBkUnits; ++i) {
+    const int jj = w + kWaves * i, g = (lane >> 4) & 3, pc = lane & 15;
+    int a = ia[0];
 #pragma unroll
-    for (int i = 0; i < kBkPieces; ++i)
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(lds + kBkBytes) + (i * kR + k) * kD +
-                                8 * piece) = rows[i];
+    for (int k = 1; k < kItemAgents; ++k)
+      if (jj == k && k < na) a = ia[k];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      bkr[i][r] = *reinterpret_cast<const uint4*>(Bk + (size_t(a) * kR + 4 * g + r) * n + h * kD +
+                                                  8 * pc);
   }
   const float qscale = p.sm_scale_log2;
 
@@ -615,25 +613,28 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     tsv[i] = __builtin_amdgcn_sinf(x);
     tcv[i] = __builtin_amdgcn_cosf(x);
   }
-  {
-    const uint16_t* raw = reinterpret_cast<const uint16_t*>(lds + kBkBytes);
-    __syncthreads();  // the B_k rows are staged
-    // (unrolled, with a compile-time trip count, so that its LDS reads are in flight together)
+  // pack the B_k units into operand order: dim x sits in tile T, row m with
+  // x = perm_dim(T, m), and the lane 16 g + m of that tile holds ranks 4g .. 4g+3
 #pragma unroll
-    for (int i = 0; i < kItemAgents * 8 * 64 / kThreads; ++i) {
-      const int x = tid + kThreads * i;
-      const int jj = x / (8 * 64), T = (x / 64) % 8, l = x % 64;
-      if (jj < na) {
-        const int dim = perm_dim(T, l & 15);
-        const uint16_t* src = raw + jj * kR * kD + dim;
-        const int k0 = 4 * (l >> 4);
+  for (int i = 0; i < kBkUnits; ++i) {
+    const int jj = w + kWaves * i, g = (lane >> 4) & 3, pc = lane & 15;
+    if (jj < na) {  // wave-uniform
+      const uint32_t r0[4] = {bkr[i][0].x, bkr[i][0].y, bkr[i][0].z, bkr[i][0].w};
+      const uint32_t r1[4] = {bkr[i][1].x, bkr[i][1].y, bkr[i][1].z, bkr[i][1].w};
+      const uint32_t r2[4] = {bkr[i][2].x, bkr[i][2].y, bkr[i][2].z, bkr[i][2].w};
+      const uint32_t r3[4] = {bkr[i][3].x, bkr[i][3].y, bkr[i][3].z, bkr[i][3].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int x = 8 * pc + e;
+        const int T = 2 * (x >> 5) + ((x & 7) >> 2), m = 4 * ((x & 31) >> 3) + (x & 3);
+        // ranks (4g, 4g+1) and (4g+2, 4g+3) of dim x: the low or high halves of word e/2
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         uint2 v;
-        v.x = uint32_t(src[k0 * kD]) | (uint32_t(src[(k0 + 1) * kD]) << 16);
-        v.y = uint32_t(src[(k0 + 2) * kD]) | (uint32_t(src[(k0 + 3) * kD]) << 16);
-        bkl[x] = v;
+        v.x = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1], sel);
+        v.y = __builtin_amdgcn_perm(r3[e >> 1], r2[e >> 1], sel);
+        bkl[(jj * 8 + T) * 64 + 16 * g + m] = v;
       }
     }
-    __syncthreads();  // the staging area is free again
   }
 #pragma unroll
   for (int i = 0; i < kTrigPer; ++i) {
