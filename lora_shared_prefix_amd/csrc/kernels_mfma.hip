@@ -1,5 +1,7 @@
-// MFMA (matrix-core) ResidualAttention decode kernel for gfx950: bf16 storage, d = 128,
-// r = 16, page size 16, up to 16 query columns (agents x GQA group) per wave.
+// MFMA (matrix-core) ResidualAttention kernels for gfx950, bf16 storage, d = 128, r = 16,
+// page size 16: the split-K decode kernel (up to 16 query columns -- agents x GQA group --
+// per wave; with decode-with-append it also stores the new rows first) and, further down,
+// the chunked-prefill kernel.
 //
 // ForkKV study note, "7. 实现 cross-reference" (kernel; core barriers (1) and (2)) and
 // "4. 作者证明" (Eq.(4), reproduction checks 3, 4 and 6): for each page the key of every
