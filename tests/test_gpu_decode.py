@@ -194,6 +194,26 @@ def test_ragged_tiny_batches(seed, dtype, kernel):
         assert errors(g, ref)[1] < 1e-5
 
 
+@pytest.mark.parametrize("G", [1, 2, 3, 16])
+def test_mfma_gqa_group_sizes(G):
+    """GQA groups the other tests leave out: G = 1 (one query head per KV head, four columns
+    of a wave's 16 used), 2, 3 (columns not a power of two) and 16 (one agent per wave, every
+    column used); ragged lengths and unaligned forks as above."""
+    case, arrays, host_after, b, bt, rt, lens = _tiny_batch(
+        760 + G, "bf16", fk.KERNEL_MFMA, Hq=2 * G, Hkv=2, d=128, r=16, n_agents=6,
+        max_prefix=200, max_suffix=40, num_pages=128)
+    assert b.plan.info["kernel"] == fk.KERNEL_MFMA
+    print(f"[gpu-decode] G={G} lens={list(lens)}", flush=True)
+    _poison(b.out)
+    out = b.decode(case["lora_scale"], case["sm_scale"], case["theta"])
+    torch.cuda.synchronize()
+    ref = decode_attention(Geometry(page_size=16, num_q_heads=2 * G, num_kv_heads=2,
+                                    head_dim=128, rank=16, dtype="bf16"), host_after,
+                           arrays["rpool"], bt, rt, lens, case["q"], case["Bk"], case["Bv"],
+                           case["lora_scale"], case["sm_scale"], case["theta"])
+    assert_close(gpu_values(out, "bf16"), ref, f"mfma G={G}", scale_abs=True)
+
+
 def test_placement_invariance_bitwise():
     """The same logical caches at other physical pages give bit-identical outputs."""
     case = tiny_case(801, "bf16", Hq=8, Hkv=2, d=128, r=16, n_agents=4, max_prefix=90,

@@ -73,6 +73,29 @@ def test_ragged_tiny_prefill(seed, dtype):
         assert errors(gv, ref)[1] < 1e-5
 
 
+@pytest.mark.parametrize("G", [1, 3, 16])
+def test_mfma_prefill_gqa_group_sizes(G):
+    """The MFMA prefill kernel flattens (query, head of the group) into rows of 256-row
+    blocks: G = 1 (one block), 3 (a block ends inside a query's heads) and 16 (seven blocks),
+    over a 101-query chunk, so the last block is ragged."""
+    C = 101
+    case = tiny_case(930 + G, "bf16", Hq=2 * G, Hkv=2, d=128, r=16, n_agents=2, chunk=C,
+                     max_prefix=70, max_suffix=20, num_pages=64)
+    case["ops"] = [op if op[0] != "fork" else (op[0], op[1], (op[2] // 16) * 16, op[3])
+                   for op in case["ops"]]
+    geom = dict(num_bpages=64, num_rpages=64, num_kv_heads=2, num_q_heads=2 * G, head_dim=128,
+                rank=16, dtype="bf16")
+    print(f"[gpu-prefill] mfma G={G} C={C}", flush=True)
+    b, out, ref, bt, rt, start, g = _run(geom, case, case["ops"], case["agents"], case["perm_b"],
+                                         case["perm_r"], C, case["lora_scale"], case["sm_scale"],
+                                         case["theta"])
+    exp_b, exp_r = apply_chunk_write(g, case["bpool"], case["rpool"], bt, rt, start,
+                                     case["k_new"], case["v_new"], case["rk_new"], case["rv_new"])
+    assert np.array_equal(_host(b.bcache, "bf16").view(np.uint8), exp_b.view(np.uint8))
+    assert np.array_equal(_host(b.rcache, "bf16").view(np.uint8), exp_r.view(np.uint8))
+    assert_close(gpu_values(out, "bf16"), ref, f"prefill mfma G={G}", scale_abs=True)
+
+
 def test_qwen3_shape_scaled_prefill():
     """Qwen3-8B attention shape (32/8 heads, d=128, r=16, theta 1e6) at a reduced prefix."""
     rng = np.random.default_rng(44)
