@@ -383,6 +383,12 @@ def test_empty_agent_and_errors():
         fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab[:, :0].contiguous(),
                                 b.rtab, b.out, b.workspace, 1.0, 0.3, 1e4)
     assert e.value.code == fk.EINVAL
+    # a negative or non-finite softmax scale, theta <= 0
+    for sm, theta in ((-0.3, 1e4), (float("nan"), 1e4), (0.3, 0.0)):
+        with pytest.raises(fk.ForkKVError) as e:
+            fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab, b.rtab, b.out,
+                                    b.workspace, 1.0, sm, theta)
+        assert e.value.code == fk.EINVAL
     # device buffers off a 16-byte boundary
     qm = torch.empty(b.q.numel() + 1, dtype=b.q.dtype, device="cuda")[1:].view_as(b.q)
     with pytest.raises(fk.ForkKVError) as e:
