@@ -26,8 +26,8 @@ hipEvent_t get_event(forkkv_plan* pl) {
   return e;
 }
 
-// Scales are finite; the softmax scale is also >= 0 (the attention kernels take each
-// row's maximum of the raw scores and scale it afterwards), theta > 0.
+// Scales are finite; the softmax scale is also >= 0 (the MFMA prefill kernel takes each
+// row's maximum of the raw scores and scales it afterwards), theta > 0.
 bool finite(float x) { return std::isfinite(x); }
 
 // Device buffers are read and written with 8- and 16-byte vector accesses.
