@@ -28,6 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# the timed decode workload, the two other decode shapes reported beside it, and the
+# prefill workload
+DECODE_WORKLOAD = "llama3_8b_mapreduce_decode"
+OTHER_DECODE_WORKLOADS = ("llama3_8b_react_decode", "qwen25_14b_batched_decode")
+PREFILL_WORKLOAD = "qwen3_8b_chunked_prefill"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_pmc_llama3_8b_mapreduce.json")
 KERNEL_SOURCES = {
     "generic": "lora_shared_prefix_amd/csrc/kernels_generic.hip",
@@ -111,12 +116,13 @@ def prefill_flops(cfg):
 
 
 def bench_prefill(steps, warmup):
-    """Chunk tokens/s of the prefill call (row write + causal attention) on workload 4."""
+    """Chunk tokens/s of the prefill call (row write + causal attention) on the Qwen3-8B
+    workload: 8 agents, one 512-row chunk each, after a shared 131072-token prefix."""
     import numpy as np
     import torch
     from lora_shared_prefix_amd.session import DeviceBatch, to_device, workload_geom
-    from workloads import CONFIGS, draw_inputs, pool_ops
-    cfg = CONFIGS[4]
+    from workloads import config_by_name, draw_inputs, pool_ops
+    cfg = config_by_name(PREFILL_WORKLOAD)
     log(f"drawing inputs of {cfg.name}")
     x = draw_inputs(cfg)
     ops, agents = pool_ops(cfg)
@@ -181,16 +187,17 @@ def bench_prefill(steps, warmup):
     return res
 
 
-def bench_decode(idx, steps, warmup, kernel, pages_per_item, copies_arg):
-    """Decode step time (graph replay), split/combine launch times (events) on workload idx."""
+def bench_decode(name, steps, warmup, kernel, pages_per_item, copies_arg):
+    """Decode step time (graph replay), split/combine launch times (events) on the named
+    decode workload."""
     import numpy as np
     import torch
 
     from lora_shared_prefix_amd import forkkv as fk
     from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
-    from workloads import CONFIGS, draw_inputs, pool_ops
+    from workloads import config_by_name, draw_inputs, pool_ops
 
-    cfg = CONFIGS[idx]
+    cfg = config_by_name(name)
     assert cfg.kind == "decode"
     log(f"drawing inputs of {cfg.name}")
     x = draw_inputs(cfg)
@@ -284,7 +291,7 @@ def bench_decode(idx, steps, warmup, kernel, pages_per_item, copies_arg):
     wsplit, _, wl = plan.timing()
 
     achieved = split_bytes / (split_avg * 1e-3) / 1e9
-    traffic = load_traffic(kname) if idx == 2 else None
+    traffic = load_traffic(kname) if name == DECODE_WORKLOAD else None
     pct = np.percentile(np.array(split_samples) * 1e3, [10, 50, 90]).tolist()
     return {
         "_cfg": cfg, "_x": x, "_ops": ops, "_agents": agents,
@@ -451,14 +458,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="index of the decode workload")
+    ap.add_argument("--workload", default=DECODE_WORKLOAD, help="name of the decode workload")
     ap.add_argument("--kernel", choices=["auto", "generic", "mfma"], default="auto")
     ap.add_argument("--pages-per-item", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--cpu-sample", type=int, default=8,
                     help="agents timed on the oracle (0 = skip; 8 = the whole batch, about 10 s)")
     ap.add_argument("--no-more-workloads", action="store_true",
-                    help="skip the extra decode figures of workloads 1 and 3")
+                    help="skip the extra decode figures of the ReAct and batched workloads")
     ap.add_argument("--no-next", action="store_true",
                     help="skip decode-with-append, frozen-tail decode and eviction/refill timing")
     ap.add_argument("--no-prefill", action="store_true",
@@ -468,7 +475,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -477,8 +484,6 @@ def main():
 
     from lora_shared_prefix_amd import forkkv as fk
     from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
-    from workloads import CONFIGS, draw_inputs, pool_ops
-
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * 2 ** 20) // 4
@@ -519,11 +524,11 @@ def main():
         "copy_bandwidth_gbs": ceiling,
         "split_frac_of_copy_bandwidth": d["roofline"]["achieved"] / ceiling,
     }
-    if not args.no_more_workloads and args.workload == 2:
+    if not args.no_more_workloads and args.workload == DECODE_WORKLOAD:
         others = {}
-        for idx in (1, 3):
+        for name in OTHER_DECODE_WORKLOADS:
             torch.cuda.empty_cache()
-            o = bench_decode(idx, max(10, args.steps // 2), max(2, args.warmup // 2), kernel, 0, 0)
+            o = bench_decode(name, max(10, args.steps // 2), max(2, args.warmup // 2), kernel, 0, 0)
             for k in ("_cfg", "_x", "_ops", "_agents"):
                 o.pop(k)
             others[o["config"]["workload"]] = {
@@ -533,7 +538,7 @@ def main():
                 "algorithmic_bytes_per_launch": o["roofline"]["algorithmic_bytes_per_launch"],
                 "combine_avg_us": o["combine_avg_us"], "config": o["config"]}
         result["other_decode_workloads"] = others
-    if not args.no_next and args.workload == 2:
+    if not args.no_next and args.workload == DECODE_WORKLOAD:
         torch.cuda.empty_cache()
         result["next_rows"] = bench_next_rows(cfg, x, ops, agents, max(10, args.steps // 2))
     if not args.no_prefill:

@@ -12,7 +12,7 @@ import pytest
 from lora_shared_prefix_amd import forkkv as fk
 from oracle import PoolError, PoolModel
 from tests.pool_scenarios import fanout_ops, read_table
-from workloads import CONFIGS, chunk_ops, pool_ops
+from workloads import CONFIGS, chunk_ops, config_by_name, pool_ops
 
 ITEM_INTS = 20   # lp0, pages, agents, unused, 8 agent ids, 8 slot ids
 
@@ -55,9 +55,9 @@ def _replay_both(lp, pm, ops):
     return names_l
 
 
-@pytest.mark.parametrize("idx", range(5))
-def test_workload_topologies_match_model(idx):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("name", [c.name for c in CONFIGS])
+def test_workload_topologies_match_model(name):
+    cfg = config_by_name(name)
     rng = np.random.default_rng(cfg.seed)
     pb = rng.permutation(cfg.num_bpages)
     pr = rng.permutation(cfg.num_rpages)
@@ -204,12 +204,12 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
     assert slots_seen == set(range(n_slots))
 
 
-@pytest.mark.parametrize("idx,kernel", [(0, fk.KERNEL_GENERIC), (1, fk.KERNEL_GENERIC),
-                                        (2, fk.KERNEL_GENERIC), (3, fk.KERNEL_GENERIC),
-                                        (1, fk.KERNEL_MFMA), (2, fk.KERNEL_MFMA),
-                                        (3, fk.KERNEL_MFMA)])
-def test_plan_covers_workloads(idx, kernel):
-    cfg = CONFIGS[idx]
+@pytest.mark.parametrize("name,kernel", [("tiny_f32", fk.KERNEL_GENERIC), ("llama3_8b_react_decode", fk.KERNEL_GENERIC),
+                                         ("llama3_8b_mapreduce_decode", fk.KERNEL_GENERIC),
+                                         ("qwen25_14b_batched_decode", fk.KERNEL_GENERIC), ("llama3_8b_react_decode", fk.KERNEL_MFMA),
+                                         ("llama3_8b_mapreduce_decode", fk.KERNEL_MFMA), ("qwen25_14b_batched_decode", fk.KERNEL_MFMA)])
+def test_plan_covers_workloads(name, kernel):
+    cfg = config_by_name(name)
     lp = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim, cfg.rank,
                  cfg.dtype)
     ops, agents = pool_ops(cfg)

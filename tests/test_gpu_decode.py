@@ -16,7 +16,7 @@ from oracle.attention import Geometry, decode_attention  # noqa: E402
 from tests.cases import encode, tiny_case  # noqa: E402
 from tests.gpu_common import (apply_cows_host, assert_close, errors, gpu_values,  # noqa: E402
                               model_tables, poison_unused, used_rows)
-from workloads import CONFIGS, draw_inputs, pool_ops  # noqa: E402
+from workloads import config_by_name, draw_inputs, pool_ops  # noqa: E402
 
 KERNELS = [fk.KERNEL_GENERIC, fk.KERNEL_MFMA]
 
@@ -51,17 +51,17 @@ def _poison(t):
         t.fill_(0x7FC0)
 
 
-def _workload(idx):
-    if idx not in _CACHE:
-        cfg = CONFIGS[idx]
+def _workload(name):
+    if name not in _CACHE:
+        cfg = config_by_name(name)
         print(f"[gpu-decode] drawing inputs of {cfg.name}", flush=True)
         _CACHE.clear()
-        _CACHE[idx] = (cfg, draw_inputs(cfg))
-    return _CACHE[idx]
+        _CACHE[name] = (cfg, draw_inputs(cfg))
+    return _CACHE[name]
 
 
-def _run_workload(idx, kernel, sample_agents=None, sample_heads=None, arrays=None):
-    cfg, x = _workload(idx)
+def _run_workload(name, kernel, sample_agents=None, sample_heads=None, arrays=None):
+    cfg, x = _workload(name)
     if arrays is not None:
         x = dict(x, **arrays)
     ops, agents = pool_ops(cfg)
@@ -86,26 +86,26 @@ def _run_workload(idx, kernel, sample_agents=None, sample_heads=None, arrays=Non
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_tiny_fp32_workload(kernel):
-    cfg = CONFIGS[0]
+    cfg = config_by_name("tiny_f32")
     if not _kernel_available(cfg.dtype, cfg.head_dim, cfg.rank, cfg.group, kernel):
         pytest.skip("kernel does not cover this shape")
-    cfg, g, ref, mask = _run_workload(0, kernel)
+    cfg, g, ref, mask = _run_workload("tiny_f32", kernel)
     assert_close(g, ref, "tiny fp32")
     a, rel = errors(g, ref)
     assert rel < 1e-5  # fp32 throughout
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("idx,agents,heads", [
-    (1, None, None),
-    (2, None, [0, 3, 7]),
-    (3, [0, 9, 18, 31], [0, 5]),
+@pytest.mark.parametrize("name,agents,heads", [
+    ("llama3_8b_react_decode", None, None),
+    ("llama3_8b_mapreduce_decode", None, [0, 3, 7]),
+    ("qwen25_14b_batched_decode", [0, 9, 18, 31], [0, 5]),
 ])
-def test_bf16_workloads(kernel, idx, agents, heads):
-    cfg = CONFIGS[idx]
+def test_bf16_workloads(kernel, name, agents, heads):
+    cfg = config_by_name(name)
     if not _kernel_available(cfg.dtype, cfg.head_dim, cfg.rank, cfg.group, kernel):
         pytest.skip("kernel does not cover this shape")
-    cfg, g, ref, mask = _run_workload(idx, kernel, agents, heads)
+    cfg, g, ref, mask = _run_workload(name, kernel, agents, heads)
     assert np.all(np.isfinite(g))
     assert_close(g[mask], ref[mask], cfg.name)
 
@@ -113,12 +113,13 @@ def test_bf16_workloads(kernel, idx, agents, heads):
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_residual_delta(kernel):
     """The adapter's contribution itself must match, not only the (base-dominated) output."""
-    cfg = CONFIGS[1]
+    cfg = config_by_name("llama3_8b_react_decode")
     if not _kernel_available(cfg.dtype, cfg.head_dim, cfg.rank, cfg.group, kernel):
         pytest.skip("kernel does not cover this shape")
-    _, gB, rB, _ = _run_workload(1, kernel)
-    zero = {"Bk": np.zeros_like(_CACHE[1][1]["Bk"]), "Bv": np.zeros_like(_CACHE[1][1]["Bv"])}
-    _, g0, r0, _ = _run_workload(1, kernel, arrays=zero)
+    _, gB, rB, _ = _run_workload("llama3_8b_react_decode", kernel)
+    x = _CACHE["llama3_8b_react_decode"][1]
+    zero = {"Bk": np.zeros_like(x["Bk"]), "Bv": np.zeros_like(x["Bv"])}
+    _, g0, r0, _ = _run_workload("llama3_8b_react_decode", kernel, arrays=zero)
     dg, dr = gB - g0, rB - r0
     rel = np.linalg.norm(dg - dr) / np.linalg.norm(dr)
     print(f"[parity] residual delta rel={rel:.3e}", flush=True)
@@ -243,7 +244,7 @@ def test_placement_invariance_bitwise():
 
 def test_sharing_invariance():
     """Duplicating the shared prefix per agent (no aliasing) gives the same outputs."""
-    cfg = CONFIGS[1]
+    cfg = config_by_name("llama3_8b_react_decode")
     cfg_small = dict(num_bpages=2048, num_rpages=4096, num_kv_heads=8, num_q_heads=32,
                      head_dim=128, rank=16, dtype="bf16")
     rng = np.random.default_rng(5)
@@ -284,7 +285,7 @@ def test_sharing_invariance():
 def test_graph_replay_matches_eager(kernel):
     """A decode call captured in a HIP graph gives the eager call's bytes on every replay
     (three replays, with eager work on the output between them)."""
-    cfg, x = _workload(1)
+    cfg, x = _workload("llama3_8b_react_decode")
     ops, agents = pool_ops(cfg)
     b = DeviceBatch(workload_geom(cfg), x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel)
     sm = 1.0 / np.sqrt(cfg.head_dim)
@@ -307,8 +308,9 @@ def test_graph_replay_matches_eager(kernel):
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_many_partials_per_agent(kernel):
     """One page per split item: every agent's row merges well over 64 split-K partials, so
-    the combine takes several chunks per row (workload 1, heads 0 and 5 checked)."""
-    cfg, x = _workload(1)
+    the combine takes several chunks per row (the Llama3-8B ReAct workload, heads 0 and 5
+    checked)."""
+    cfg, x = _workload("llama3_8b_react_decode")
     ops, agents = pool_ops(cfg)
     b = DeviceBatch(workload_geom(cfg), x, ops, agents, x["perm_b"], x["perm_r"], kernel=kernel,
                     pages_per_item=1)

@@ -22,7 +22,7 @@ from oracle.attention import Geometry, apply_chunk_write, decode_attention  # no
 from tests.cases import encode  # noqa: E402
 from tests.gpu_common import (apply_cows_host, assert_close, gpu_values,  # noqa: E402
                               model_tables, poison_unused, used_rows)
-from workloads import CONFIGS, draw_inputs, pool_ops  # noqa: E402
+from workloads import config_by_name, draw_inputs, pool_ops  # noqa: E402
 
 
 def _fork_ops(rng, n_agents, L0):
@@ -195,9 +195,9 @@ def test_decode_append_steps(kernel, freeze):
 
 
 def test_decode_append_llama3_react_shape():
-    """Workload 1 (4 agents, 8192 shared + 512 private tokens, Llama3-8B attention shape):
+    """The Llama3-8B ReAct workload (4 agents, 8192 shared + 512 private tokens):
     one appended token per agent at position 8704, MFMA kernel, sampled heads."""
-    cfg = CONFIGS[1]
+    cfg = config_by_name("llama3_8b_react_decode")
     print(f"[gpu-append] drawing inputs of {cfg.name}", flush=True)
     x = draw_inputs(cfg)
     ops, agents = pool_ops(cfg)

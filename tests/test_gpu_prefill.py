@@ -14,7 +14,7 @@ from lora_shared_prefix_amd.session import DeviceBatch, to_device, workload_geom
 from oracle.attention import Geometry, apply_chunk_write, prefill_attention  # noqa: E402
 from tests.cases import encode, tiny_case  # noqa: E402
 from tests.gpu_common import assert_close, errors, gpu_values, model_tables  # noqa: E402
-from workloads import CONFIGS, chunk_ops, draw_inputs, pool_ops  # noqa: E402
+from workloads import chunk_ops, config_by_name, draw_inputs, pool_ops  # noqa: E402
 
 
 def _host(t, dtype):
@@ -126,12 +126,13 @@ def test_qwen3_shape_scaled_prefill():
 
 
 def test_qwen3_8b_chunked_prefill_workload():
-    """Workload 4 at full size: 8 agents x 512-token chunks over a 131072-token shared prefix.
+    """The Qwen3-8B prefill workload at full size: 8 agents x 512-token chunks over a
+    131072-token shared prefix.
 
     Written rows are checked bit for bit at sampled slots; attention is checked on sampled
     (agent, query, head) rows the oracle computes one by one.
     """
-    cfg = CONFIGS[4]
+    cfg = config_by_name("qwen3_8b_chunked_prefill")
     print(f"[gpu-prefill] drawing inputs of {cfg.name}", flush=True)
     x = draw_inputs(cfg)
     ops, agents = pool_ops(cfg)

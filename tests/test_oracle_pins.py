@@ -22,7 +22,7 @@ from oracle.storage import base_key_rows, base_value_rows, decode_values
 from tests.bruteforce import brute_decode, brute_prefill, brute_prefill_at
 from tests.cases import tiny_case
 from tests.fused_model import fused_decode
-from workloads import CONFIGS, draw_inputs, pool_ops
+from workloads import config_by_name, draw_inputs, pool_ops
 
 
 def _nrel(a, b):
@@ -62,8 +62,8 @@ def _brute(case, bt, rt, lens):
 # ---- C2: brute force on tiny inputs ---------------------------------------------------------
 
 def test_tiny_config_matches_brute_force():
-    """Workload 0 (tiny, fp32) in full against the pure-Python scalar brute force."""
-    cfg = CONFIGS[0]
+    """The tiny fp32 workload in full against the pure-Python scalar brute force."""
+    cfg = config_by_name("tiny_f32")
     x = draw_inputs(cfg)
     pm = PoolModel(cfg.num_bpages, cfg.num_rpages, cfg.page_size, x["perm_b"], x["perm_r"])
     ops, agents = pool_ops(cfg)

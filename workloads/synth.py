@@ -5,7 +5,7 @@ and the list of pool operations (create / append / fork) that builds each
 workload's sharing topology.  Both the oracle's bookkeeping model and the HIP
 library replay the same operation list with their own code.
 
-Storage layout of the two page pools (the pages are silent on it; this build
+Storage layout of the two page pools (the pages are silent on it; the library
 fixes it, and both sides read the same bytes): a base page is
 ``bpool[page][plane][Hkv][P*d]`` (plane 0 = post-RoPE keys, plane 1 = values)
 and a residual page ``rpool[page][plane][P*r]`` (plane 0 = key residual,
