@@ -276,7 +276,7 @@ typedef struct {
   const int32_t* rtab;      /* device [N][max_pages] */
   int32_t max_pages;        /* row stride of btab / rtab */
   float lora_scale;         /* s */
-  float sm_scale;           /* softmax scale >= 0, e.g. 1/sqrt(d) */
+  float sm_scale;           /* softmax scale > 0, e.g. 1/sqrt(d) */
   float rope_theta;         /* theta */
   void* out;                /* device [N][Hq][d], pool dtype; an agent with len 0 gets 0 */
   void* workspace;          /* device, workspace_bytes of the plan */
@@ -288,7 +288,7 @@ typedef struct {
 } forkkv_decode_args;
 
 /* Errors: FORKKV_EINVAL (null pointers, a plan of another geometry, max_pages below the
- * plan's, a small workspace, non-finite scales, a negative sm_scale, theta <= 0, no pstart
+ * plan's, a small workspace, non-finite scales, sm_scale <= 0, theta <= 0, no pstart
  * for a plan over a frozen tail);
  * FORKKV_ESTATE (pool without device storage, plan not uploaded); FORKKV_EHIP. */
 int forkkv_residual_attn_decode(const forkkv_decode_args* args, hipStream_t stream);
@@ -354,7 +354,7 @@ typedef struct {
   int32_t max_pages;
   const int32_t* start_pos;      /* device [N] */
   const int32_t* start_pos_host; /* host [N], same values (validation and launch shape) */
-  float lora_scale, sm_scale, rope_theta;  /* finite; sm_scale >= 0, rope_theta > 0 */
+  float lora_scale, sm_scale, rope_theta;  /* finite; sm_scale > 0, rope_theta > 0 */
   void* out;                /* device [N][C][Hq][d] */
   const int32_t* positions;      /* nullable: device [N][C], row positions (see above) */
   const int32_t* positions_host; /* host [N][C], same values; required with positions */

@@ -26,8 +26,9 @@ hipEvent_t get_event(forkkv_plan* pl) {
   return e;
 }
 
-// Scales are finite; the softmax scale is also >= 0 (the MFMA prefill kernel takes each
-// row's maximum of the raw scores and scales it afterwards), theta > 0.
+// Scales are finite; the softmax scale is also > 0 (the MFMA prefill kernel takes each
+// row's maximum of the raw scores and scales it afterwards, and scales masked scores of
+// -inf), theta > 0.
 bool finite(float x) { return std::isfinite(x); }
 
 // Device buffers are read and written with 8- and 16-byte vector accesses.
@@ -89,7 +90,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   if (!pl->aligned && !a->pstart) return FORKKV_EINVAL;  // a frozen tail needs the slot map
   if (pl->n_slots > 0 && (!a->workspace || a->workspace_bytes < pl->workspace_bytes))
     return FORKKV_EINVAL;
-  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->sm_scale >= 0.f) ||
+  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->sm_scale > 0.f) ||
       !(a->rope_theta > 0.f) || !finite(a->rope_theta))
     return FORKKV_EINVAL;
 
@@ -242,7 +243,7 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
     return FORKKV_EINVAL;
   if (listed ? !a->positions_host : (!a->start_pos || !a->start_pos_host)) return FORKKV_EINVAL;
   if (a->max_pages < 1) return FORKKV_EINVAL;
-  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->sm_scale >= 0.f) ||
+  if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->sm_scale > 0.f) ||
       !(a->rope_theta > 0.f) || !finite(a->rope_theta))
     return FORKKV_EINVAL;
   const int64_t cap = int64_t(a->max_pages) * kPage;

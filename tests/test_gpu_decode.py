@@ -385,8 +385,8 @@ def test_empty_agent_and_errors():
         fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab[:, :0].contiguous(),
                                 b.rtab, b.out, b.workspace, 1.0, 0.3, 1e4)
     assert e.value.code == fk.EINVAL
-    # a negative or non-finite softmax scale, theta <= 0
-    for sm, theta in ((-0.3, 1e4), (float("nan"), 1e4), (0.3, 0.0)):
+    # a softmax scale that is not positive and finite, theta <= 0
+    for sm, theta in ((-0.3, 1e4), (0.0, 1e4), (float("nan"), 1e4), (0.3, 0.0)):
         with pytest.raises(fk.ForkKVError) as e:
             fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab, b.rtab, b.out,
                                     b.workspace, 1.0, sm, theta)

@@ -121,8 +121,8 @@ def test_prefill_positions_qwen3_shape():
 
 
 def test_prefill_positions_errors():
-    """Non-increasing positions, positions outside the tables and a negative softmax scale
-    are rejected."""
+    """Non-increasing positions, positions outside the tables and a softmax scale that is
+    not positive are rejected."""
     rng, ops, agents, perm_b, perm_r, arrays, geom, rows = _case(9, "f32", 16, 4, 4, 2, 2, 16,
                                                                  20, 2, 2, 32)
     b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
@@ -137,11 +137,13 @@ def test_prefill_positions_errors():
                                      positions=torch.tensor(bad, dtype=torch.int32).cuda(),
                                      positions_host=bad)
         assert e.value.code == fk.EINVAL
-    # a negative softmax scale (valid positions)
+    # a softmax scale that is not positive (valid positions)
     good = [[1, 2, 3, 4], [1, 2, 3, 4]]
-    with pytest.raises(fk.ForkKVError) as e:
-        fk.residual_attn_prefill(b.pool, dev["q"], dev["k_new"], dev["v_new"], dev["rk_new"],
-                                 dev["rv_new"], b.Bk, b.Bv, b.btab, b.rtab, None, None, out, 1.0,
-                                 -0.25, 1e4, positions=torch.tensor(good, dtype=torch.int32).cuda(),
-                                 positions_host=good)
-    assert e.value.code == fk.EINVAL
+    for sm in (-0.25, 0.0):
+        with pytest.raises(fk.ForkKVError) as e:
+            fk.residual_attn_prefill(b.pool, dev["q"], dev["k_new"], dev["v_new"],
+                                     dev["rk_new"], dev["rv_new"], b.Bk, b.Bv, b.btab, b.rtab,
+                                     None, None, out, 1.0, sm, 1e4,
+                                     positions=torch.tensor(good, dtype=torch.int32).cuda(),
+                                     positions_host=good)
+        assert e.value.code == fk.EINVAL
