@@ -242,7 +242,10 @@ typedef struct {
 } forkkv_plan_info;
 
 /* Build the decode plan of the n sequences seqs (agent a = seqs[a]) for num_q_heads
- * query heads.  opts is nullable. */
+ * query heads.  opts is nullable.  Kernel coverage: the MFMA kernel takes bf16, d = 128,
+ * r = 16 and up to 16 query heads per KV head; the generic kernel every pool shape whose
+ * group G = num_q_heads / Hkv has G * d <= 8192 and G * r <= 2048 (its LDS plan may use up
+ * to 160 KiB); other shapes return FORKKV_EUNSUPPORTED, as does prefill for them. */
 int forkkv_plan_decode(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
                        int32_t num_q_heads, const forkkv_plan_opts* opts, forkkv_plan** out);
 int forkkv_plan_get_info(const forkkv_plan* plan, forkkv_plan_info* out);

@@ -67,7 +67,10 @@ __host__ __device__ inline GenLds gen_lds(int na, int rows, int d, int r) {
   return L;
 }
 
-constexpr int kMaxLds = 64 * 1024;
+// A gfx950 workgroup may use the CU's whole 160 KiB of LDS; launches above the default
+// 64 KiB of dynamic LDS raise the kernel's limit first (see launch_generic).
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kDefaultDynLds = 64 * 1024;
 
 // Rows of the workgroup: decode = (agent j of the item, q head within the group);
 // prefill = (query of the block, q head within the group), one agent.
@@ -675,17 +678,29 @@ int generic_max_agents(int group, int head_dim, int rank) {
   return best;
 }
 
+// Launch one instantiation of the generic kernel with lds bytes of dynamic LDS.
+template <typename T, bool kPrefill>
+hipError_t launch_generic(dim3 grid, int lds, hipStream_t s, const DecodeParams& dp,
+                          const PrefillParams& pp) {
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  if (lds > kDefaultDynLds) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&residual_attn_generic<T, kPrefill>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((residual_attn_generic<T, kPrefill>), grid, dim3(kGenericThreads), lds, s,
+                     dp, pp);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_generic(const DecodeParams& p, int dtype, int max_agents, hipStream_t s) {
   const int rows = max_agents * p.group;
   const int lds = gen_lds(max_agents, rows, p.head_dim, p.rank).total;
-  if (lds > kMaxLds) return hipErrorInvalidValue;
   dim3 grid(p.n_items, p.num_kv_heads);
   PrefillParams none{};
-  if (dtype == FORKKV_DTYPE_F32)
-    hipLaunchKernelGGL((residual_attn_generic<float, false>), grid, dim3(kGenericThreads), lds, s, p, none);
-  else
-    hipLaunchKernelGGL((residual_attn_generic<uint16_t, false>), grid, dim3(kGenericThreads), lds, s, p, none);
-  return hipGetLastError();
+  return dtype == FORKKV_DTYPE_F32 ? launch_generic<float, false>(grid, lds, s, p, none)
+                                   : launch_generic<uint16_t, false>(grid, lds, s, p, none);
 }
 
 template <typename T, int kDG>
@@ -747,14 +762,10 @@ hipError_t launch_prefill_generic(const PrefillParams& p, int dtype, hipStream_t
   const int QB = prefill_rows(p.group, p.head_dim, p.rank);
   if (QB < 1) return hipErrorInvalidValue;
   const int lds = gen_lds(1, QB * p.group, p.head_dim, p.rank).total;
-  if (lds > kMaxLds) return hipErrorInvalidValue;
   dim3 grid((p.chunk_len + QB - 1) / QB, p.num_kv_heads, p.n_agents);
   DecodeParams none{};
-  if (dtype == FORKKV_DTYPE_F32)
-    hipLaunchKernelGGL((residual_attn_generic<float, true>), grid, dim3(kGenericThreads), lds, s, none, p);
-  else
-    hipLaunchKernelGGL((residual_attn_generic<uint16_t, true>), grid, dim3(kGenericThreads), lds, s, none, p);
-  return hipGetLastError();
+  return dtype == FORKKV_DTYPE_F32 ? launch_generic<float, true>(grid, lds, s, none, p)
+                                   : launch_generic<uint16_t, true>(grid, lds, s, none, p);
 }
 
 hipError_t launch_cow_copy(void* bcache, int dtype, int Hkv, int d, int32_t src, int32_t dst,

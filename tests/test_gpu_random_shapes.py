@@ -103,3 +103,47 @@ def test_random_prefill(seed):
     assert np.array_equal(_host(b.bcache, dtype).view(np.uint8), exp_b.view(np.uint8)), what
     assert np.array_equal(_host(b.rcache, dtype).view(np.uint8), exp_r.view(np.uint8)), what
     _check(gpu_values(out, dtype), ref, dtype, what)
+
+
+# The largest shapes the pools accept: d = 256 and r = 64 (the generic kernel, whose LDS plan
+# then exceeds the default 64 KiB), and the largest GQA group at each size.
+MAX_SHAPES = [("f32", 256, 64, 2, 1), ("bf16", 256, 64, 1, 4), ("f32", 256, 16, 1, 32),
+              ("bf16", 224, 64, 2, 8), ("bf16", 128, 16, 1, 64)]
+
+
+@pytest.mark.parametrize("dtype,d,r,Hkv,G", MAX_SHAPES)
+def test_max_shapes_decode(dtype, d, r, Hkv, G):
+    what = f"max-shape decode {dtype} d={d} r={r} Hkv={Hkv} G={G}"
+    print(f"[gpu-random] {what}", flush=True)
+    case, arrays, host_after, b, bt, rt, lens = _tiny_batch(
+        4400 + d + r + G, dtype, fk.KERNEL_AUTO, Hq=G * Hkv, Hkv=Hkv, d=d, r=r, n_agents=5,
+        max_prefix=150, max_suffix=40, num_pages=96)
+    _poison(b.out)
+    out = b.decode(case["lora_scale"], case["sm_scale"], case["theta"])
+    torch.cuda.synchronize()
+    ref = decode_attention(Geometry(page_size=16, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                                    head_dim=d, rank=r, dtype=dtype), host_after,
+                           arrays["rpool"], bt, rt, lens, case["q"], case["Bk"], case["Bv"],
+                           case["lora_scale"], case["sm_scale"], case["theta"])
+    _check(gpu_values(out, dtype), ref, dtype, f"{what} kernel={b.plan.info['kernel']}")
+
+
+@pytest.mark.parametrize("dtype,d,r,Hkv,G", MAX_SHAPES)
+def test_max_shapes_prefill(dtype, d, r, Hkv, G):
+    C = 37
+    what = f"max-shape prefill {dtype} d={d} r={r} Hkv={Hkv} G={G} C={C}"
+    print(f"[gpu-random] {what}", flush=True)
+    case = tiny_case(5400 + d + r + G, dtype, Hq=G * Hkv, Hkv=Hkv, d=d, r=r, n_agents=2,
+                     chunk=C, max_prefix=60, max_suffix=20, num_pages=48)
+    case["ops"] = [op if op[0] != "fork" else (op[0], op[1], (op[2] // 16) * 16, op[3])
+                   for op in case["ops"]]
+    geom = dict(num_bpages=48, num_rpages=48, num_kv_heads=Hkv, num_q_heads=G * Hkv,
+                head_dim=d, rank=r, dtype=dtype)
+    b, out, ref, bt, rt, start, g = _run(geom, case, case["ops"], case["agents"], case["perm_b"],
+                                         case["perm_r"], C, case["lora_scale"], case["sm_scale"],
+                                         case["theta"])
+    exp_b, exp_r = apply_chunk_write(g, case["bpool"], case["rpool"], bt, rt, start,
+                                     case["k_new"], case["v_new"], case["rk_new"], case["rv_new"])
+    assert np.array_equal(_host(b.bcache, dtype).view(np.uint8), exp_b.view(np.uint8)), what
+    assert np.array_equal(_host(b.rcache, dtype).view(np.uint8), exp_r.view(np.uint8)), what
+    _check(gpu_values(out, dtype), ref, dtype, what)
