@@ -160,3 +160,40 @@ def test_qwen3_8b_chunked_prefill_workload():
             rpage = rt[a][t // 16]
             assert np.array_equal(rpool[rpage, 0, res_key_offset(row, ranks)], x["rk_new"][a, i])
             assert np.array_equal(rpool[rpage, 1, res_value_offset(row, ranks, 16)], x["rv_new"][a, i])
+
+
+@pytest.mark.parametrize("dtype,d,r,Hkv,G", [("bf16", 128, 16, 2, 4), ("f32", 256, 64, 1, 2)])
+def test_prefill_graph_replay_matches_eager(dtype, d, r, Hkv, G):
+    """A prefill call captured in a HIP graph (row write, then attention: the MFMA kernel, or
+    at d = 256 the generic kernel with more than 64 KiB of LDS) gives the eager call's output
+    and pool bytes on every replay (three replays, eager work on the output between them)."""
+    C = 29
+    case = tiny_case(960 + d, dtype, Hq=G * Hkv, Hkv=Hkv, d=d, r=r, n_agents=2, chunk=C,
+                     max_prefix=50, max_suffix=20, num_pages=48)
+    case["ops"] = [op if op[0] != "fork" else (op[0], op[1], (op[2] // 16) * 16, op[3])
+                   for op in case["ops"]]
+    geom = dict(num_bpages=48, num_rpages=48, num_kv_heads=Hkv, num_q_heads=G * Hkv,
+                head_dim=d, rank=r, dtype=dtype)
+    print(f"[gpu-prefill] graph replay {dtype} d={d} r={r} G={G}", flush=True)
+    b = DeviceBatch(geom, case, case["ops"], case["agents"], case["perm_b"], case["perm_r"],
+                    plan=False)
+    b.reserve_chunk(C)
+    chunk = {k: to_device(case[k]) for k in ("q", "k_new", "v_new", "rk_new", "rv_new")}
+    args = (case["lora_scale"], case["sm_scale"], case["theta"])
+    out = torch.empty_like(chunk["q"])
+    b.prefill(chunk, *args, out=out)
+    torch.cuda.synchronize()
+    eager, pool_b, pool_r = out.clone(), b.bcache.clone(), b.rcache.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.prefill(chunk, *args, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(rep + 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = (torch.equal(out, eager) and torch.equal(b.bcache, pool_b)
+                and torch.equal(b.rcache, pool_r))
+        print(f"[parity] prefill graph replay {rep}: bitwise equal={same}", flush=True)
+        assert same
