@@ -252,3 +252,48 @@ def test_decode_append_errors():
     with pytest.raises(fk.ForkKVError) as e:
         b.decode_append(rows, 1.0, 0.25, 1e4)
     assert e.value.code == fk.EINVAL
+
+
+@pytest.mark.parametrize("kernel,dtype,d,r", [(fk.KERNEL_GENERIC, "f32", 16, 4),
+                                              (fk.KERNEL_MFMA, "bf16", 128, 16)])
+def test_decode_append_graph_replay_matches_eager(kernel, dtype, d, r):
+    """A decode-with-append call captured in a HIP graph (the rows stored, then attended)
+    gives the eager call's output and pool bytes on every replay (three replays, with eager
+    work on the output between them)."""
+    rng = np.random.default_rng(990 + d)
+    n_agents, num_pages, Hq, Hkv = 5, 64, 8, 2
+    ops, agents = _fork_ops(rng, n_agents, int(rng.integers(20, 120)))
+    perm_b = rng.permutation(num_pages).astype(np.int32)
+    perm_r = rng.permutation(num_pages).astype(np.int32)
+    arrays = dict(bpool=encode(rng.standard_normal((num_pages, 2, Hkv, 16 * d)), dtype),
+                  rpool=encode(rng.standard_normal((num_pages, 2, 16 * r)), dtype),
+                  q=encode(rng.standard_normal((n_agents, Hq, d)), dtype),
+                  Bk=encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype),
+                  Bv=encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype))
+    rows = {k: to_device(encode(rng.standard_normal(shape), dtype)) for k, shape in
+            (("k_new", (n_agents, Hkv, d)), ("v_new", (n_agents, Hkv, d)),
+             ("rk_new", (n_agents, r)), ("rv_new", (n_agents, r)))}
+    geom = dict(num_bpages=num_pages, num_rpages=num_pages, num_kv_heads=Hkv, num_q_heads=Hq,
+                head_dim=d, rank=r, dtype=dtype)
+    b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
+    b.reserve_chunk(1)
+    b.make_plan(kernel)
+    assert b.plan.info["kernel"] == kernel
+    args = (2.0, 1.0 / np.sqrt(d), 5e5)
+    b.decode_append(rows, *args)
+    torch.cuda.synchronize()
+    eager, pool_b, pool_r = b.out.clone(), b.bcache.clone(), b.rcache.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.decode_append(rows, *args)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        b.out.fill_(rep + 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = (torch.equal(b.out, eager) and torch.equal(b.bcache, pool_b)
+                and torch.equal(b.rcache, pool_r))
+        print(f"[parity] decode-append graph replay {rep} kernel={kernel}: bitwise equal={same}",
+              flush=True)
+        assert same
