@@ -251,8 +251,9 @@ int forkkv_plan_decode(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t 
 int forkkv_plan_get_info(const forkkv_plan* plan, forkkv_plan_info* out);
 /* Copy the plan's integer blob (plan_bytes / 4 int32) to host memory, for inspection. */
 int forkkv_plan_export(const forkkv_plan* plan, int32_t* host_blob);
-/* Copy the plan blob to a caller-owned device buffer of plan_bytes (async on stream);
- * the plan remembers the buffer. */
+/* Copy the plan blob to a caller-owned device buffer of plan_bytes on stream and wait for
+ * the copy (the host blob is its source); the plan remembers the buffer.  Not for use
+ * inside a stream capture. */
 int forkkv_plan_upload(forkkv_plan* plan, void* dev_buf, hipStream_t stream);
 int forkkv_plan_destroy(forkkv_plan* plan);
 

@@ -9,9 +9,11 @@
  *
  * Output lines: "seq NAME LEN b0 .. b7 r0 .. r7" (tables, 8 pages), "cow SRC DST N" (every
  * copy-on-write row copy reported, in order), "plan ITEMS SLOTS BLOB_INTS", "blob i0 i1 ..",
+ * "err CASE CODE" (calls that must fail before any device work, with the code returned),
  * then "ok".  Any failing call prints "fail NAME CODE" and exits with 1. */
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "forkkv.h"
 
@@ -74,8 +76,35 @@ int main(void) {
   for (size_t i = 0; i < n_ints; ++i) printf(" %d", blob[i]);
   printf("\n");
   free(blob);
+  /* error paths that are decided before any device work */
+  {
+    forkkv_decode_args da;
+    memset(&da, 0, sizeof da);
+    printf("err decode_null %d\n", forkkv_residual_attn_decode(NULL, NULL));
+    da.pool = pool;
+    da.plan = plan;
+    printf("err decode_no_storage %d\n", forkkv_residual_attn_decode(&da, NULL));
+    forkkv_prefill_args pa;
+    memset(&pa, 0, sizeof pa);
+    printf("err prefill_null %d\n", forkkv_residual_attn_prefill(NULL, NULL));
+    pa.pool = pool;
+    pa.n_agents = 1;
+    pa.chunk_len = 1;
+    pa.num_q_heads = 4;
+    printf("err prefill_no_storage %d\n", forkkv_residual_attn_prefill(&pa, NULL));
+    printf("err upload_null %d\n", forkkv_plan_upload(plan, NULL, NULL));
+    forkkv_plan* bad = NULL;
+    printf("err plan_heads %d\n", forkkv_plan_decode(pool, a, 3, 3, NULL, &bad));
+    forkkv_seq c2;
+    printf("err fork_past_end %d\n", forkkv_fork(pool, a[2], 1000, &c2, &cow));
+    forkkv_pool_desc d8 = d;
+    forkkv_pool* p8 = NULL;
+    d8.page_size = 8;
+    printf("err page_size %d\n", forkkv_pool_create(&d8, NULL, NULL, &p8));
+  }
   CHECK(forkkv_plan_destroy(plan));
   for (int i = 0; i < 3; ++i) CHECK(forkkv_seq_free(pool, a[i]));
+  printf("err append_freed %d\n", forkkv_seq_append(pool, a[0], 1, NULL, NULL, &cow));
   CHECK(forkkv_seq_free(pool, root));
   forkkv_stats st;
   CHECK(forkkv_pool_stats(pool, &st));

@@ -82,3 +82,14 @@ def test_c_client_plan_matches_the_binding(client_output):
     assert int(head[1]) == plan.info["n_items"] and int(head[2]) == plan.info["n_slots"]
     assert int(head[3]) == got.size == want.size
     assert np.array_equal(got, want)
+
+
+def test_c_client_error_paths(client_output):
+    """Calls that the header says fail before any device work return the documented codes."""
+    from lora_shared_prefix_amd import forkkv as fk
+    got = {l.split()[1]: int(l.split()[2]) for l in client_output if l.startswith("err ")}
+    assert got == {"decode_null": fk.EINVAL, "decode_no_storage": fk.ESTATE,
+                   "prefill_null": fk.EINVAL, "prefill_no_storage": fk.ESTATE,
+                   "upload_null": fk.EINVAL, "plan_heads": fk.EINVAL,
+                   "fork_past_end": fk.EINVAL, "page_size": fk.EINVAL,
+                   "append_freed": fk.EINVAL}
