@@ -58,6 +58,12 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   if (kernel == FORKKV_KERNEL_MFMA) {
     if (!mfma_ok) return FORKKV_EUNSUPPORTED;
     cap = forkkv::mfma_group_agents(group_q);
+    // A full item's agent groups share the workgroup's four waves: keep their count a
+    // divisor of four (three agents per wave: items of six, not eight), so no wave idles.
+    const int per_wave = forkkv::mfma_agents_per_wave(group_q);
+    int groups = (cap + per_wave - 1) / per_wave;
+    while (4 % groups) --groups;
+    cap = std::min(cap, groups * per_wave);
   } else if (kernel == FORKKV_KERNEL_GENERIC) {
     cap = forkkv::generic_max_agents(group_q, g.head_dim, g.rank);
     if (cap < 1) return FORKKV_EUNSUPPORTED;

@@ -221,7 +221,12 @@ def test_plan_covers_workloads(name, kernel):
     # shared pages are read once per agent chunk, not once per agent
     blob = plan.blob()
     items = [blob[16 + i * ITEM_INTS: 16 + (i + 1) * ITEM_INTS] for i in range(blob[2])]
-    assert max(it[2] for it in items) == min(cfg.agents_per_session, 8)
+    cap = 8
+    if kernel == fk.KERNEL_MFMA:
+        # the largest item whose agent groups (A agents each) split four waves evenly
+        A = min(4, 16 // cfg.group)
+        cap = max(k * A for k in (1, 2, 4) if k * A <= 8)
+    assert max(it[2] for it in items) == min(cfg.agents_per_session, cap)
     if kernel == fk.KERNEL_MFMA:
         # four waves per item: agents in groups of A = min(4, 16 // G), pages split over the
         # remaining waves; no wave may get more than 64 pages, and the grid fits one round
