@@ -363,15 +363,26 @@ typedef struct {
   const int32_t* positions;      /* nullable: device [N][C], row positions (see above) */
   const int32_t* positions_host; /* host [N][C], same values; required with positions */
   const int32_t* pstart;         /* nullable: device [N][max_pages] page start positions, for
-                                    sequences holding a frozen tail (the slot map); such calls
-                                    run the generic attention kernel */
+                                    sequences holding a frozen tail (the slot map) */
+  int32_t kernel;                /* FORKKV_KERNEL_*: 0 = auto (the MFMA kernel where it covers
+                                    the shape: bf16, d = 128, r = 16, G <= 16); GENERIC runs
+                                    the generic kernel; MFMA returns FORKKV_EUNSUPPORTED for a
+                                    shape it does not cover */
 } forkkv_prefill_args;
 
-/* Errors: FORKKV_EINVAL for null pointers, C < 1, a head count that is not a multiple of
- * Hkv, rows outside the tables, positions that do not strictly increase, or scales out of
- * range;
- * FORKKV_EUNSUPPORTED for a shape no kernel covers; FORKKV_ESTATE when the pool has no
- * device storage; FORKKV_EHIP when a launch fails. */
+/* Missing pages.  A base table entry of -1 (a page evicted with forkkv_evict_bpages and not
+ * yet refilled) holds no keys: no query attends to its positions, and chunk rows that fall
+ * on it are not stored.  A residual table entry of -1 (a sequence without residual pages,
+ * such as a base-only snapshot) reads as zero residual rows (the key and value are the base
+ * rows alone), and chunk residual rows that fall on it are not stored.  Both kernels follow
+ * this rule.
+ *
+ * Errors: FORKKV_EINVAL for null pointers, C < 1, a head count that is not a multiple of
+ * Hkv, rows outside the tables, positions that do not strictly increase, scales out of
+ * range, or an unknown kernel;
+ * FORKKV_EUNSUPPORTED for a shape no kernel covers (or the MFMA kernel asked for a shape
+ * it does not cover); FORKKV_ESTATE when the pool has no device storage; FORKKV_EHIP when a
+ * launch fails. */
 
 int forkkv_residual_attn_prefill(const forkkv_prefill_args* args, hipStream_t stream);
 

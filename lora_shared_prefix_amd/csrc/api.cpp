@@ -246,6 +246,9 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   if (!finite(a->lora_scale) || !finite(a->sm_scale) || !(a->sm_scale > 0.f) ||
       !(a->rope_theta > 0.f) || !finite(a->rope_theta))
     return FORKKV_EINVAL;
+  if (a->kernel != FORKKV_KERNEL_AUTO && a->kernel != FORKKV_KERNEL_GENERIC &&
+      a->kernel != FORKKV_KERNEL_MFMA)
+    return FORKKV_EINVAL;
   const int64_t cap = int64_t(a->max_pages) * kPage;
   for (int32_t i = 0; i < a->n_agents; ++i) {
     if (listed) {
@@ -292,11 +295,13 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   if (p.group > forkkv::kGenericMaxRows || forkkv::generic_max_agents(p.group, p.head_dim, p.rank) < 1)
     return FORKKV_EUNSUPPORTED;
 
+  // (the MFMA prefill kernel assumes pages at multiples of P: a slot map runs the generic one)
+  const bool mfma_ok = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, p.group) &&
+                       forkkv::prefill_mfma_enabled() && !a->pstart;
+  if (a->kernel == FORKKV_KERNEL_MFMA && !mfma_ok) return FORKKV_EUNSUPPORTED;
+  const bool mfma = mfma_ok && a->kernel != FORKKV_KERNEL_GENERIC;
   (void)hipGetLastError();
   if (forkkv::launch_prefill_write(p, g.dtype, stream) != hipSuccess) return FORKKV_EHIP;
-  // (the MFMA prefill kernel assumes pages at multiples of P: a slot map runs the generic one)
-  const bool mfma = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, p.group) &&
-                    forkkv::prefill_mfma_enabled() && !a->pstart;
   hipError_t err = mfma ? forkkv::launch_prefill_mfma(p, a->start_pos_host, stream)
                         : forkkv::launch_prefill_generic(p, g.dtype, stream);
   if (err != hipSuccess) return FORKKV_EHIP;

@@ -249,7 +249,6 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
           qoff = (size_t(agents[j]) * Hq + h * G + g) * d;
           valid = t < prow[j];
         }
-        valid = valid && rok[j];
         float sc = -INFINITY;
         if (valid) {
           float dot = 0.f;

@@ -745,6 +745,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // feeds one K = 32 MFMA (8 bytes of page 0, then 8 of page 1)
   __shared__ __align__(16) uint4 s_v[2][8 * 64];
   __shared__ __align__(16) uint4 s_rv[2][64];         // [buf][lane], same page halves
+  __shared__ int s_miss[2][2];                          // [buf][page]: base page missing
   const int Hkv = p.num_kv_heads, G = p.group, Hq = p.num_q_heads, C = p.chunk_len;
   // the workgroups of one KV head share an XCD (block ids are dealt round robin over the
   // 8 XCDs), so the shared prefix of that head streams through one L2
@@ -831,24 +832,29 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     uint2 rk;     // key-residual B operand of page pg
     uint4 v;      // quarter tp of page pg's value tile (operand pieces of lanes 2l, 2l+1)
     uint2 rv;     // value-residual operand of page pg (staged by the tp == 0 waves)
+    bool miss;    // page pg's base page is missing (evicted): its keys take no part
   };
   // Page ids: lane i holds the ids of this wave's page at iteration 64 k + i (block k),
-  // checked against the pools once here; a page's ids then come from a readlane.
-  int ids_b = 0, ids_r = 0;
+  // checked against the pools once here (a missing or out-of-pool page is -1); a page's ids
+  // then come from a readlane.  A missing base page is read from page 0 (any in-pool page)
+  // and then masked; a missing residual page reads the zero page.
+  int ids_b = -1, ids_r = -1;
   auto fetch_ids = [&](int blk) {
     const int lp = min(2 * (64 * blk + lane) + pg, lp_end - 1);
     const int bp = p.btab[size_t(a) * p.max_pages + lp];
     const int rp = p.rtab[size_t(a) * p.max_pages + lp];
-    ids_b = (bp >= 0 && bp < p.num_bpages) ? bp : 0;
-    ids_r = (rp >= 0 && rp < p.num_rpages) ? rp : 0;
+    ids_b = (bp >= 0 && bp < p.num_bpages) ? bp : -1;
+    ids_r = (rp >= 0 && rp < p.num_rpages) ? rp : -1;
   };
   auto load = [&](int it, PfBuf& B) {
     if ((it & 63) == 0) fetch_ids(it >> 6);  // wave-uniform
-    const size_t pb = __builtin_amdgcn_readlane(ids_b, it & 63);
-    const size_t pr = __builtin_amdgcn_readlane(ids_r, it & 63);
+    const int ib = __builtin_amdgcn_readlane(ids_b, it & 63);
+    const int ir = __builtin_amdgcn_readlane(ids_r, it & 63);
+    B.miss = ib < 0;
+    const size_t pb = max(ib, 0);
     const uint16_t* kt = bcache + (pb * 2 * Hkv + h) * tile;
     const uint16_t* vt = bcache + (pb * 2 * Hkv + Hkv + h) * tile;
-    const uint16_t* rb_ = rcache + pr * 2 * kPage * kR;
+    const uint16_t* rb_ = ir >= 0 ? rcache + size_t(ir) * 2 * kPage * kR : g_zero_res;
     for (int u = 0; u < 2; ++u) {
       // dims perm_dim(T, 4 g4 + i), i = 0..3: 4 consecutive dims of one 8-dim block
       const int x0 = perm_dim(tp + 4 * u, 4 * g4);
@@ -909,10 +915,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // arbitrary bytes (even NaN); a zero probability times NaN is NaN, so they are zeroed.
     // The 16 bytes this lane stages are the operand pieces of reader lanes 2l and 2l+1
     // (tokens 4 g .. 4 g + 3, g = ((2l) mod 64) / 16); its value-residual piece is its own.
-    const int last = lp < lp_end ? end_pos - lp * kPage : 0;
+    const int last = (lp < lp_end && !B.miss) ? end_pos - lp * kPage : 0;
     uint4 v = B.v;
     uint2 rv = B.rv;
-    if (last < kPage) {  // wave-uniform: only the pages at the end of the sequence
+    if (last < kPage) {  // wave-uniform: the pages at the end of the sequence, missing pages
       const int tvv = last - 4 * (((2 * lane) & 63) >> 4);
       m2(tvv, v.x, v.y);
       m2(tvv, v.z, v.w);
@@ -926,7 +932,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       sv[2 * slot + pg] = make_uint2(v.x, v.y);
       sv[2 * (slot + 1) + pg] = make_uint2(v.z, v.w);
     }
-    if (tp == 0) reinterpret_cast<uint2*>(&s_rv[buf][0])[2 * lane + pg] = rv;
+    if (tp == 0) {
+      reinterpret_cast<uint2*>(&s_rv[buf][0])[2 * lane + pg] = rv;
+      if (lane == 0) s_miss[buf][pg] = B.miss;
+    }
   };
 
   auto compute = [&](int it) {
@@ -950,7 +959,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // precedes every query):
     // no mask at all.  Rows past the chunk have zero q and are never written, so they need
     // none either.  (Wave-uniform.)
-    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < first_pos;
+    const bool miss[2] = {s_miss[buf][0] != 0, s_miss[buf][1] != 0};  // wave-uniform
+    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < first_pos &&
+                          !miss[0] && !miss[1];
     for (int rt = 0; rt < 2; ++rt) {
       // raw scores (q.k); the softmax scale (> 0, log2 units) is applied inside the exp
       float sc[8], pmax = -INFINITY;
@@ -960,7 +971,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       } else {
         for (int pgi = 0; pgi < 2; ++pgi) {
           const int lp = 2 * it + pgi;
-          const int lim = lp < lp_end ? qpos[rt] - lp * kPage - 4 * g4 : -1;  // keys i <= lim
+          const int lim = (lp < lp_end && !miss[pgi]) ? qpos[rt] - lp * kPage - 4 * g4 : -1;
           for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[rt][pgi][i] : -INFINITY;
         }
       }

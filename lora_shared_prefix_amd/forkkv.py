@@ -73,7 +73,7 @@ class PrefillArgs(C.Structure):
                 ("rtab", C.c_void_p), ("max_pages", C.c_int32), ("start_pos", C.c_void_p),
                 ("start_pos_host", _i32p), ("lora_scale", C.c_float), ("sm_scale", C.c_float),
                 ("rope_theta", C.c_float), ("out", C.c_void_p), ("positions", C.c_void_p),
-                ("positions_host", _i32p), ("pstart", C.c_void_p)]
+                ("positions_host", _i32p), ("pstart", C.c_void_p), ("kernel", C.c_int32)]
 
 
 class WriteArgs(C.Structure):
@@ -401,10 +401,12 @@ def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, o
 
 def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, btab, rtab,
                           start_pos, start_pos_host, out, lora_scale, sm_scale, rope_theta,
-                          stream=None, positions=None, positions_host=None, pstart=None):
+                          stream=None, positions=None, positions_host=None, pstart=None,
+                          kernel=KERNEL_AUTO):
     """Launch prefill (async): store the rows, then attend causally.  Rows sit at
     start_pos[a] + i, or at positions[a][i] when a position list (device int32 [N][C] plus
-    the same values on the host) is given."""
+    the same values on the host) is given.  kernel: KERNEL_AUTO, KERNEL_GENERIC or
+    KERNEL_MFMA."""
     N, Cn, Hq = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     sp = _i32_array(start_pos_host) if start_pos_host is not None else None
     ph = (_i32_array([int(x) for row in positions_host for x in row])
@@ -416,7 +418,8 @@ def residual_attn_prefill(pool: Pool, q, k_new, v_new, rk_new, rv_new, Bk, Bv, b
                        C.cast(sp, _i32p) if sp is not None else None, float(lora_scale),
                        float(sm_scale), float(rope_theta), out.data_ptr(),
                        positions.data_ptr() if positions is not None else None,
-                       C.cast(ph, _i32p) if ph is not None else None, _ptr(pstart))
+                       C.cast(ph, _i32p) if ph is not None else None, _ptr(pstart),
+                       int(kernel))
     _check(lib().forkkv_residual_attn_prefill(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_prefill")
 

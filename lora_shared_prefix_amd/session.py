@@ -108,14 +108,16 @@ class DeviceBatch:
         self.start_dev = torch.tensor(self.start, dtype=torch.int32, device=self.device)
         return self.start
 
-    def prefill(self, chunk, lora_scale, sm_scale, rope_theta, stream=None, out=None):
+    def prefill(self, chunk, lora_scale, sm_scale, rope_theta, stream=None, out=None,
+                kernel=fk.KERNEL_AUTO):
         """chunk: dict of device tensors q, k_new, v_new, rk_new, rv_new."""
         if out is None:
             out = torch.empty_like(chunk["q"])
         fk.residual_attn_prefill(self.pool, chunk["q"], chunk["k_new"], chunk["v_new"],
                                  chunk["rk_new"], chunk["rv_new"], self.Bk, self.Bv, self.btab,
                                  self.rtab, self.start_dev, self.start, out, lora_scale,
-                                 sm_scale, rope_theta, stream, pstart=self.pstart)
+                                 sm_scale, rope_theta, stream, pstart=self.pstart,
+                                 kernel=kernel)
         return out
 
 

@@ -20,7 +20,7 @@ import numpy as np
 from .rope import rope_rotate, rope_unrotate
 from .storage import (base_key_rows, base_value_rows, decode_values, key_offset,
                       res_key_offset, res_key_rows, res_value_offset, res_value_rows,
-                      value_offset)
+                      table_pages, value_offset)
 
 
 class Geometry:
@@ -37,12 +37,23 @@ class Geometry:
 
 
 def _cached_rows(geo, bpool, rpool, btab, rtab, a, h, positions, starts=None):
+    """Stored rows of agent a, KV head h at the given positions, and which positions are keys.
+
+    Missing pages (table entry -1; ForkKV study note, "Error / eviction recovery"): a
+    position whose base page was evicted holds no key until it is refilled, so it takes no
+    part in attention (``present`` is False there); a position without a residual page (a
+    sequence that has none, such as a base-only snapshot) has a zero residual.
+    """
     st = None if starts is None else starts[a]
     bk = base_key_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype, st)
     bv = base_value_rows(bpool, btab[a], positions, h, geo.P, geo.d, geo.dtype, st)
     rk = res_key_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype, st)
     rv = res_value_rows(rpool, rtab[a], positions, geo.P, geo.r, geo.dtype, st)
-    return bk, bv, rk, rv
+    present = table_pages(btab[a], positions, geo.P, st) >= 0
+    no_res = table_pages(rtab[a], positions, geo.P, st) < 0
+    rk[no_res] = 0.0
+    rv[no_res] = 0.0
+    return bk, bv, rk, rv, present
 
 
 def merged_kv(geo, bk, bv, rk, rv, Bk_a, Bv_a, h, positions, lora_scale, theta):
@@ -88,9 +99,14 @@ def decode_attention(geo, bpool, rpool, btab, rtab, seq_lens, q, Bk, Bv, lora_sc
             if L == 0:
                 out[a, list(gs)] = 0.0
                 continue
-            bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, pos, starts)
+            bk, bv, rk, rv, present = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, pos,
+                                                   starts)
             k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
+            k, v = k[present], v[present]
             for g in gs:
+                if len(k) == 0:
+                    out[a, g] = 0.0
+                    continue
                 p = _softmax_rows(sm_scale * (k @ qv[a, g]))
                 out[a, g] = p @ v
     return out
@@ -112,7 +128,7 @@ def apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_
     Row i of agent a goes to position ``positions[a][i]``: page ``table[a][pos // P]``,
     row ``pos % P`` (under a slot map: the page whose start is the last one <= pos, row
     pos - start), laid out as the pool layout says.  With ``rk_new`` None only the base
-    pool is written.
+    pool is written.  A row whose page is missing (table entry -1) is not stored.
     """
     bp, rp = bpool.copy(), rpool.copy()
     N, C = k_new.shape[0], k_new.shape[1]
@@ -123,11 +139,11 @@ def apply_rows_write(geo, bpool, rpool, btab, rtab, positions, k_new, v_new, rk_
             t = int(positions[a][i])
             lp, row = _slot(geo, starts, a, t)
             page = int(btab[a][lp])
-            for h in range(geo.Hkv):
+            for h in range(geo.Hkv if page >= 0 else 0):
                 bp[page, 0, h, key_offset(row, dims)] = k_new[a, i, h]
                 bp[page, 1, h, value_offset(row, dims)] = v_new[a, i, h]
-            if rk_new is not None:
-                page = int(rtab[a][lp])
+            page = int(rtab[a][lp]) if rk_new is not None else -1
+            if page >= 0:
                 rp[page, 0, res_key_offset(row, ranks)] = rk_new[a, i]
                 rp[page, 1, res_value_offset(row, ranks, r)] = rv_new[a, i]
     return bp, rp
@@ -173,17 +189,22 @@ def prefill_attention(geo, bpool, rpool, btab, rtab, start_pos, q, k_new, v_new,
         last = start + max(i for i, _ in rows)
         pos = np.arange(last + 1, dtype=np.int64)
         old = pos[pos < start]
-        bk, bv, rk, rv = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, old)
+        bk, bv, rk, rv, present = _cached_rows(geo, bpool, rpool, btab, rtab, a, h, old)
         n_new = last + 1 - start
+        present = np.concatenate([present, table_pages(btab[a], pos[start:], geo.P) >= 0])
+        no_res = np.concatenate([np.zeros(len(old), bool),
+                                 table_pages(rtab[a], pos[start:], geo.P) < 0])
         bk = np.concatenate([bk, decode_values(k_new[a, :n_new, h], geo.dtype)])
         bv = np.concatenate([bv, decode_values(v_new[a, :n_new, h], geo.dtype)])
         rk = np.concatenate([rk, decode_values(rk_new[a, :n_new], geo.dtype)])
         rv = np.concatenate([rv, decode_values(rv_new[a, :n_new], geo.dtype)])
+        rk[no_res] = 0.0  # a chunk row without a residual page has no residual to store
+        rv[no_res] = 0.0
         k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
         for i, g in rows:
-            n_keys = start + i + 1
-            p = _softmax_rows(sm_scale * (k[:n_keys] @ qv[a, i, g]))
-            out[a, i, g] = p @ v[:n_keys]
+            sel = present[:start + i + 1]
+            p = _softmax_rows(sm_scale * (k[:start + i + 1][sel] @ qv[a, i, g]))
+            out[a, i, g] = p @ v[:start + i + 1][sel]
     return out
 
 
@@ -215,10 +236,11 @@ def prefill_attention_at(geo, bpool, rpool, btab, rtab, positions, q, k_new, v_n
     for (a, h), rows in sorted(want.items()):
         last = max(int(positions[a][i]) for i, _ in rows)
         pos = np.arange(last + 1, dtype=np.int64)
-        bk, bv, rk, rv = _cached_rows(geo, bp, rp, btab, rtab, a, h, pos, starts)
+        bk, bv, rk, rv, present = _cached_rows(geo, bp, rp, btab, rtab, a, h, pos, starts)
         k, v = merged_kv(geo, bk, bv, rk, rv, Bkv[a], Bvv[a], h, pos, lora_scale, theta)
         for i, g in rows:
             n_keys = int(positions[a][i]) + 1
-            p = _softmax_rows(sm_scale * (k[:n_keys] @ qv[a, i, g]))
-            out[a, i, g] = p @ v[:n_keys]
+            sel = present[:n_keys]
+            p = _softmax_rows(sm_scale * (k[:n_keys][sel] @ qv[a, i, g]))
+            out[a, i, g] = p @ v[:n_keys][sel]
     return out

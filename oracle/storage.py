@@ -57,29 +57,40 @@ def _pages_rows(tab_row: np.ndarray, positions: np.ndarray, P_: int, starts_row=
     return np.asarray(tab_row)[lp].astype(np.int64), (positions - st[lp]).astype(np.int64)
 
 
+def table_pages(tab_row, positions, P_, starts_row=None):
+    """Table entry (physical page, or -1 for a missing page) of each position."""
+    return _pages_rows(tab_row, positions, P_, starts_row)[0]
+
+
+def _readable(pages_rows):
+    """Missing pages (-1) are read as page 0 here; callers discard or zero those rows."""
+    pages, rows = pages_rows
+    return np.maximum(pages, 0), rows
+
+
 def base_key_rows(bpool, btab_row, positions, head, P_, d, dtype, starts_row=None):
     """Stored (post-RoPE) base keys of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P_, starts_row)
+    pages, rows = _readable(_pages_rows(btab_row, positions, P_, starts_row))
     idx = key_offset(rows[:, None], np.arange(d)[None, :])
     return decode_values(bpool[:, 0, head, :][pages[:, None], idx], dtype)
 
 
 def base_value_rows(bpool, btab_row, positions, head, P_, d, dtype, starts_row=None):
     """Base values of one KV head at the given positions -> [L, d]."""
-    pages, rows = _pages_rows(btab_row, positions, P_, starts_row)
+    pages, rows = _readable(_pages_rows(btab_row, positions, P_, starts_row))
     idx = value_offset(rows[:, None], np.arange(d)[None, :])
     return decode_values(bpool[:, 1, head, :][pages[:, None], idx], dtype)
 
 
 def res_key_rows(rpool, rtab_row, positions, P_, r, dtype, starts_row=None):
     """Rank-r key residuals (no RoPE) at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P_, starts_row)
+    pages, rows = _readable(_pages_rows(rtab_row, positions, P_, starts_row))
     idx = res_key_offset(rows[:, None], np.arange(r)[None, :])
     return decode_values(rpool[:, 0, :][pages[:, None], idx], dtype)
 
 
 def res_value_rows(rpool, rtab_row, positions, P_, r, dtype, starts_row=None):
     """Rank-r value residuals at the given positions -> [L, r]."""
-    pages, rows = _pages_rows(rtab_row, positions, P_, starts_row)
+    pages, rows = _readable(_pages_rows(rtab_row, positions, P_, starts_row))
     idx = res_value_offset(rows[:, None], np.arange(r)[None, :], r)
     return decode_values(rpool[:, 1, :][pages[:, None], idx], dtype)

@@ -37,18 +37,28 @@ def _slot_of(P, starts_a, t):
 
 def _key_value(P, d, r, dtype, bpool, rpool, btab_a, rtab_a, Bk_a, Bv_a, h, t, s, theta,
                row_override=None, starts_a=None):
-    """Merged key and value of one agent/head at position t (lists of d floats)."""
+    """Merged key and value of one agent/head at position t (lists of d floats), or None
+    when the position's base page is missing (-1: evicted, so no key there).  A missing
+    residual page contributes nothing (zero residual rows)."""
+    lp, row = _slot_of(P, starts_a, t)
+    if btab_a[lp] < 0:
+        return None
     if row_override is not None:
         bk, bv, rk, rv = row_override
+        if rtab_a[lp] < 0:  # the row's residual cannot be stored: zero residual
+            rk, rv = [0.0] * r, [0.0] * r
     else:
-        lp, row = _slot_of(P, starts_a, t)
         bp, rp = btab_a[lp], rtab_a[lp]
         # tiles are stored in matrix-core operand order (see include/forkkv.h)
         bk = [_val(bpool[bp][0][h][(j // 8) * 128 + row * 8 + j % 8], dtype) for j in range(d)]
         bv = [_val(bpool[bp][1][h][((j // 16) * 4 + row // 4) * 64 + (j % 16) * 4 + row % 4],
                    dtype) for j in range(d)]
-        rk = [_val(rpool[rp][0][(k // 4) * 64 + row * 4 + k % 4], dtype) for k in range(r)]
-        rv = [_val(rpool[rp][1][(row // 4) * 4 * r + k * 4 + row % 4], dtype) for k in range(r)]
+        if rp < 0:
+            rk, rv = [0.0] * r, [0.0] * r
+        else:
+            rk = [_val(rpool[rp][0][(k // 4) * 64 + row * 4 + k % 4], dtype) for k in range(r)]
+            rv = [_val(rpool[rp][1][(row // 4) * 4 * r + k * 4 + row % 4], dtype)
+                  for k in range(r)]
     half = d // 2
     key = [0.0] * d
     for j in range(half):
@@ -68,6 +78,7 @@ def _key_value(P, d, r, dtype, bpool, rpool, btab_a, rtab_a, Bk_a, Bv_a, h, t, s
 
 
 def _attend(qrow, kv, sm_scale, d):
+    kv = [x for x in kv if x is not None]
     if not kv:
         return [0.0] * d
     scores = [sm_scale * sum(qrow[j] * k[j] for j in range(d)) for k, _ in kv]

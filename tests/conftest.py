@@ -1,6 +1,8 @@
 import os
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -8,3 +10,23 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _nan_workspace(request, monkeypatch):
+    """GPU tests: every split-K workspace a plan hands out starts as all-ones bytes (a NaN in
+    every fp32 word), so a combine that read a partial slot no workgroup wrote would put NaN
+    into the output and fail the test."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    from lora_shared_prefix_amd import forkkv as fk
+    original = fk.Plan.workspace
+
+    def poisoned(self):
+        ws = original(self)
+        ws.fill_(0xFF)
+        return ws
+
+    monkeypatch.setattr(fk.Plan, "workspace", poisoned)
+    yield

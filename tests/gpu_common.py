@@ -96,3 +96,19 @@ def poison_unused(bpool, rpool, used_b, used_r, dtype, d, r):
                 rp[page, 0, res_key_offset(row, ranks)] = nan
                 rp[page, 1, res_value_offset(row, ranks, r)] = nan
     return bp, rp
+
+
+def model_replay(num_bpages, num_rpages, perm_b, perm_r, ops):
+    """Replay a pool script on the oracle's model; returns (model, names, cow row copies)."""
+    pm = PoolModel(num_bpages, num_rpages, 16, perm_b, perm_r)
+    names, cows = {}, []
+    for op in ops:
+        if op[0] == "create":
+            names[op[1]] = pm.create(bool(op[2]))
+        elif op[0] == "append":
+            c = pm.append(names[op[1]], op[2])[2]
+            cows += [c] if c else []
+        else:
+            names[op[3]], c = pm.fork(names[op[1]], op[2], *op[4:])
+            cows += [c] if c else []
+    return pm, names, cows

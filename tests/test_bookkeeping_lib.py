@@ -179,6 +179,19 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
                 covered[(a, lpg)] = i
     want = {(a, lpg) for a in range(n_agents) for lpg in range(-(-lens[a] // 16))}
     assert set(covered) == want
+    # read once: a physical base page held by n agents of the batch is streamed by exactly
+    # ceil(n / cap) items (one per chunk of at most cap agents), per KV head -- a planner that
+    # split the agents sharing a page any further would pass the coverage checks above and
+    # show only as extra HBM traffic
+    cap = blob[11]
+    assert 1 <= cap <= group_cap
+    holders, items_of = {}, {}
+    for (a, lpg), i in covered.items():
+        page = bt[a][lpg]
+        holders.setdefault(page, set()).add(a)
+        items_of.setdefault(page, set()).add(i)
+    for page, hs_ in holders.items():
+        assert len(items_of[page]) == -(-len(hs_) // cap), (page, len(hs_), cap)
     # decode with append: item bit j marks agent j's last page; the append section holds the
     # base and residual slot (page * 16 + row) of every agent's last row
     off_app = blob[12]
@@ -217,7 +230,6 @@ def test_plan_covers_workloads(name, kernel):
     hs = [names[a] for a in agents]
     plan = fk.Plan(lp, hs, cfg.num_q_heads, kernel=kernel)
     mp = -(-cfg.seq_len // 16)
-    _check_plan(lp, lp.tables(hs, mp), hs, plan, 8)
     # shared pages are read once per agent chunk, not once per agent
     blob = plan.blob()
     items = [blob[16 + i * ITEM_INTS: 16 + (i + 1) * ITEM_INTS] for i in range(blob[2])]
@@ -226,6 +238,8 @@ def test_plan_covers_workloads(name, kernel):
         # the largest item whose agent groups (A agents each) split four waves evenly
         A = min(4, 16 // cfg.group)
         cap = max(k * A for k in (1, 2, 4) if k * A <= 8)
+    assert blob[11] == cap
+    _check_plan(lp, lp.tables(hs, mp), hs, plan, cap)
     assert max(it[2] for it in items) == min(cfg.agents_per_session, cap)
     if kernel == fk.KERNEL_MFMA:
         # four waves per item: agents in groups of A = min(4, 16 // G), pages split over the

@@ -111,18 +111,25 @@ def test_bf16_workloads(kernel, name, agents, heads):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_residual_delta(kernel):
-    """The adapter's contribution itself must match, not only the (base-dominated) output."""
-    cfg = config_by_name("llama3_8b_react_decode")
+@pytest.mark.parametrize("name,agents,heads", [
+    ("llama3_8b_react_decode", None, None),
+    ("llama3_8b_mapreduce_decode", None, [0, 3, 7]),
+    ("qwen25_14b_batched_decode", [0, 9, 18, 31], [0, 5]),
+])
+def test_residual_delta(kernel, name, agents, heads):
+    """The adapter's contribution itself must match, not only the (base-dominated) output:
+    (output with B) - (output with B = 0) against the oracle's same difference, normwise
+    within 5e-2, on every decode workload (sampled agents and heads as above)."""
+    cfg = config_by_name(name)
     if not _kernel_available(cfg.dtype, cfg.head_dim, cfg.rank, cfg.group, kernel):
         pytest.skip("kernel does not cover this shape")
-    _, gB, rB, _ = _run_workload("llama3_8b_react_decode", kernel)
-    x = _CACHE["llama3_8b_react_decode"][1]
+    _, gB, rB, mask = _run_workload(name, kernel, agents, heads)
+    x = _CACHE[name][1]
     zero = {"Bk": np.zeros_like(x["Bk"]), "Bv": np.zeros_like(x["Bv"])}
-    _, g0, r0, _ = _run_workload("llama3_8b_react_decode", kernel, arrays=zero)
-    dg, dr = gB - g0, rB - r0
+    _, g0, r0, _ = _run_workload(name, kernel, agents, heads, arrays=zero)
+    dg, dr = (gB - g0)[mask], (rB - r0)[mask]
     rel = np.linalg.norm(dg - dr) / np.linalg.norm(dr)
-    print(f"[parity] residual delta rel={rel:.3e}", flush=True)
+    print(f"[parity] {name} residual delta rel={rel:.3e}", flush=True)
     assert rel <= 5e-2
 
 

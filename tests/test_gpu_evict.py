@@ -21,10 +21,12 @@ if not torch.cuda.is_available():
 
 from lora_shared_prefix_amd import forkkv as fk  # noqa: E402
 from lora_shared_prefix_amd.session import DeviceBatch, to_device  # noqa: E402
-from oracle.attention import Geometry, decode_attention  # noqa: E402
+from oracle.attention import (Geometry, apply_chunk_write, decode_attention,  # noqa: E402
+                              prefill_attention)
 from oracle.storage import key_offset, value_offset  # noqa: E402
 from tests.cases import encode  # noqa: E402
-from tests.gpu_common import assert_close, gpu_values  # noqa: E402
+from tests.gpu_common import (apply_cows_host, assert_close, gpu_values,  # noqa: E402
+                              model_replay)
 
 
 def _rows_of(bpool, pages, Hkv, d):
@@ -128,3 +130,63 @@ def test_write_rows_errors():
         fk.write_rows(b.pool, b.btab, b.rtab, torch.tensor([[1, 2]], dtype=torch.int32).cuda(),
                       [[1, 2]], k, k, rk_new=torch.zeros((1, 2, 4), device="cuda"))
     assert e.value.code == fk.EINVAL
+
+
+@pytest.mark.parametrize("kernel", [fk.KERNEL_MFMA, fk.KERNEL_GENERIC])
+def test_prefill_over_missing_pages(kernel):
+    """Prefill over a partial hit: one shared trunk page evicted from every holder (no key
+    there until a refill), and the base-only trunk itself in the batch (no residual pages: a
+    zero residual, its chunk's residual rows not stored).  Both prefill kernels follow the
+    oracle's rule, each against the oracle, every output row."""
+    rng = np.random.default_rng(71)
+    d, r, Hq, Hkv, C = 128, 16, 8, 2, 40
+    L0, npg, nrp = 16 * 30 + 5, 96, 128
+    agents = ["a0", "a1", "t"]
+    ops = [("create", "t", 0), ("append", "t", L0), ("fork", "t", 16 * 30, "a0"),
+           ("fork", "t", L0, "a1"), ("append", "a0", 7)]
+    perm_b = rng.permutation(npg).astype(np.int32)
+    perm_r = rng.permutation(nrp).astype(np.int32)
+    N = len(agents)
+    arrays = dict(bpool=encode(rng.standard_normal((npg, 2, Hkv, 16 * d)), "bf16"),
+                  rpool=encode(rng.standard_normal((nrp, 2, 16 * r)), "bf16"),
+                  Bk=encode(0.3 * rng.standard_normal((N, r, Hkv * d)), "bf16"),
+                  Bv=encode(0.3 * rng.standard_normal((N, r, Hkv * d)), "bf16"),
+                  q=encode(rng.standard_normal((N, C, Hq, d)), "bf16"),
+                  k_new=encode(rng.standard_normal((N, C, Hkv, d)), "bf16"),
+                  v_new=encode(rng.standard_normal((N, C, Hkv, d)), "bf16"),
+                  rk_new=encode(rng.standard_normal((N, C, r)), "bf16"),
+                  rv_new=encode(rng.standard_normal((N, C, r)), "bf16"))
+    geom = dict(num_bpages=npg, num_rpages=nrp, num_kv_heads=Hkv, num_q_heads=Hq, head_dim=d,
+                rank=r, dtype="bf16")
+    print(f"[gpu-evict] prefill over missing pages kernel={kernel}", flush=True)
+    b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
+    start = b.reserve_chunk(C)
+    # evict the trunk's page 3 (shared by a0, a1 and the trunk), then re-export the tables
+    victim = int(b.btab_host[2][3])
+    b.pool.evict_base([victim])
+    b.refresh_tables()
+    assert b.btab_host[0][3] == -1 and b.btab_host[1][3] == -1 and b.btab_host[2][3] == -1
+    assert np.all(b.rtab_host[2] == -1)
+    chunk = {k: to_device(arrays[k]) for k in ("q", "k_new", "v_new", "rk_new", "rv_new")}
+    out = b.prefill(chunk, 2.0, 1 / np.sqrt(d), 1e6, kernel=kernel)
+    torch.cuda.synchronize()
+    # oracle side: the model's tables after the same script, chunk appends and eviction
+    pm, names, cows = model_replay(npg, nrp, perm_b, perm_r,
+                                   ops + [("append", a, C) for a in agents])
+    pm.evict_base([victim])
+    hs = [names[a] for a in agents]
+    bt, rt, _ = (np.array(x) for x in pm.tables(hs, b.max_pages))
+    assert np.array_equal(bt, b.btab_host) and np.array_equal(rt, b.rtab_host)
+    host_b = apply_cows_host(arrays["bpool"], cows, Hkv, d)
+    g = Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, rank=r,
+                 dtype="bf16")
+    ref = prefill_attention(g, host_b, arrays["rpool"], bt, rt, np.array(start), arrays["q"],
+                            arrays["k_new"], arrays["v_new"], arrays["rk_new"], arrays["rv_new"],
+                            arrays["Bk"], arrays["Bv"], 2.0, 1 / np.sqrt(d), 1e6)
+    assert_close(gpu_values(out, "bf16"), ref, f"prefill over missing pages kernel={kernel}",
+                 scale_abs=True)
+    # rows on the evicted page are absent; the pool's other bytes are as the write leaves them
+    exp_b, exp_r = apply_chunk_write(g, host_b, arrays["rpool"], bt, rt, start, arrays["k_new"],
+                                     arrays["v_new"], arrays["rk_new"], arrays["rv_new"])
+    assert np.array_equal(b.bcache.cpu().numpy().view(np.uint16), exp_b)
+    assert np.array_equal(b.rcache.cpu().numpy().view(np.uint16), exp_r)

@@ -22,11 +22,14 @@ def _host(t, dtype):
     return a.view(np.uint16) if dtype == "bf16" else a
 
 
-def _run(geom, arrays, ops, agents, perm_b, perm_r, C, s, sm, theta, samples=None):
+def _run(geom, arrays, ops, agents, perm_b, perm_r, C, s, sm, theta, samples=None,
+         keep=None):
     b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
     pool_before = (arrays["bpool"], arrays["rpool"])
     start = b.reserve_chunk(C)
     chunk = {k: to_device(arrays[k]) for k in ("q", "k_new", "v_new", "rk_new", "rv_new")}
+    if keep is not None:
+        keep["chunk"] = chunk
     out = b.prefill(chunk, s, sm, theta)
     torch.cuda.synchronize()
     dtype = geom["dtype"]
@@ -130,17 +133,20 @@ def test_qwen3_8b_chunked_prefill_workload():
     131072-token shared prefix.
 
     Written rows are checked bit for bit at sampled slots; attention is checked on sampled
-    (agent, query, head) rows the oracle computes one by one.
+    (agent, query, head) rows the oracle computes one by one, and so is the adapter's own
+    contribution: a second call on the same batch with B = 0 (it stores the same rows again),
+    (output with B) - (output with B = 0) against the oracle's difference, normwise <= 5e-2.
     """
     cfg = config_by_name("qwen3_8b_chunked_prefill")
     print(f"[gpu-prefill] drawing inputs of {cfg.name}", flush=True)
     x = draw_inputs(cfg)
     ops, agents = pool_ops(cfg)
     samples = [(a, i, g) for a in (0, 3, 7) for i in (0, 1, 255, 511) for g in (0, 17, 31)]
+    keep = {}
+    sm = 1 / np.sqrt(cfg.head_dim)
     b, out, ref, bt, rt, start, g = _run(workload_geom(cfg), x, ops, agents, x["perm_b"],
-                                          x["perm_r"], cfg.chunk_len, cfg.lora_scale,
-                                          1 / np.sqrt(cfg.head_dim), cfg.rope_theta,
-                                          samples=samples)
+                                          x["perm_r"], cfg.chunk_len, cfg.lora_scale, sm,
+                                          cfg.rope_theta, samples=samples, keep=keep)
     gv = gpu_values(out, "bf16")
     assert np.all(np.isfinite(gv))
     idx = tuple(np.array(samples).T)
@@ -160,6 +166,20 @@ def test_qwen3_8b_chunked_prefill_workload():
             rpage = rt[a][t // 16]
             assert np.array_equal(rpool[rpage, 0, res_key_offset(row, ranks)], x["rk_new"][a, i])
             assert np.array_equal(rpool[rpage, 1, res_value_offset(row, ranks, 16)], x["rv_new"][a, i])
+    # the adapter's contribution
+    zB = np.zeros_like(x["Bk"])
+    b.Bk, b.Bv = to_device(zB), to_device(zB)
+    out0 = b.prefill(keep["chunk"], cfg.lora_scale, sm, cfg.rope_theta)
+    torch.cuda.synchronize()
+    g0 = gpu_values(out0, "bf16")[idx]
+    r0 = prefill_attention(g, x["bpool"], x["rpool"], bt, rt, np.array(start), x["q"],
+                           x["k_new"], x["v_new"], x["rk_new"], x["rv_new"], zB, zB,
+                           cfg.lora_scale, sm, cfg.rope_theta, samples=samples)[idx]
+    assert_close(g0, r0, "qwen3-8b chunked prefill, B = 0 (sampled rows)")
+    dg, dr = gv[idx] - g0, ref[idx] - r0
+    rel = np.linalg.norm(dg - dr) / np.linalg.norm(dr)
+    print(f"[parity] qwen3-8b prefill residual delta rel={rel:.3e}", flush=True)
+    assert rel <= 5e-2
 
 
 @pytest.mark.parametrize("dtype,d,r,Hkv,G", [("bf16", 128, 16, 2, 4), ("f32", 256, 64, 1, 2)])

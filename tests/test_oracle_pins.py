@@ -231,6 +231,81 @@ def test_zero_adapter_equals_sdpa(variant):
         assert _nrel(o[a], ref[0, :, 0].numpy()) < 1e-12
 
 
+# ---- missing pages (ForkKV study note, "Error / eviction recovery") -------------------------
+# A base page evicted from every holder leaves table entries of -1 until it is refilled: its
+# positions hold no key.  A sequence without residual pages has table entries of -1 there and
+# a zero residual.
+
+def _knock_out(bt, rt, lens, rng):
+    """Mark one inner base page of each agent with keys as missing, and one residual page."""
+    bt, rt = bt.copy(), rt.copy()
+    for a in range(len(lens)):
+        n = -(-int(lens[a]) // 16)
+        if n >= 2:
+            bt[a, int(rng.integers(0, n - 1))] = -1
+        if n >= 1:
+            rt[a, int(rng.integers(0, n))] = -1
+    return bt, rt
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_missing_pages_decode_matches_brute_force(seed):
+    case = tiny_case(150 + seed, "f32", Hq=4, Hkv=2, d=16, r=4, n_agents=3, max_prefix=60)
+    bt, rt, lens, _, _ = _build(case)
+    bt, rt = _knock_out(bt, rt, lens, np.random.default_rng(seed))
+    assert (bt < 0).any() and (rt < 0).any()
+    assert _nrel(_oracle_decode(case, bt, rt, lens), _brute(case, bt, rt, lens)) < 1e-12
+
+
+def test_missing_pages_prefill_matches_brute_force():
+    C = 5
+    case = tiny_case(160, "f32", Hq=2, Hkv=1, d=16, r=4, n_agents=2, chunk=C, max_prefix=60)
+    pm = PoolModel(64, 64, 16, case["perm_b"], case["perm_r"])
+    names = pm.replay(case["ops"])
+    hs = [names[a] for a in case["agents"]]
+    start = np.array([pm.length(h) for h in hs])
+    for h in hs:
+        pm.append(h, C)
+    bt, rt, lens = (np.array(x) for x in pm.tables(hs, 64))
+    # base pages go missing only wholly before the chunk (the chunk's own rows are stored);
+    # a residual page anywhere, the chunk's last page included
+    bt2, rt2 = _knock_out(bt, rt, np.minimum(lens, start // 16 * 16 + 1),
+                          np.random.default_rng(7))
+    rt2[1, (int(lens[1]) - 1) // 16] = -1
+    args = (case["bpool"], case["rpool"], bt2, rt2, start, case["q"], case["k_new"],
+            case["v_new"], case["rk_new"], case["rv_new"], case["Bk"], case["Bv"],
+            case["lora_scale"], case["sm_scale"], case["theta"])
+    o = prefill_attention(_geo(case), *args)
+    b = np.array(brute_prefill(16, 2, 1, 16, 4, "f32", *args))
+    assert _nrel(o, b) < 1e-12
+
+
+def test_missing_base_page_zero_adapter_equals_masked_sdpa():
+    """With B = 0, attention over a sequence with a missing base page is the library routine
+    with those keys masked out (and a missing residual page changes nothing)."""
+    case = tiny_case(170, "f32", Hq=6, Hkv=2, d=16, r=4, n_agents=3, max_prefix=70)
+    case["Bk"] = np.zeros_like(case["Bk"])
+    case["Bv"] = np.zeros_like(case["Bv"])
+    bt, rt, lens, _, _ = _build(case)
+    bt2, rt2 = _knock_out(bt, rt, lens, np.random.default_rng(3))
+    o = _oracle_decode(case, bt2, rt2, lens)
+    geo = _geo(case)
+    for a in range(3):
+        pos = np.arange(lens[a])
+        K = np.stack([base_key_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32") for h in range(2)])
+        V = np.stack([base_value_rows(case["bpool"], bt[a], pos, h, 16, 16, "f32") for h in range(2)])
+        K = torch.from_numpy(np.repeat(K, geo.G, axis=0))[None]
+        V = torch.from_numpy(np.repeat(V, geo.G, axis=0))[None]
+        keep = torch.from_numpy(bt2[a][pos // 16] >= 0)[None, None, None, :]
+        q = torch.from_numpy(decode_values(case["q"][a], "f32"))[None, :, None, :]
+        if not bool(keep.any()):
+            assert np.all(o[a] == 0.0)
+            continue
+        ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=keep,
+                                                               scale=case["sm_scale"])
+        assert _nrel(o[a], ref[0, :, 0].numpy()) < 1e-12
+
+
 # ---- C3: RoPE invariants ------------------------------------------------------------------
 
 def test_rope_invariants():
