@@ -83,7 +83,8 @@ enum {
   FORKKV_ENOMEM = -2,      /* page pool exhausted (state unchanged) */
   FORKKV_EHIP = -3,        /* a HIP call or kernel launch failed */
   FORKKV_ESTATE = -4,      /* call not valid in the current state (e.g. plan not uploaded) */
-  FORKKV_EUNSUPPORTED = -5 /* shape or dtype outside what the kernels implement */
+  FORKKV_EUNSUPPORTED = -5, /* shape or dtype outside what the kernels implement */
+  FORKKV_ETOOBIG = -6       /* plan's workspace exceeds the static scratch (no-alloc decode) */
 };
 
 enum { FORKKV_DTYPE_F32 = 0, FORKKV_DTYPE_BF16 = 1 };
@@ -296,6 +297,28 @@ typedef struct {
  * for a plan over a frozen tail);
  * FORKKV_ESTATE (pool without device storage, plan not uploaded); FORKKV_EHIP. */
 int forkkv_residual_attn_decode(const forkkv_decode_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode without allocation, for callers that cannot call hipMalloc or bring a device
+ * workspace (code under HIP stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same computation, kernels and output as forkkv_residual_attn_decode; the
+ * split-K workspace is instead a static device array of the library, one per GPU, of
+ * FORKKV_NOALLOC_SCRATCH_BYTES (32 MiB: the MFMA plans of the Llama3-8B and Qwen2.5-14B
+ * decode workloads need 3.2, 7.8 and 20.7 MiB), held until the process ends.
+ *   args->workspace and args->workspace_bytes are ignored (pass NULL / 0).
+ *   No plan timing is recorded (forkkv_plan_set_timing is ignored by this call).
+ *   The first call on a device resolves that device's array address (hipGetSymbolAddress,
+ *   with the device current); no call allocates device or host memory.
+ *   Nothing in the array needs clearing between calls: the split kernel writes every
+ *   partial slot the combine reads.  All calls on one GPU share its array, so calls that
+ *   overlap on one GPU (two streams, two threads) race and must be serialised by the
+ *   caller; calls on one stream are ordered and safe.
+ * Errors: as forkkv_residual_attn_decode, plus FORKKV_ETOOBIG when the plan's
+ * workspace_bytes exceed FORKKV_NOALLOC_SCRATCH_BYTES (decided on the host, before any
+ * device work).
+ * --------------------------------------------------------------------------------- */
+#define FORKKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int forkkv_residual_attn_decode_noalloc(const forkkv_decode_args* args, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------
  * Decode step with append: each agent's newest token is stored into the pools first, then

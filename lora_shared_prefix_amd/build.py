@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libforkkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 CPP_SOURCES = ["pool.cpp", "plan.cpp", "api.cpp"]
-HIP_SOURCES = ["kernels_generic.hip", "kernels_mfma.hip"]
+HIP_SOURCES = ["kernels_generic.hip", "kernels_mfma.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",

@@ -134,9 +134,10 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
 }
 
 // Split kernel + combine on the stream, with the plan's optional event timing.
-int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hipStream_t stream) {
+int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hipStream_t stream,
+                  bool allow_timing = true) {
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
-  if (pl->timing) {
+  if (pl->timing && allow_timing) {
     for (auto& e : ev) {
       e = get_event(pl);
       if (!e) return FORKKV_EHIP;
@@ -153,7 +154,7 @@ int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hip
   if (ev[2] && hipEventRecord(ev[2], stream) != hipSuccess) return FORKKV_EHIP;
   if (forkkv::launch_combine(p, dtype, stream) != hipSuccess) return FORKKV_EHIP;
   if (ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return FORKKV_EHIP;
-  if (pl->timing) {
+  if (pl->timing && allow_timing) {
     if (pl->n_items > 0) {
       pl->pending.push_back({0, ev[0], ev[1]});
     } else {
@@ -176,6 +177,26 @@ int forkkv_residual_attn_decode(const forkkv_decode_args* a, hipStream_t stream)
   if (rc != FORKKV_OK || a->plan->n_agents == 0) return rc;
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   return launch_decode(const_cast<forkkv_plan*>(a->plan), p, a->pool->desc.dtype, stream);
+}
+
+int forkkv_residual_attn_decode_noalloc(const forkkv_decode_args* a, hipStream_t stream) {
+  if (!a || !a->plan) return FORKKV_EINVAL;
+  if (a->plan->workspace_bytes > FORKKV_NOALLOC_SCRATCH_BYTES) return FORKKV_ETOOBIG;
+  forkkv_decode_args args = *a;
+  args.workspace = nullptr;
+  args.workspace_bytes = 0;
+  if (a->plan->n_slots > 0) {
+    hipError_t err = hipSuccess;
+    args.workspace = forkkv::noalloc_scratch(&err);
+    if (!args.workspace) return FORKKV_EHIP;
+    args.workspace_bytes = FORKKV_NOALLOC_SCRATCH_BYTES;
+  }
+  forkkv::DecodeParams p;
+  const int rc = prepare_decode(&args, &p);
+  if (rc != FORKKV_OK || a->plan->n_agents == 0) return rc;
+  (void)hipGetLastError();
+  return launch_decode(const_cast<forkkv_plan*>(a->plan), p, a->pool->desc.dtype, stream,
+                       /*allow_timing=*/false);
 }
 
 int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipStream_t stream) {

@@ -211,6 +211,9 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t* start_host
 hipError_t launch_cow_copy(void* bcache, int dtype, int num_kv_heads, int head_dim,
                            int32_t src_page, int32_t dst_page, int32_t n_rows, hipStream_t s);
 
+// Device address of the current device's static split-K scratch (scratch.hip).
+void* noalloc_scratch(hipError_t* err);
+
 // Limits of the generic kernel.
 constexpr int kGenericThreads = 256;
 constexpr int kGenericAccPerThread = 32;   // rows * d <= 256 * 32

@@ -78,6 +78,7 @@ const char* forkkv_strerror(int code) {
     case FORKKV_EHIP: return "HIP error";
     case FORKKV_ESTATE: return "invalid state";
     case FORKKV_EUNSUPPORTED: return "unsupported shape or dtype";
+    case FORKKV_ETOOBIG: return "plan needs more split-K workspace than the static scratch holds";
     default: return "unknown error";
   }
 }

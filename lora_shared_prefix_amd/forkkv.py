@@ -13,7 +13,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libforkkv.so")
 
-OK, EINVAL, ENOMEM, EHIP, ESTATE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ENOMEM, EHIP, ESTATE, EUNSUPPORTED, ETOOBIG = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DTYPE_F32, DTYPE_BF16 = 0, 1
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
 FORK_PACK, FORK_FREEZE, FORK_AUTO = 0, 1, 2
@@ -112,6 +113,7 @@ _SIGS = {
     "forkkv_plan_set_timing": (C.c_int, [C.c_void_p, C.c_int32]),
     "forkkv_plan_timing": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_double), _i32p]),
     "forkkv_residual_attn_decode": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
+    "forkkv_residual_attn_decode_noalloc": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "forkkv_residual_attn_decode_append": (C.c_int, [C.POINTER(DecodeAppendArgs), C.c_void_p]),
     "forkkv_residual_attn_prefill": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
     "forkkv_write_rows": (C.c_int, [C.POINTER(WriteArgs), C.c_void_p]),
@@ -380,6 +382,17 @@ def residual_attn_decode(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, wor
                       _ptr(pstart))
     _check(lib().forkkv_residual_attn_decode(C.byref(args), _stream(stream)),
            "forkkv_residual_attn_decode")
+
+
+def residual_attn_decode_noalloc(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out,
+                                 lora_scale, sm_scale, rope_theta, stream=None, pstart=None):
+    """Launch decode (async) with the library's static split-K scratch instead of a caller
+    workspace: nothing is allocated.  Calls that overlap on one GPU race."""
+    args = DecodeArgs(pool.handle, plan.handle, q.data_ptr(), Bk.data_ptr(), Bv.data_ptr(),
+                      btab.data_ptr(), rtab.data_ptr(), int(btab.shape[1]), float(lora_scale),
+                      float(sm_scale), float(rope_theta), out.data_ptr(), None, 0, _ptr(pstart))
+    _check(lib().forkkv_residual_attn_decode_noalloc(C.byref(args), _stream(stream)),
+           "forkkv_residual_attn_decode_noalloc")
 
 
 def residual_attn_decode_append(pool: Pool, plan: Plan, q, Bk, Bv, btab, rtab, out, workspace,
