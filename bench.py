@@ -6,8 +6,11 @@ one decode query per agent.  A step is one decode call (split-K kernel + LSE/B_v
 combine) over the whole batch; inputs are resident in HBM.  Input copies are rotated
 so the step streams from HBM rather than the 256 MB Infinity Cache.  The step time comes
 from the K calls captured as one HIP graph and replayed (no host launch cost inside); the
-split kernel's launch duration (for the roofline figure) from a further pass of K eager
-calls with per-launch events recorded by the library on the launch stream.
+split kernel's time (for the roofline figure) from the same K calls captured the same way
+with the plan in split-only mode (the split kernel launched alone), so both come from one
+kind of timing and the split time is the smaller.  The roofline is reported against the
+8 TB/s spec peak and against the box's measured read-only streaming ceiling; the GPU
+clocks and power cap are read while the step graph replays.
 
 Also reported (skippable): the other two decode workloads, decode with append, decode over
 a frozen tail, eviction / refill / base-only row write (`next_rows`), chunked prefill on the
@@ -101,7 +104,7 @@ def cpu_baseline(cfg, x, ops, agents, n_sample):
                       f"fp64 numpy, {dt:.1f} s; host cpus={len(os.sched_getaffinity(0))}"}
 
 
-MFMA_PEAK_BF16_TFLOPS = 2500.0
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 (spec)
 
 
 def prefill_flops(cfg):
@@ -187,9 +190,10 @@ def bench_prefill(steps, warmup):
     return res
 
 
-def bench_decode(name, steps, warmup, kernel, pages_per_item, copies_arg):
-    """Decode step time (graph replay), split/combine launch times (events) on the named
-    decode workload."""
+def bench_decode(name, steps, warmup, kernel, pages_per_item, copies_arg, clocks=None):
+    """Decode step time and split-kernel time (both from graph replays) on the named decode
+    workload; ``clocks`` (a dict) receives the GPU clocks and power read while the step
+    graph replays."""
     import numpy as np
     import torch
 
@@ -248,51 +252,38 @@ def bench_decode(name, steps, warmup, kernel, pages_per_item, copies_arg):
     # 1) the timed region: the K steps captured once as a HIP graph (K decode calls, the
     #    input copies in rotation), replayed once untimed, then once timed, bracketed by
     #    events on the replay stream; no per-call events or host launches inside
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    t0.record()
-    graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / steps
-    # 2) the same K steps again with HIP events recorded by the library around each kernel
-    #    launch (on the launch stream): average launch duration of the split and combine
-    plan.timing()  # drop anything recorded so far
-    plan.set_timing(True)
-    split_ms = comb_ms = 0.0
-    launches = 0
-    split_samples = []
-    for i in range(steps):
-        step(i)
-        if (i + 1) % copies == 0 or i + 1 == steps:  # read the events of this rotation
-            torch.cuda.synchronize()
-            sm_, cm_, n_ = plan.timing()
-            split_ms, comb_ms, launches = split_ms + sm_, comb_ms + cm_, launches + n_
-            split_samples.append(sm_ / max(n_, 1))
-    plan.set_timing(False)
-    split_avg = split_ms / max(launches, 1)
-    comb_avg = comb_ms / max(launches, 1)
+    graph = _capture(lambda: [step(i) for i in range(steps)])
+    ms_step = _replay_ms(graph, steps)
+    # 2) the split kernel alone, timed the same way: the same K calls (same rotation) with
+    #    the plan in split-only mode, captured as a graph of K split launches
+    plan.set_timing(fk.TIMING_SPLIT_ONLY)
+    split_graph = _capture(lambda: [step(i) for i in range(steps)])
+    plan.set_timing(fk.TIMING_OFF)
+    split_avg = _replay_ms(split_graph, steps)
+    # spread over further timed replays of both graphs (per-call ms of each replay)
+    reps = [_replay_ms(split_graph, steps, warm=False) for _ in range(5)]
+    step_reps = [_replay_ms(graph, steps) for _ in range(1)]
+    step_reps += [_replay_ms(graph, steps, warm=False) for _ in range(4)]
+    comb_avg = ms_step - split_avg  # the combine launch and the gap before it
     log(f"step {ms_step * 1e3:.1f} us (eager {eager_ms_step * 1e3:.1f} us); split "
-        f"{split_avg * 1e3:.1f} us, combine {comb_avg * 1e3:.1f} us")
+        f"{split_avg * 1e3:.1f} us, combine + gap {comb_avg * 1e3:.1f} us")
+    if clocks is not None:
+        clocks.update(gpu_clocks_under_load(graph))
+    del graph, split_graph
 
-    # warm (cache-resident) figure for context: the same copy every step
-    plan.set_timing(True)
-    for _ in range(steps):
-        fk.residual_attn_decode(first.pool, plan, first.q, first.Bk, first.Bv, first.btab,
-                                first.rtab, first.out, first.workspace, cfg.lora_scale, sm,
-                                cfg.rope_theta)
-    torch.cuda.synchronize()
-    plan.set_timing(False)
-    wsplit, _, wl = plan.timing()
+    # warm (cache-resident) figure for context: the same copy every step, split only
+    plan.set_timing(fk.TIMING_SPLIT_ONLY)
+    wgraph = _capture(lambda: [fk.residual_attn_decode(
+        first.pool, plan, first.q, first.Bk, first.Bv, first.btab, first.rtab, first.out,
+        first.workspace, cfg.lora_scale, sm, cfg.rope_theta) for _ in range(steps)])
+    plan.set_timing(fk.TIMING_OFF)
+    wsplit_ms = _replay_ms(wgraph, steps)
+    del wgraph
 
     achieved = split_bytes / (split_avg * 1e-3) / 1e9
     traffic = load_traffic(kname) if name == DECODE_WORKLOAD else None
-    pct = np.percentile(np.array(split_samples) * 1e3, [10, 50, 90]).tolist()
+    pct = np.percentile(np.array(reps) * 1e3, [10, 50, 90]).tolist()
+    step_pct = np.percentile(np.array(step_reps) * 1e3, [10, 50, 90]).tolist()
     return {
         "_cfg": cfg, "_x": x, "_ops": ops, "_agents": agents,
         "agent_tokens_per_s": cfg.n_agents / (ms_step * 1e-3),
@@ -304,48 +295,109 @@ def bench_decode(name, steps, warmup, kernel, pages_per_item, copies_arg):
                    "input_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": f"residual_attn_{kname} (split-K decode)",
+                     "kernel": f"decode_mfma_kernel (split-K decode)" if kname == "mfma"
+                               else "residual_attn_generic (split-K decode)",
                      "algorithmic_bytes_per_launch": split_bytes,
-                     "avg_launch_us": split_avg * 1e3},
+                     "avg_launch_us": split_avg * 1e3,
+                     "timing": "graph of the timed K calls in split-only mode, one timed replay"},
         "step_hbm_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
         "split_us_p10_p50_p90": pct,
-        "combine_avg_us": comb_avg * 1e3,
+        "step_us_p10_p50_p90": step_pct,
+        "combine_and_gap_us": comb_avg * 1e3,
         "eager_ms_per_step": eager_ms_step,
-        "warm_split_avg_us": wsplit / max(wl, 1) * 1e3,
+        "warm_split_avg_us": wsplit_ms * 1e3,
     }
 
 
-def _graph_ms(fn, steps):
-    """Per-call ms of `steps` calls of fn captured as one HIP graph (after one untimed replay)."""
+def _capture(fn):
+    """fn() once eagerly, then captured as a HIP graph and replayed once (untimed)."""
     import torch
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(steps):
-            fn()
+        fn()
     g.replay()
     torch.cuda.synchronize()
+    return g
+
+
+WARM_S = 0.2  # back-to-back replays before a timed replay
+
+
+def _warm(g, seconds=WARM_S):
+    """Replay g back to back for about `seconds`: after an idle gap (graph capture on the
+    host, set-up) the device takes some milliseconds to return to its working clocks, and
+    a decode step in a serving loop runs right after the previous one."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+
+
+def _replay_ms(g, calls, warm=True):
+    """Per-call ms of one timed replay of a graph of `calls` calls (events on the replay
+    stream, synchronised before and after), after back-to-back warm replays."""
+    import torch
+    if warm:
+        _warm(g)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0.record()
     g.replay()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return t0.elapsed_time(t1) / calls
+
+
+def gpu_clocks_under_load(graph, seconds=1.5):
+    """GPU clocks, power and power cap (rocm-smi) read while `graph` replays back to back."""
+    import subprocess
+    import threading
+
+    import torch
+    res = {}
+
+    def read():
+        time.sleep(seconds / 3)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
+                                "--json"], capture_output=True, text=True, timeout=30)
+            card = next(iter(json.loads(r.stdout).values()))
+            res["under_load"] = {k: v for k, v in card.items()
+                                 if "clk" in k.lower() or "power" in k.lower()}
+        except Exception as e:  # no rocm-smi or no permission: record why
+            res["under_load_error"] = repr(e)[:200]
+
+    th = threading.Thread(target=read)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        graph.replay()
+        torch.cuda.synchronize()
+    th.join()
+    return res
+
+
+def _graph_ms(fn, steps):
+    """Per-call ms of `steps` calls of fn captured as one HIP graph (warm replays, then one
+    timed replay)."""
+    g = _capture(lambda: [fn() for _ in range(steps)])
+    return _replay_ms(g, steps)
 
 
 def _split_us(plan, fn, steps):
-    """Average split-kernel and combine launch durations (library events), in us."""
-    import torch
-    plan.timing()
-    plan.set_timing(True)
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    plan.set_timing(False)
-    s, c, n = plan.timing()
-    return s / max(n, 1) * 1e3, c / max(n, 1) * 1e3
+    """Split-kernel time per call in us: `steps` calls with the plan in split-only mode,
+    captured as a graph and replayed (timed like the whole call)."""
+    from lora_shared_prefix_amd import forkkv as fk
+    plan.set_timing(fk.TIMING_SPLIT_ONLY)
+    try:
+        ms = _graph_ms(fn, steps)
+    finally:
+        plan.set_timing(fk.TIMING_OFF)
+    return ms * 1e3
 
 
 def bench_next_rows(cfg, x, ops, agents, steps):
@@ -368,7 +420,7 @@ def bench_next_rows(cfg, x, ops, agents, steps):
     ab = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"])
     dec = lambda: ab.decode(cfg.lora_scale, sm, cfg.rope_theta)
     plain_ms = _graph_ms(dec, steps)
-    plain_split, _ = _split_us(ab.plan, dec, steps)
+    plain_split = _split_us(ab.plan, dec, steps)
     out["plain_decode"] = {"ms_per_call": plain_ms, "split_avg_us": plain_split}
 
     # decode with append: every agent's new token is stored, then attended (one call)
@@ -396,7 +448,7 @@ def bench_next_rows(cfg, x, ops, agents, steps):
     assert fb.pstart is not None
     fdec = lambda: fb.decode(cfg.lora_scale, sm, cfg.rope_theta)
     f_ms = _graph_ms(fdec, steps)
-    f_split, _ = _split_us(fb.plan, fdec, steps)
+    f_split = _split_us(fb.plan, fdec, steps)
     f_bytes, _ = algorithmic_bytes(cfg, L0 + N * cfg.suffix_len)
     out["frozen_tail_decode"] = {
         "ms_per_call": f_ms, "split_avg_us": f_split,
@@ -429,6 +481,74 @@ def bench_next_rows(cfg, x, ops, agents, steps):
                            "write_rows_gbs": 2 * w_bytes / (w_ms * 1e-3) / 1e9}
     log("next rows: " + json.dumps(out))
     return out
+
+
+def _microbench_lib():
+    import ctypes as C
+    path = os.path.join(ROOT, "lora_shared_prefix_amd", "libforkkv_microbench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+    L = C.CDLL(path)
+    L.mb_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int,
+                                 C.c_void_p]
+    L.mb_mfma_bf16.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
+    L.mb_mfma_chains.restype = C.c_int
+    return L
+
+
+def measured_ceilings():
+    """The box's own ceilings, each self-checked: a read-only streaming reduction over 1 GiB
+    (four times the 256 MB Infinity Cache) and a bf16 16x16x32 MFMA loop."""
+    import torch
+    L = _microbench_lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    # read-only stream: int32 ones, so every pass must sum to the word count
+    n_bytes = 1 << 30
+    buf = torch.ones(n_bytes // 4, dtype=torch.int32, device="cuda")
+    passes = 20
+    best = None
+    names = {0: "4 loads in flight", 1: "8 loads in flight", 2: "8 non-temporal loads in flight"}
+    for variant in (0, 1, 2):
+        for blocks in (2048, 8192):
+            part = torch.zeros(blocks, dtype=torch.int64, device="cuda")
+            for _ in range(passes):  # back to back: the device at its working clocks
+                assert L.mb_stream_read(buf.data_ptr(), n_bytes, part.data_ptr(), blocks,
+                                        variant, sp) == 0
+            t0.record()
+            for _ in range(passes):
+                L.mb_stream_read(buf.data_ptr(), n_bytes, part.data_ptr(), blocks, variant, sp)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / passes
+            assert int(part.sum().item()) == n_bytes // 4, "stream-read checksum"
+            if best is None or ms < best[0]:
+                best = (ms, f"{blocks} blocks x 256 threads, {names[variant]}")
+    read_ms = best[0]
+    del buf, part
+    # bf16 MFMA loop: A = 1, B = 1/32 (exact in bf16), so each MFMA adds 1.0 per element
+    ops = torch.tensor([0x3F80] * 8 + [0x3D00] * 8, dtype=torch.int16, device="cuda")
+    mblocks, iters = 256 * 8, 2048
+    chains = L.mb_mfma_chains()
+    out = torch.zeros(mblocks * 4, dtype=torch.float32, device="cuda")
+    assert L.mb_mfma_bf16(ops.data_ptr(), iters, out.data_ptr(), mblocks, sp) == 0
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(5):
+        L.mb_mfma_bf16(ops.data_ptr(), iters, out.data_ptr(), mblocks, sp)
+    t1.record()
+    torch.cuda.synchronize()
+    mfma_ms = t0.elapsed_time(t1) / 5
+    assert bool(torch.all(out == float(4 * chains * iters))), "MFMA-loop checksum"
+    flops = mblocks * 4 * chains * iters * 2 * 16 * 16 * 32
+    return {"hbm_read_gbs": n_bytes / (read_ms * 1e-3) / 1e9,
+            "hbm_read_test": f"read-only sum of 1 GiB, best of 6 launch shapes ({best[1]}, "
+                             f"16 B loads), {passes} passes, checksum ok",
+            "mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "mfma_test": f"{mblocks * 4} waves x {chains} chains x {iters} "
+                         "v_mfma_f32_16x16x32_bf16, checksum ok"}
 
 
 def copy_bandwidth_gbs():
@@ -496,11 +616,19 @@ def main():
         return
 
     kernel = {"auto": fk.KERNEL_AUTO, "generic": fk.KERNEL_GENERIC, "mfma": fk.KERNEL_MFMA}[args.kernel]
+    clocks = {"rocm": torch.version.hip}
     d = bench_decode(args.workload, args.steps, args.warmup, kernel, args.pages_per_item,
-                     args.copies)
+                     args.copies, clocks=clocks)
     cfg, x, ops, agents = d.pop("_cfg"), d.pop("_x"), d.pop("_ops"), d.pop("_agents")
     ceiling = copy_bandwidth_gbs()
     log(f"device copy bandwidth {ceiling:.0f} GB/s (read + write bytes / time, 1 GiB copy)")
+    torch.cuda.empty_cache()
+    ceilings = measured_ceilings()
+    ceilings["copy_read_write_gbs"] = ceiling
+    log(f"measured ceilings: {json.dumps(ceilings)}")
+    rl = d["roofline"]
+    rl["peak_measured"] = ceilings["hbm_read_gbs"]
+    rl["frac_of_measured"] = rl["achieved"] / ceilings["hbm_read_gbs"]
     result = {
         "metric": "ResidualAttention decode agent-tokens/s + achieved HBM GB/s (% roofline), 1 GPU",
         "value": d["agent_tokens_per_s"],
@@ -518,11 +646,12 @@ def main():
         "roofline": d["roofline"],
         "step_hbm_gbs": d["step_hbm_gbs"],
         "split_us_p10_p50_p90": d["split_us_p10_p50_p90"],
-        "combine_avg_us": d["combine_avg_us"],
+        "step_us_p10_p50_p90": d["step_us_p10_p50_p90"],
+        "combine_and_gap_us": d["combine_and_gap_us"],
         "eager_ms_per_step": d["eager_ms_per_step"],
         "warm_split_avg_us": d["warm_split_avg_us"],
-        "copy_bandwidth_gbs": ceiling,
-        "split_frac_of_copy_bandwidth": d["roofline"]["achieved"] / ceiling,
+        "ceilings": ceilings,
+        "gpu": clocks,
     }
     if not args.no_more_workloads and args.workload == DECODE_WORKLOAD:
         others = {}
@@ -536,7 +665,7 @@ def main():
                 "split_avg_us": o["roofline"]["avg_launch_us"],
                 "split_hbm_gbs": o["roofline"]["achieved"], "split_frac": o["roofline"]["frac"],
                 "algorithmic_bytes_per_launch": o["roofline"]["algorithmic_bytes_per_launch"],
-                "combine_avg_us": o["combine_avg_us"], "config": o["config"]}
+                "combine_and_gap_us": o["combine_and_gap_us"], "config": o["config"]}
         result["other_decode_workloads"] = others
     if not args.no_next and args.workload == DECODE_WORKLOAD:
         torch.cuda.empty_cache()
@@ -544,6 +673,9 @@ def main():
     if not args.no_prefill:
         torch.cuda.empty_cache()  # the decode inputs are freed by now
         result["prefill"] = bench_prefill(args.steps, args.warmup)
+        result["prefill"]["peak_measured_tflops"] = ceilings["mfma_bf16_tflops"]
+        result["prefill"]["mfma_frac_of_measured"] = (result["prefill"]["tflops"]
+                                                      / ceilings["mfma_bf16_tflops"])
     if args.cpu_sample > 0:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(cfg, x, ops, agents, args.cpu_sample)

@@ -258,10 +258,17 @@ int forkkv_plan_export(const forkkv_plan* plan, int32_t* host_blob);
 int forkkv_plan_upload(forkkv_plan* plan, void* dev_buf, hipStream_t stream);
 int forkkv_plan_destroy(forkkv_plan* plan);
 
-/* Per-kernel timing with HIP events recorded on the launch stream around each launch
- * of the plan's split kernel and combine kernel (enable = 1).  forkkv_plan_timing
- * waits for the recorded events and returns the summed milliseconds and the number
- * of timed launches, then clears the sums. */
+/* Per-kernel timing.
+ *   FORKKV_TIMING_OFF (0): no timing.
+ *   FORKKV_TIMING_EVENTS (1): HIP events recorded on the launch stream around each launch of
+ *     the plan's split kernel and combine kernel; forkkv_plan_timing waits for them and
+ *     returns the summed milliseconds and the number of timed launches, then clears the sums.
+ *   FORKKV_TIMING_SPLIT_ONLY (2): measurement only -- decode calls with this plan launch the
+ *     split-K kernel alone (no combine, the output is not written, no events), so that a
+ *     caller can time the split kernel from replays of a captured graph of such calls, the
+ *     same way it times whole decode calls.
+ * Other values return FORKKV_EINVAL. */
+enum { FORKKV_TIMING_OFF = 0, FORKKV_TIMING_EVENTS = 1, FORKKV_TIMING_SPLIT_ONLY = 2 };
 int forkkv_plan_set_timing(forkkv_plan* plan, int32_t enable);
 int forkkv_plan_timing(forkkv_plan* plan, double* split_ms, double* combine_ms,
                        int32_t* launches);

@@ -15,6 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libforkkv.so")
+MICROBENCH_LIB = os.path.join(PKG, "libforkkv_microbench.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 CPP_SOURCES = ["pool.cpp", "plan.cpp", "api.cpp"]
@@ -61,6 +62,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([f"{ROCM}/bin/hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # device ceilings for the bench (a separate library: not part of the C ABI)
+    tmp = MICROBENCH_LIB + ".tmp"
+    _run([f"{ROCM}/bin/hipcc", *HIPFLAGS, "-shared", os.path.join(CSRC, "microbench.hip"),
+          "-o", tmp])
+    os.replace(tmp, MICROBENCH_LIB)
     return LIB
 
 

@@ -41,8 +41,9 @@ bool all_aligned16(const P*... ps) { return (aligned16(ps) && ...); }
 extern "C" {
 
 int forkkv_plan_set_timing(forkkv_plan* pl, int32_t enable) {
-  if (!pl) return FORKKV_EINVAL;
-  pl->timing = enable != 0;
+  if (!pl || enable < FORKKV_TIMING_OFF || enable > FORKKV_TIMING_SPLIT_ONLY) return FORKKV_EINVAL;
+  pl->timing = enable == FORKKV_TIMING_EVENTS;
+  pl->split_only = enable == FORKKV_TIMING_SPLIT_ONLY;
   return FORKKV_OK;
 }
 
@@ -151,6 +152,7 @@ int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hip
     if (err != hipSuccess) return FORKKV_EHIP;
     if (ev[1] && hipEventRecord(ev[1], stream) != hipSuccess) return FORKKV_EHIP;
   }
+  if (pl->split_only) return hipGetLastError() == hipSuccess ? FORKKV_OK : FORKKV_EHIP;
   if (ev[2] && hipEventRecord(ev[2], stream) != hipSuccess) return FORKKV_EHIP;
   if (forkkv::launch_combine(p, dtype, stream) != hipSuccess) return FORKKV_EHIP;
   if (ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return FORKKV_EHIP;

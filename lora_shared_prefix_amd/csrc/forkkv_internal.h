@@ -88,7 +88,8 @@ struct forkkv_plan {
   int32_t max_pages_needed = 0;
   int32_t max_agent_slots = 0;  // the largest number of partials of one agent
   // timing: (kind, begin, end) per timed launch, kind 0 = split, 1 = combine
-  bool timing = false;
+  bool timing = false;       // FORKKV_TIMING_EVENTS
+  bool split_only = false;   // FORKKV_TIMING_SPLIT_ONLY
   struct Timed { int kind; hipEvent_t b, e; };
   std::vector<Timed> pending;
   std::vector<hipEvent_t> spare;

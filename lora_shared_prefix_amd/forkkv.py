@@ -18,6 +18,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 DTYPE_F32, DTYPE_BF16 = 0, 1
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
 FORK_PACK, FORK_FREEZE, FORK_AUTO = 0, 1, 2
+TIMING_OFF, TIMING_EVENTS, TIMING_SPLIT_ONLY = 0, 1, 2
 PAGE = 16
 
 _i32p = C.POINTER(C.c_int32)
@@ -346,7 +347,9 @@ class Plan:
         return self
 
     def set_timing(self, enable):
-        _check(lib().forkkv_plan_set_timing(self.handle, int(bool(enable))), "forkkv_plan_set_timing")
+        """0 / False: off; 1 / True: events around each launch; TIMING_SPLIT_ONLY: decode
+        calls launch the split kernel alone (measurement only; the output is not written)."""
+        _check(lib().forkkv_plan_set_timing(self.handle, int(enable)), "forkkv_plan_set_timing")
 
     def timing(self):
         s, c, k = C.c_double(), C.c_double(), C.c_int32()
