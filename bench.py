@@ -360,11 +360,18 @@ def gpu_clocks_under_load(graph, seconds=1.5):
     import torch
     res = {}
 
+    # rocm-smi is a Python script: run it with this interpreter (no `env` re-exec), and not
+    # at all under a profiler whose preloaded library would initialise the GPU in the child
+    smi = "/opt/rocm/bin/rocm-smi"
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or not os.path.exists(smi):
+        return {"under_load_error": "not read (profiler preloaded or rocm-smi missing)"}
+
     def read():
         time.sleep(seconds / 3)
         try:
-            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
-                                "--json"], capture_output=True, text=True, timeout=30)
+            r = subprocess.run([sys.executable, smi, "--showclocks", "--showpower",
+                                "--showmaxpower", "--json"], capture_output=True, text=True,
+                               timeout=30)
             card = next(iter(json.loads(r.stdout).values()))
             res["under_load"] = {k: v for k, v in card.items()
                                  if "clk" in k.lower() or "power" in k.lower()}
@@ -423,20 +430,7 @@ def bench_next_rows(cfg, x, ops, agents, steps):
     plain_split = _split_us(ab.plan, dec, steps)
     out["plain_decode"] = {"ms_per_call": plain_ms, "split_avg_us": plain_split}
 
-    # decode with append: every agent's new token is stored, then attended (one call)
-    pb = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], plan=False)
-    pb.reserve_chunk(1)
-    pb.make_plan()
-    bf = torch.bfloat16
-    rows = {"k_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
-            "v_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
-            "rk_new": torch.randn(N, r, dtype=bf, device="cuda"),
-            "rv_new": torch.randn(N, r, dtype=bf, device="cuda")}
-    app = lambda: pb.decode_append(rows, cfg.lora_scale, sm, cfg.rope_theta)
-    app_ms = _graph_ms(app, steps)
-    out["decode_append"] = {"ms_per_call": app_ms, "agent_tokens_per_s": N / (app_ms * 1e-3),
-                            "over_plain_decode_us": (app_ms - plain_ms) * 1e3}
-    del pb
+    out["serving_loop"] = serving_loop(cfg, x, ops, agents, 64)
 
     # decode over a frozen tail: the trunk ends 7 rows into a page that every agent shares
     # read-only (fork mode freeze); the agents' own rows start on fresh pages
@@ -459,6 +453,7 @@ def bench_next_rows(cfg, x, ops, agents, steps):
     # decoupled eviction: 64 shared trunk pages leave every holder, fresh pages are mapped
     # back into the agents (host bookkeeping), and the recomputed base rows are stored
     # through one holder (base pool only; the residual pages never left)
+    bf = torch.bfloat16
     lp0, lp1 = 1000, 1064
     pages = [int(v) for v in ab.btab_host[0][lp0:lp1]]
     t = time.perf_counter()
@@ -549,6 +544,73 @@ def measured_ceilings():
             "mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
             "mfma_test": f"{mblocks * 4} waves x {chains} chains x {iters} "
                          "v_mfma_f32_16x16x32_bf16, checksum ok"}
+
+
+def serving_loop(cfg, x, ops, agents, steps):
+    """A serving loop of decode with append at the decode workload's shape (one input copy):
+    `steps` steps in a row on one plan.  Each step the host reserves every agent's next
+    token (one batched call); at a page crossing (every 16 steps here: the agents' lengths
+    are multiples of 16) it also updates the device tables in place and rebuilds and
+    re-uploads the plan; then the step runs -- as an eager call, and in a second pass as a
+    replay of one captured call (the plan's device lengths advance inside each call, so the
+    same graph serves every step).  Reported per step: wall time with all host work, GPU
+    time, and the host's share."""
+    import numpy as np
+    import torch
+
+    from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
+
+    geom = workload_geom(cfg)
+    sm = 1.0 / np.sqrt(cfg.head_dim)
+    N, Hkv, d, r = cfg.n_agents, cfg.num_kv_heads, cfg.head_dim, cfg.rank
+    bf = torch.bfloat16
+    rows = {"k_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
+            "v_new": torch.randn(N, Hkv, d, dtype=bf, device="cuda"),
+            "rk_new": torch.randn(N, r, dtype=bf, device="cuda"),
+            "rv_new": torch.randn(N, r, dtype=bf, device="cuda")}
+    res = {}
+    for mode in ("eager", "graph"):
+        b = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], plan=False)
+        b.pool.append_batch(b.handles, 1)
+        b.refresh_tables(extra_pages=steps // 16 + 2)
+        b.make_plan()
+        call = lambda: b.decode_append(rows, cfg.lora_scale, sm, cfg.rope_theta)
+        call()  # first step (untimed): compiles nothing, warms the device
+        g = None
+        if mode == "graph":
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+        torch.cuda.synchronize()
+        host, rebuilds = 0.0, 0
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        t0.record()
+        for _ in range(steps):
+            th = time.perf_counter()
+            same, _ = b.next_step()
+            rebuilds += int(b.lens[0] % 16 == 1)
+            assert same, "the captured step outlived the plan's capacities"
+            host += time.perf_counter() - th
+            if g is not None:
+                g.replay()
+            else:
+                call()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        gpu_ms = t0.elapsed_time(t1)
+        res[mode] = {"steps": steps, "page_crossings": rebuilds,
+                     "wall_us_per_step": wall / steps * 1e6,
+                     "gpu_us_per_step": gpu_ms / steps * 1e3,
+                     "host_us_per_step": host / steps * 1e6,
+                     "agent_tokens_per_s": N * steps / wall}
+        del b, g
+        torch.cuda.empty_cache()
+    log("serving loop: " + json.dumps(res))
+    return res
 
 
 def copy_bandwidth_gbs():

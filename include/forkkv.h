@@ -171,6 +171,17 @@ int forkkv_fork(forkkv_pool* pool, forkkv_seq parent, int32_t alias_len, forkkv_
 int forkkv_fork_ex(forkkv_pool* pool, forkkv_seq parent, int32_t alias_len, int32_t mode,
                    int32_t suffix_hint, forkkv_seq* child, forkkv_cow_op* cow);
 
+/* Reserve `rows` rows at the end of each of the n distinct sequences seqs (one decode step
+ * of a batch: rows = 1), as forkkv_seq_append does for each in order, all or nothing (on
+ * FORKKV_ENOMEM nothing changes).  bslots / rslots (host, nullable, n * rows) receive the
+ * slots, agent-major; cows (host, nullable, n entries) the copy-on-write row copy of each
+ * sequence (n_rows = 0 if none); *new_pages (nullable) the number of base pages the call
+ * took from the free list -- nonzero means some agent entered a new page, after which a
+ * decode plan over the batch needs forkkv_plan_rebuild. */
+int forkkv_seq_append_batch(forkkv_pool* pool, const forkkv_seq* seqs, int32_t n, int32_t rows,
+                            int32_t* bslots, int32_t* rslots, forkkv_cow_op* cows,
+                            int32_t* new_pages);
+
 /* Release a sequence: each page's reference count drops; pages reaching 0 return to the
  * tail of their free list. */
 int forkkv_seq_free(forkkv_pool* pool, forkkv_seq seq);
@@ -234,27 +245,44 @@ typedef struct {
   int32_t pages_per_item;     /* split-K length: pages per item (generic kernel) or pages per
                                  wave (MFMA kernel, <= 64); 0 = auto (MFMA: items sized so the
                                  grid fits one round of resident waves, balanced per wave) */
+  int32_t spare_items;        /* room for items beyond the first build's, so rebuilds after
+                                 page crossings keep the launch; 0 = one per agent */
 } forkkv_plan_opts;
 
 typedef struct {
   int32_t n_agents, n_items, n_slots, kernel, item_ints, num_q_heads;
   size_t plan_bytes;      /* device bytes forkkv_plan_upload needs */
   size_t workspace_bytes; /* device workspace forkkv_residual_attn_decode needs */
+  int32_t item_capacity;  /* items the decode launch covers (>= n_items; only grows) */
+  int32_t slot_capacity;  /* split-K partial slots the workspace holds (>= n_slots) */
 } forkkv_plan_info;
 
 /* Build the decode plan of the n sequences seqs (agent a = seqs[a]) for num_q_heads
  * query heads.  opts is nullable.  Kernel coverage: the MFMA kernel takes bf16, d = 128,
  * r = 16 and up to 16 query heads per KV head; the generic kernel every pool shape whose
  * group G = num_q_heads / Hkv has G * d <= 8192 and G * r <= 2048 (its LDS plan may use up
- * to 160 KiB); other shapes return FORKKV_EUNSUPPORTED, as does prefill for them. */
+ * to 160 KiB); other shapes return FORKKV_EUNSUPPORTED, as does prefill for them.
+ * The plan captures each agent's length and last page; the lengths also live in its
+ * device copy, where decode with append advances them (see below). */
 int forkkv_plan_decode(const forkkv_pool* pool, const forkkv_seq* seqs, int32_t n,
                        int32_t num_q_heads, const forkkv_plan_opts* opts, forkkv_plan** out);
+/* Rebuild a plan in place from the pool's current state (same options), e.g. after a
+ * decode step with append took an agent into a new page or a copy-on-write.  Capacities
+ * only grow: *same_launch (nullable) is 1 when the batch size, item capacity, slot
+ * capacity and kernel are unchanged, so that -- after forkkv_plan_upload to the same device
+ * buffer, which must hold plan_bytes -- a decode launch captured before (a HIP graph) stays
+ * valid; 0 when the caller must check plan_bytes / workspace_bytes and launch anew.  On an
+ * error the plan is unchanged.  The device copy is stale until the next upload. */
+int forkkv_plan_rebuild(forkkv_plan* plan, const forkkv_pool* pool, const forkkv_seq* seqs,
+                        int32_t n, int32_t* same_launch);
 int forkkv_plan_get_info(const forkkv_plan* plan, forkkv_plan_info* out);
 /* Copy the plan's integer blob (plan_bytes / 4 int32) to host memory, for inspection. */
 int forkkv_plan_export(const forkkv_plan* plan, int32_t* host_blob);
-/* Copy the plan blob to a caller-owned device buffer of plan_bytes on stream and wait for
- * the copy (the host blob is its source); the plan remembers the buffer.  Not for use
- * inside a stream capture. */
+/* Copy the plan blob to a caller-owned device buffer of plan_bytes, asynchronously on
+ * stream (from one of two pinned staging buffers the plan owns; the call waits only for the
+ * copy made two uploads earlier from the same buffer).  The plan remembers the buffer.
+ * Order the upload before the decode calls that use it (same stream, or an event).  Not
+ * for use inside a stream capture. */
 int forkkv_plan_upload(forkkv_plan* plan, void* dev_buf, hipStream_t stream);
 int forkkv_plan_destroy(forkkv_plan* plan);
 
@@ -329,13 +357,22 @@ int forkkv_residual_attn_decode_noalloc(const forkkv_decode_args* args, hipStrea
 
 /* ---------------------------------------------------------------------------------
  * Decode step with append: each agent's newest token is stored into the pools first, then
- * the agent's query attends to its keys 0 .. len-1, the new token included.  The caller
- * has reserved the token with forkkv_seq_append (running the copy-on-write row copy it
- * reports with forkkv_cow_copy, so a tail page shared after a fork is first packed into a
- * private page -- ForkServe README, "Design vs APC": pack plus an n_valid-row copy, not a
- * whole page), re-exported the tables and built the plan over the new lengths.  Within one
- * call the rows are written before any attention reads them (Penelope review, 部件二:
- * each layer writes the batch's K/V, then attends).
+ * the agent's query attends to its keys 0 .. len-1, the new token included, where len is
+ * the length in the plan's device copy.  Within one call the rows are written before any
+ * attention reads them (Penelope review, 部件二: each layer writes the batch's K/V, then
+ * attends).  After the call every device length has advanced by one, so the next call
+ * appends at the following position with the same plan: a serving loop replays one call
+ * (or one captured graph) step after step with no host work on the plan.
+ *
+ * Serving loop.  Before the first step the caller reserves the token with forkkv_seq_append
+ * (or forkkv_seq_append_batch) and builds and uploads the plan, whose lengths then count it.
+ * Each later step it reserves the next token on the host the same way.  When a reservation
+ * took an agent into a new page or needed a copy-on-write (ForkServe README, "Design vs
+ * APC": a tail page shared after a fork is first packed into a private page, an
+ * n_valid-row copy, not a whole page), the caller runs the copy (forkkv_cow_copy), brings
+ * the device tables up to date, and calls forkkv_plan_rebuild and forkkv_plan_upload
+ * before the step; otherwise nothing.  A token whose row would fall outside its agent's
+ * last page (a crossing without a rebuild) is neither stored nor attended to.
  * --------------------------------------------------------------------------------- */
 typedef struct {
   forkkv_decode_args decode; /* as for decode; every plan length counts the new token (>= 1)
@@ -347,11 +384,11 @@ typedef struct {
 } forkkv_decode_append_args;
 
 /* Same errors as forkkv_residual_attn_decode; FORKKV_EINVAL also for a null row pointer or
- * a plan length below 1.  The new rows land at position len - 1 of each agent, in the slot
- * the pool holds for it when the plan is built (the tables passed are the ones exported for
- * that plan).  A sequence appears at most once in the batch.  On the MFMA kernel the split
- * kernel stores the rows itself, ahead of the pages that hold them; the generic kernel runs
- * a row-write kernel first. */
+ * a plan length below 1.  The new rows land at position len - 1 of each agent: row
+ * (len - 1) - (start of its last page), in the pages the tables name for the plan's last
+ * page of the agent.  A sequence appears at most once in the batch.  On the MFMA kernel the
+ * split kernel stores the rows itself, ahead of the pages that hold them; the generic
+ * kernel runs a row-write kernel first.  The combine kernel advances the lengths. */
 int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* args,
                                        hipStream_t stream);
 

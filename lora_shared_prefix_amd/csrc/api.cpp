@@ -113,7 +113,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   p.ws_accr = reinterpret_cast<float*>(ws + pl->ws_off_accr);
   p.out = a->out;
   p.n_agents = pl->n_agents;
-  p.n_items = pl->n_items;
+  p.n_items = pl->item_capacity;  // the launch grid; the kernels read the live count
   p.num_q_heads = pl->num_q_heads;
   p.num_kv_heads = g.num_kv_heads;
   p.head_dim = g.head_dim;
@@ -126,7 +126,7 @@ int prepare_decode(const forkkv_decode_args* a, forkkv::DecodeParams* out) {
   p.off_lens = pl->blob[forkkv::kHdrOffLens];
   p.off_slot_ptr = pl->blob[forkkv::kHdrOffSlotPtr];
   p.off_slot_list = pl->blob[forkkv::kHdrOffSlotList];
-  p.off_append = pl->blob[forkkv::kHdrOffAppend];
+  p.off_lastpage = pl->blob[forkkv::kHdrOffLastPage];
   p.max_agent_slots = pl->max_agent_slots;
   p.lora_scale = a->lora_scale;
   p.sm_scale_log2 = a->sm_scale * kLog2e;
@@ -144,7 +144,7 @@ int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hip
       if (!e) return FORKKV_EHIP;
     }
   }
-  if (pl->n_items > 0) {
+  if (pl->item_capacity > 0) {
     if (ev[0] && hipEventRecord(ev[0], stream) != hipSuccess) return FORKKV_EHIP;
     hipError_t err = pl->kernel == FORKKV_KERNEL_MFMA
                          ? forkkv::launch_decode_mfma(p, stream)
@@ -157,7 +157,7 @@ int launch_decode(forkkv_plan* pl, const forkkv::DecodeParams& p, int dtype, hip
   if (forkkv::launch_combine(p, dtype, stream) != hipSuccess) return FORKKV_EHIP;
   if (ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return FORKKV_EHIP;
   if (pl->timing && allow_timing) {
-    if (pl->n_items > 0) {
+    if (pl->item_capacity > 0) {
       pl->pending.push_back({0, ev[0], ev[1]});
     } else {
       pl->spare.push_back(ev[0]);
@@ -238,6 +238,8 @@ int forkkv_residual_attn_decode_append(const forkkv_decode_append_args* a, hipSt
   w.num_bpages = g.num_bpages;
   w.num_rpages = g.num_rpages;
   (void)hipGetLastError();
+  // the combine kernel advances the device lengths once the call has read them
+  p.advance = static_cast<int32_t*>(pl->dev) + off_lens;
   if (pl->kernel == FORKKV_KERNEL_MFMA) {
     // the split kernel stores the new rows itself, ahead of the pages that hold them
     p.k_new = a->k_new;

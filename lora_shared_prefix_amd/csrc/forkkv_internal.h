@@ -17,7 +17,7 @@ constexpr int kPage = 16;
 // One decode work item: a run of logical pages that every listed agent maps to the same
 // physical base pages, processed by one workgroup per KV head.
 //   [0] first logical page   [1] number of pages   [2] number of agents
-//   [3] bit j set: agent j's last row lies in this item's pages (decode with append)
+//   [3] reserved (0)
 //   [4 .. 4+kItemAgents) agent indices
 //   [4+kItemAgents .. 4+2*kItemAgents) partial slot of each agent; the slots of one agent
 //   are consecutive (slot_ptr[a] .. slot_ptr[a+1]), so the combine needs no slot list
@@ -28,7 +28,9 @@ constexpr int kItemInts = 4 + 2 * kItemAgents;
 enum : int {
   kHdrMagic = 0, kHdrAgents, kHdrItems, kHdrSlots, kHdrItemInts, kHdrQHeads,
   kHdrOffItems, kHdrOffLens, kHdrOffSlotPtr, kHdrOffSlotList, kHdrKernel, kHdrGroup,
-  kHdrOffAppend,  // per agent: base slot, residual slot of its last row (page * P + row)
+  kHdrOffLastPage,   // per agent: its last logical page (-1 without rows)
+  kHdrItemCapacity,  // items the launch grid covers (the items section has room for them)
+  kHdrSlotCapacity,  // split-K slots the workspace holds
   kHdrWords = 16
 };
 constexpr int32_t kPlanMagic = 0x464b5631;  // "FKV1"
@@ -38,6 +40,7 @@ struct Seq {
   bool has_res = false;
   bool closed = false;            // the last page takes no more rows (a frozen tail)
   int32_t len = 0;
+  int32_t missing = 0;            // base table entries that are -1 (evicted, not refilled)
   std::vector<int32_t> bpages, rpages;
   std::vector<int32_t> starts;    // position of row 0 of each logical page (the slot map)
 
@@ -56,11 +59,7 @@ struct Seq {
       if (starts[j] != static_cast<int32_t>(j) * kPage) return false;
     return true;
   }
-  bool missing_base() const {
-    for (int32_t pg : bpages)
-      if (pg < 0) return true;
-    return false;
-  }
+  bool missing_base() const { return missing > 0; }
 };
 
 }  // namespace forkkv
@@ -74,11 +73,21 @@ struct forkkv_pool {
   std::vector<forkkv::Seq> seqs;
 };
 
+namespace forkkv {
+// A maximal run of logical pages over which one set of agents maps the same physical page.
+struct Run {
+  std::vector<int32_t> agents;
+  int32_t lp0, lp1;  // [lp0, lp1)
+};
+}  // namespace forkkv
+
 struct forkkv_plan {
   forkkv_pool_desc geo{};   // geometry copy (orders cleared)
   void* bcache = nullptr;
   void* rcache = nullptr;
+  forkkv_plan_opts opts{};  // the options it was built with (kept by rebuilds)
   int32_t n_agents = 0, n_items = 0, n_slots = 0, num_q_heads = 0, kernel = 0;
+  int32_t item_capacity = 0, slot_capacity = 0;  // launch grid / workspace sizes (only grow)
   int32_t group = 0;        // agents per item the kernel was planned for
   bool aligned = true;      // every page of every agent starts at a multiple of P
   std::vector<int32_t> blob;
@@ -93,6 +102,15 @@ struct forkkv_plan {
   struct Timed { int kind; hipEvent_t b, e; };
   std::vector<Timed> pending;
   std::vector<hipEvent_t> spare;
+  // what a rebuild can reuse: the batch, its base page tables and the runs found in them
+  std::vector<int32_t> seq_ids;
+  std::vector<std::vector<int32_t>> bpages_seen;
+  std::vector<forkkv::Run> runs;
+  // asynchronous upload: two pinned staging buffers, each with the event of its last copy
+  void* staging[2] = {nullptr, nullptr};
+  size_t staging_bytes[2] = {0, 0};
+  hipEvent_t staged[2] = {nullptr, nullptr};
+  int next_staging = 0;
 };
 
 namespace forkkv {
@@ -132,9 +150,13 @@ struct DecodeParams {
   const void* v_new;   // [N][Hkv][d]
   const void* rk_new;  // [N][r]
   const void* rv_new;  // [N][r]
+  // decode with append: the plan's device lengths, each advanced by one by the combine
+  // kernel once the call has read them (the next call appends at the following position)
+  int32_t* advance;
+  // n_items is the launch's item capacity; the kernels read the live count from the plan
   int32_t n_agents, n_items, num_q_heads, num_kv_heads, head_dim, rank, group;
   int32_t max_pages, num_bpages, num_rpages;
-  int32_t off_items, off_lens, off_slot_ptr, off_slot_list, off_append;
+  int32_t off_items, off_lens, off_slot_ptr, off_slot_list, off_lastpage;
   int32_t max_agent_slots;  // the largest number of split-K partials of one agent
   float lora_scale, sm_scale_log2, rope_theta;
 };

@@ -123,6 +123,8 @@ residual_attn_generic(DecodeParams dp, PrefillParams pp) {
     lp_begin = 0;
     lp_end = page_of(pstart, max_pages, a_pf, last_pos) + 1;
   } else {
+    // the grid covers the plan's item capacity; items past the live count are empty
+    if (static_cast<int>(blockIdx.x) >= dp.plan[kHdrItems]) return;  // uniform per block
     const int32_t* it = dp.plan + dp.off_items + blockIdx.x * kItemInts;
     lp_begin = it[0];
     lp_end = it[0] + it[1];
@@ -482,6 +484,8 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
     const float o = Lsum > 0.f ? (acc + p.lora_scale * res) / Lsum : 0.f;
     E::st(static_cast<T*>(p.out), (size_t(a) * Hq + g) * d + tid, o);
   }
+  // decode with append: the call has read every length; the next call appends one further
+  if (p.advance && g == 0 && tid == 0) p.advance[a] += 1;
 }
 
 // The same merge for d = 128, r = 16, one wave per output row and no LDS: quarter qd of the
@@ -604,6 +608,8 @@ __global__ void __launch_bounds__(64) combine_row_kernel(DecodeParams p) {
     for (int e = 0; e < 8; ++e)
       E::st(o, e, l_t > 0.f ? (acc[e] + p.lora_scale * res[e]) / l_t : 0.f);
   }
+  // decode with append: the call has read every length; the next call appends one further
+  if (p.advance && g == 0 && lane == 0) p.advance[a] += 1;
 }
 
 // Store the chunk rows at their slots (bit-exact copies in the pool layout).  The slot of

@@ -166,7 +166,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int xcd = b & 7, s = b >> 3;
   const int h = s % Hkv;
   const int item = xcd + 8 * (s / Hkv);
-  if (item >= n_items) return;
+  // the grid covers the plan's item capacity; items past the live count are empty
+  if (item >= n_items || item >= p.plan[kHdrItems]) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
@@ -554,24 +555,29 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     if constexpr (A > 2) if (na_g == 2) f(std::integral_constant<int, 2>{});
     if constexpr (A > 1) if (na_g == 1) f(std::integral_constant<int, 1>{});
   };
-  // Decode with append: the new token of every item agent whose last row lies in this item's
+  // Decode with append: the new token of every item agent whose last page lies in this item's
   // pages is stored first -- this KV head's key and value rows, and the residual rows (the
   // same bytes from every head's workgroup) -- and the workgroup waits for the stores before
   // any page is read.  Only this item's workgroups read those pages: a row just appended sits
-  // in a page private to its agent.
+  // in a page private to its agent.  The token sits at position length - 1 (the length on
+  // the device, which the previous call advanced), in the agent's last page.
   static_assert(kThreads == 2 * kD, "one thread per key and per value element of a row");
   if (p.k_new != nullptr) {  // uniform over the grid
-    const int mask = it[3];
     uint16_t* const bw = const_cast<uint16_t*>(bcache);
     uint16_t* const rw = const_cast<uint16_t*>(rcache);
 #pragma unroll
     for (int j = 0; j < kItemAgents; ++j) {
-      if (!((mask >> j) & 1)) continue;  // uniform
+      if (j >= na) continue;  // uniform
       const int a = ia[j];
-      const int bs = p.plan[p.off_append + 2 * a], rs = p.plan[p.off_append + 2 * a + 1];
-      const int bpg = bs / kPage, rpg = rs / kPage;
-      if (bs < 0 || rs < 0 || bpg >= p.num_bpages || rpg >= p.num_rpages) continue;
-      const int brow = bs % kPage, rrow = rs % kPage;
+      const int lp_last = p.plan[p.off_lastpage + a];
+      if (lp_last < lp0 || lp_last >= lp0 + np) continue;  // uniform
+      const int row = p.plan[p.off_lens + a] - 1 - page_start(p.pstart, p.max_pages, a, lp_last);
+      // (a row past the page: the caller did not rebuild the plan after a page crossing)
+      if (row < 0 || row >= kPage) continue;
+      const int bpg = p.btab[size_t(a) * p.max_pages + lp_last];
+      const int rpg = p.rtab[size_t(a) * p.max_pages + lp_last];
+      if (bpg < 0 || rpg < 0 || bpg >= p.num_bpages || rpg >= p.num_rpages) continue;
+      const int brow = row, rrow = row;
       if (tid < kD) {
         const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (size_t(a) * Hkv + h) * kD;
         bw[(size_t(bpg) * 2 * Hkv + h) * tile + TileOrder::key(brow, tid)] = kn[tid];

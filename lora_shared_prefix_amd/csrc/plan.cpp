@@ -6,8 +6,15 @@
 // the base cache is shared globally; "3. 架构 / 方法图", Figure 6: forked agents map the
 // parent's pages).  Long runs are cut into items of a bounded number of pages whose
 // partial softmax states are merged by the combine kernel.
+//
+// A plan is step-stable: the per-step state of decode with append (each agent's length)
+// lives in the plan's device copy and the append call advances it, so successive steps
+// reuse one plan and one launch until an agent enters a new page (ForkServe README,
+// "Methods": a write allocates residual pages only).  Then forkkv_plan_rebuild redoes the
+// items in place; offsets and the launch grid come from capacities that only grow, so a
+// rebuild within them leaves a captured launch valid.
 #include <algorithm>
-#include <map>
+#include <cstring>
 #include <new>
 
 #include "forkkv_internal.h"
@@ -20,37 +27,36 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct Run {
-  std::vector<int32_t> agents;
-  int32_t lp0, lp1;  // [lp0, lp1)
-};
+using forkkv::Run;
 
-}  // namespace
-
-
-extern "C" {
-
-int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
-                       int32_t num_q_heads, const forkkv_plan_opts* opts, forkkv_plan** out) {
-  if (!p || !out || n < 0 || (n > 0 && !seqs)) return FORKKV_EINVAL;
+// Build the plan of seqs into *pl (host side only: blob, sizes, capacities).  min_items and
+// min_slots are capacities the plan must keep (those of the plan being rebuilt, or 0).
+// prev (nullable): the plan being rebuilt; its runs up to the first logical page whose base
+// pages changed are kept, and the scan resumes there (a decode step only changes the
+// agents' last pages).
+int build(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n, int32_t num_q_heads,
+          const forkkv_plan_opts& o, int32_t min_items, int32_t min_slots,
+          const forkkv_plan* prev, forkkv_plan* pl) {
   const forkkv_pool_desc& g = p->desc;
   if (num_q_heads < g.num_kv_heads || num_q_heads % g.num_kv_heads) return FORKKV_EINVAL;
   const int group_q = num_q_heads / g.num_kv_heads;
   std::vector<const forkkv::Seq*> S(n);
+  std::vector<int32_t> np(n);
   int32_t max_np = 0;
-  for (int32_t a = 0; a < n; ++a) {
-    if (seqs[a] < 0 || static_cast<size_t>(seqs[a]) >= p->seqs.size()) return FORKKV_EINVAL;
-    S[a] = &p->seqs[seqs[a]];
-    if (!S[a]->alive || !S[a]->has_res) return FORKKV_EINVAL;
-    max_np = std::max<int32_t>(max_np, static_cast<int32_t>(S[a]->bpages.size()));
+  {
+    for (int32_t a = 0; a < n; ++a) {
+      if (seqs[a] < 0 || static_cast<size_t>(seqs[a]) >= p->seqs.size()) return FORKKV_EINVAL;
+      S[a] = &p->seqs[seqs[a]];
+      if (!S[a]->alive || !S[a]->has_res) return FORKKV_EINVAL;
+      np[a] = static_cast<int32_t>(S[a]->bpages.size());
+      max_np = std::max(max_np, np[a]);
+    }
   }
   // a partial hit (an evicted base page) must be refilled before it can be attended to
   for (int32_t a = 0; a < n; ++a)
     if (S[a]->missing_base()) return FORKKV_ESTATE;
   bool aligned = true;
   for (int32_t a = 0; a < n; ++a) aligned = aligned && S[a]->aligned();
-  forkkv_plan_opts o{};
-  if (opts) o = *opts;
   int kernel = o.kernel;
   const bool mfma_ok = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, group_q);
   if (kernel == FORKKV_KERNEL_AUTO) kernel = mfma_ok ? FORKKV_KERNEL_MFMA : FORKKV_KERNEL_GENERIC;
@@ -70,45 +76,121 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   } else {
     return FORKKV_EINVAL;
   }
-  if (o.max_agents_per_item < 0 || o.pages_per_item < 0) return FORKKV_EINVAL;
+  if (o.max_agents_per_item < 0 || o.pages_per_item < 0 || o.spare_items < 0) return FORKKV_EINVAL;
   if (o.max_agents_per_item > 0) cap = std::min(cap, o.max_agents_per_item);
-  int ppi = o.pages_per_item > 0 ? o.pages_per_item : 16;
+  const int ppi = o.pages_per_item > 0 ? o.pages_per_item : 16;
 
-  // 1. Maximal runs of logical pages with an identical set of agents sharing the page.
+  // 1. Maximal runs of logical pages over which one set of agents maps the same physical
+  //    page.  A run open at lp - 1 continues at lp when all its agents map one physical page
+  //    there and no other agent of the batch maps that page; the agents left over start new
+  //    runs, one per physical page, ordered by their first agent.  Per logical page: one
+  //    agreement check per agent of an open run, one holder count per run (and per agent
+  //    outside the agreeing runs), flat arrays, no allocation in the common case.
+  std::vector<const int32_t*> bp(n);
+  for (int32_t a = 0; a < n; ++a) bp[a] = S[a]->bpages.data();
   std::vector<Run> runs;
-  std::map<std::vector<int32_t>, size_t> open;  // agent set -> run index still open
-  for (int32_t lp = 0; lp < max_np; ++lp) {
-    std::map<int32_t, std::vector<int32_t>> by_page;  // physical page -> agents (ascending)
-    for (int32_t a = 0; a < n; ++a)
-      if (lp < static_cast<int32_t>(S[a]->bpages.size())) by_page[S[a]->bpages[lp]].push_back(a);
-    std::map<std::vector<int32_t>, size_t> next_open;
-    // order groups by their first agent for determinism
-    std::vector<std::vector<int32_t>> groups;
-    for (auto& kv : by_page) groups.push_back(kv.second);
+  std::vector<int32_t> open, next_open, pending, agree;
+  std::vector<int32_t> holders(g.num_bpages, 0);  // groups mapping a page at lp (reset after)
+  std::vector<char> taken(n, 0);
+  int32_t lp_start = 0;
+  const bool reuse = prev && aligned && prev->seq_ids.size() == static_cast<size_t>(n) &&
+                     std::equal(seqs, seqs + n, prev->seq_ids.begin()) &&
+                     prev->bpages_seen.size() == static_cast<size_t>(n);
+  if (reuse) {
+    // the first logical page at which any agent's base pages differ from the last build
+    lp_start = max_np;
+    for (int32_t a = 0; a < n; ++a) {
+      const std::vector<int32_t>& old = prev->bpages_seen[a];
+      const int32_t common = std::min<int32_t>(np[a], static_cast<int32_t>(old.size()));
+      int32_t k = static_cast<int32_t>(
+          std::mismatch(bp[a], bp[a] + common, old.begin()).first - bp[a]);
+      if (k == common && np[a] == static_cast<int32_t>(old.size())) k = max_np;
+      lp_start = std::min(lp_start, k);
+    }
+    // runs that began before lp_start are kept (cut at lp_start); those open at lp_start - 1
+    // are the open set the scan resumes with
+    for (const Run& r : prev->runs) {
+      if (r.lp0 >= lp_start) break;  // runs are in order of their first page
+      runs.push_back(r);
+      if (r.lp1 >= lp_start) {
+        runs.back().lp1 = lp_start;
+        open.push_back(static_cast<int32_t>(runs.size()) - 1);
+      }
+    }
+  }
+  for (int32_t lp = lp_start; lp < max_np; ++lp) {
     // Under a slot map the kernels take a shared page's start and row count from one of its
     // holders: every holder must see the page at the same start with the same last row (the
     // pool only ever shares full pages and frozen tails, so this always holds).
-    if (!aligned)
-      for (const auto& ag : groups) {
-        const forkkv::Seq& s0 = *S[ag[0]];
-        for (int32_t a : ag) {
-          const forkkv::Seq& s = *S[a];
-          if (s.starts[lp] != s0.starts[lp] || s.rows(lp) != s0.rows(lp)) return FORKKV_ESTATE;
+    if (!aligned) {
+      for (int32_t a = 0; a < n; ++a) {
+        if (lp >= np[a]) continue;
+        for (int32_t b = a + 1; b < n; ++b) {
+          if (lp >= np[b] || bp[b][lp] != bp[a][lp]) continue;
+          if (S[b]->starts[lp] != S[a]->starts[lp] || S[b]->rows(lp) != S[a]->rows(lp))
+            return FORKKV_ESTATE;
         }
       }
-    std::sort(groups.begin(), groups.end(),
-              [](const std::vector<int32_t>& x, const std::vector<int32_t>& y) { return x[0] < y[0]; });
-    for (auto& ag : groups) {
-      auto it = open.find(ag);
-      if (it != open.end()) {
-        runs[it->second].lp1 = lp + 1;
-        next_open[ag] = it->second;
-      } else {
-        runs.push_back(Run{ag, lp, lp + 1});
-        next_open[ag] = runs.size() - 1;
-      }
     }
+    // (a) open runs whose agents still agree on one page
+    agree.clear();
+    for (int32_t ri : open) {
+      const Run& r = runs[ri];
+      const int32_t a0 = r.agents[0];
+      if (lp >= np[a0]) continue;
+      const int32_t pg = bp[a0][lp];
+      bool same = true;
+      for (size_t k = 1; same && k < r.agents.size(); ++k) {
+        const int32_t a = r.agents[k];
+        same = lp < np[a] && bp[a][lp] == pg;
+      }
+      if (!same) continue;
+      agree.push_back(ri);
+      ++holders[pg];
+      for (int32_t a : r.agents) taken[a] = 1;
+    }
+    // (b) the other agents' pages; (c) a run continues if nobody else maps its page
+    pending.clear();
+    for (int32_t a = 0; a < n; ++a)
+      if (lp < np[a] && !taken[a]) {
+        pending.push_back(a);
+        ++holders[bp[a][lp]];
+      }
+    next_open.clear();
+    for (int32_t ri : agree) {
+      const Run& r = runs[ri];
+      if (holders[bp[r.agents[0]][lp]] == 1) {
+        runs[ri].lp1 = lp + 1;
+        next_open.push_back(ri);
+      } else {
+        pending.insert(pending.end(), r.agents.begin(), r.agents.end());
+      }
+      for (int32_t a : r.agents) taken[a] = 0;
+    }
+    // (d) new runs: the pending agents grouped by physical page (agents ascending within a
+    //     group), groups in the order of their first agent
+    const size_t first_new = runs.size();
+    if (!pending.empty()) {
+      std::sort(pending.begin(), pending.end(), [&](int32_t x, int32_t y) {
+        const int32_t px = bp[x][lp], py = bp[y][lp];
+        return px != py ? px < py : x < y;
+      });
+      for (size_t i = 0; i < pending.size();) {
+        size_t j = i;
+        Run r{{}, lp, lp + 1};
+        while (j < pending.size() && bp[pending[j]][lp] == bp[pending[i]][lp])
+          r.agents.push_back(pending[j++]);
+        runs.push_back(std::move(r));
+        i = j;
+      }
+      std::sort(runs.begin() + first_new, runs.end(),
+                [](const Run& x, const Run& y) { return x.agents[0] < y.agents[0]; });
+    }
+    for (size_t k = first_new; k < runs.size(); ++k) next_open.push_back(static_cast<int32_t>(k));
     open.swap(next_open);
+    // (e) reset the holder counts touched at this page
+    for (int32_t ri : agree) holders[bp[runs[ri].agents[0]][lp]] = 0;
+    for (int32_t a : pending) holders[bp[a][lp]] = 0;
   }
 
   // 2. Cut runs into items: agent chunks of <= cap, page chunks of <= item_pages(chunk).
@@ -169,19 +251,17 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
       const int32_t item_pages =
           kernel == FORKKV_KERNEL_MFMA ? pages_per_wave(na) * n_sub_of(na) : ppi;
       for (int32_t lp = r.lp0; lp < r.lp1; lp += item_pages) {
-        const int32_t np = std::min(item_pages, r.lp1 - lp);
+        const int32_t npg = std::min(item_pages, r.lp1 - lp);
         int32_t it[kItemInts];
         std::fill(it, it + kItemInts, -1);
         it[0] = lp;
-        it[1] = np;
+        it[1] = npg;
         it[2] = na;
-        it[3] = 0;
+        it[3] = 0;  // reserved
         for (int32_t j = 0; j < na; ++j) {
           const int32_t a = r.agents[a0 + j];
           it[4 + j] = a;
           it[4 + kItemAgents + j] = per_agent[a]++;  // index within the agent, for now
-          const int32_t last = static_cast<int32_t>(S[a]->bpages.size()) - 1;
-          if (S[a]->len > 0 && last >= lp && last < lp + np) it[3] |= 1 << j;
         }
         n_slots += na;
         items.insert(items.end(), it, it + kItemInts);
@@ -200,15 +280,28 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
     int32_t* it = items.data() + size_t(i) * kItemInts;
     for (int32_t j = 0; j < it[2]; ++j) it[4 + kItemAgents + j] += slot_ptr[it[4 + j]];
   }
+  // capacities: the launch grid covers item_capacity items and the workspace slot_capacity
+  // slots, so a rebuild that stays within both keeps the launch (and a captured graph) valid
+  const int32_t spare = o.spare_items > 0 ? o.spare_items : n;
+  int32_t item_cap = std::max(min_items, n_items);
+  if (n_items > min_items) item_cap = n_items + spare;
+  int32_t slot_cap = std::max(min_slots, n_slots);
+  if (n_slots > min_slots) slot_cap = n_slots + spare * cap;
 
-  forkkv_plan* pl = new (std::nothrow) forkkv_plan();
-  if (!pl) return FORKKV_ENOMEM;
+  pl->seq_ids.assign(seqs, seqs + n);
+  pl->bpages_seen.resize(n);
+  for (int32_t a = 0; a < n; ++a) pl->bpages_seen[a].assign(bp[a], bp[a] + np[a]);
+  pl->runs = std::move(runs);
   pl->geo = g;
+  pl->geo.bpage_order = pl->geo.rpage_order = nullptr;
   pl->bcache = p->bcache;
   pl->rcache = p->rcache;
+  pl->opts = o;
   pl->n_agents = n;
   pl->n_items = n_items;
   pl->n_slots = n_slots;
+  pl->item_capacity = item_cap;
+  pl->slot_capacity = slot_cap;
   pl->num_q_heads = num_q_heads;
   pl->kernel = kernel;
   pl->group = cap;
@@ -226,33 +319,94 @@ int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
   b[forkkv::kHdrQHeads] = num_q_heads;
   b[forkkv::kHdrKernel] = kernel;
   b[forkkv::kHdrGroup] = cap;
+  b[forkkv::kHdrItemCapacity] = item_cap;
+  b[forkkv::kHdrSlotCapacity] = slot_cap;
   b[forkkv::kHdrOffItems] = static_cast<int32_t>(b.size());
   b.insert(b.end(), items.begin(), items.end());
+  b.resize(b.size() + size_t(item_cap - n_items) * kItemInts, 0);  // room for later items
   b[forkkv::kHdrOffLens] = static_cast<int32_t>(b.size());
   for (int32_t a = 0; a < n; ++a) b.push_back(S[a]->len);
   b[forkkv::kHdrOffSlotPtr] = static_cast<int32_t>(b.size());
   b.insert(b.end(), slot_ptr.begin(), slot_ptr.end());
   b[forkkv::kHdrOffSlotList] = static_cast<int32_t>(b.size());  // empty: slots are ranges
-  // slots of each agent's last row: where decode with append stores the new token
-  b[forkkv::kHdrOffAppend] = static_cast<int32_t>(b.size());
-  for (int32_t a = 0; a < n; ++a) {
-    const forkkv::Seq& sq = *S[a];
-    int32_t bs = -1, rs = -1;
-    if (sq.len > 0) {
-      const size_t last = sq.bpages.size() - 1;
-      const int32_t row = sq.len - 1 - sq.starts[last];
-      bs = sq.bpages[last] * forkkv::kPage + row;
-      rs = sq.rpages[last] * forkkv::kPage + row;
-    }
-    b.push_back(bs);
-    b.push_back(rs);
-  }
+  // last logical page of each agent: decode with append stores the new token there, at row
+  // (length - 1) - (page start), with the length read on the device
+  b[forkkv::kHdrOffLastPage] = static_cast<int32_t>(b.size());
+  for (int32_t a = 0; a < n; ++a) b.push_back(S[a]->len > 0 ? np[a] - 1 : -1);
 
-  const size_t rows = size_t(n_slots) * num_q_heads;
+  const size_t rows = size_t(slot_cap) * num_q_heads;
   pl->ws_off_acc = align256(rows * 2 * sizeof(float));
   pl->ws_off_accr = pl->ws_off_acc + align256(rows * g.head_dim * sizeof(float));
   pl->workspace_bytes = pl->ws_off_accr + align256(rows * g.rank * sizeof(float));
+  return FORKKV_OK;
+}
+
+void release_staging(forkkv_plan* pl) {
+  for (int k = 0; k < 2; ++k) {
+    if (pl->staged[k]) {
+      (void)hipEventSynchronize(pl->staged[k]);
+      (void)hipEventDestroy(pl->staged[k]);
+      pl->staged[k] = nullptr;
+    }
+    if (pl->staging[k]) (void)hipHostFree(pl->staging[k]);
+    pl->staging[k] = nullptr;
+    pl->staging_bytes[k] = 0;
+  }
+}
+
+}  // namespace
+
+
+extern "C" {
+
+int forkkv_plan_decode(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n,
+                       int32_t num_q_heads, const forkkv_plan_opts* opts, forkkv_plan** out) {
+  if (!p || !out || n < 0 || (n > 0 && !seqs)) return FORKKV_EINVAL;
+  forkkv_plan_opts o{};
+  if (opts) o = *opts;
+  forkkv_plan* pl = new (std::nothrow) forkkv_plan();
+  if (!pl) return FORKKV_ENOMEM;
+  const int rc = build(p, seqs, n, num_q_heads, o, 0, 0, nullptr, pl);
+  if (rc != FORKKV_OK) {
+    delete pl;
+    return rc;
+  }
   *out = pl;
+  return FORKKV_OK;
+}
+
+int forkkv_plan_rebuild(forkkv_plan* pl, const forkkv_pool* p, const forkkv_seq* seqs,
+                        int32_t n, int32_t* same_launch) {
+  if (!pl || !p || n < 0 || (n > 0 && !seqs)) return FORKKV_EINVAL;
+  forkkv_plan fresh;
+  const int rc = build(p, seqs, n, pl->num_q_heads, pl->opts, pl->item_capacity,
+                       pl->slot_capacity, pl, &fresh);
+  if (rc != FORKKV_OK) return rc;  // the plan is unchanged
+  const bool same = fresh.n_agents == pl->n_agents && fresh.item_capacity == pl->item_capacity &&
+                    fresh.slot_capacity == pl->slot_capacity && fresh.kernel == pl->kernel &&
+                    fresh.aligned == pl->aligned && fresh.group == pl->group;
+  pl->geo = fresh.geo;
+  pl->bcache = fresh.bcache;
+  pl->rcache = fresh.rcache;
+  pl->n_agents = fresh.n_agents;
+  pl->n_items = fresh.n_items;
+  pl->n_slots = fresh.n_slots;
+  pl->item_capacity = fresh.item_capacity;
+  pl->slot_capacity = fresh.slot_capacity;
+  pl->kernel = fresh.kernel;
+  pl->group = fresh.group;
+  pl->aligned = fresh.aligned;
+  pl->blob.swap(fresh.blob);
+  pl->seq_ids.swap(fresh.seq_ids);
+  pl->bpages_seen.swap(fresh.bpages_seen);
+  pl->runs.swap(fresh.runs);
+  pl->workspace_bytes = fresh.workspace_bytes;
+  pl->ws_off_acc = fresh.ws_off_acc;
+  pl->ws_off_accr = fresh.ws_off_accr;
+  pl->max_pages_needed = fresh.max_pages_needed;
+  pl->max_agent_slots = fresh.max_agent_slots;
+  pl->dev = nullptr;  // the device copy is stale until the next upload
+  if (same_launch) *same_launch = same ? 1 : 0;
   return FORKKV_OK;
 }
 
@@ -266,6 +420,8 @@ int forkkv_plan_get_info(const forkkv_plan* pl, forkkv_plan_info* info) {
   info->num_q_heads = pl->num_q_heads;
   info->plan_bytes = pl->blob.size() * sizeof(int32_t);
   info->workspace_bytes = pl->workspace_bytes;
+  info->item_capacity = pl->item_capacity;
+  info->slot_capacity = pl->slot_capacity;
   return FORKKV_OK;
 }
 
@@ -277,11 +433,30 @@ int forkkv_plan_export(const forkkv_plan* pl, int32_t* host_blob) {
 
 int forkkv_plan_upload(forkkv_plan* pl, void* dev, hipStream_t stream) {
   if (!pl || !dev) return FORKKV_EINVAL;
-  if (hipMemcpyAsync(dev, pl->blob.data(), pl->blob.size() * sizeof(int32_t),
-                     hipMemcpyHostToDevice, stream) != hipSuccess)
+  // Two pinned staging buffers alternate; the copy out of one must have run before it is
+  // refilled, two uploads later (in a serving loop, long done).  No stream-wide wait.
+  const int k = pl->next_staging;
+  const size_t bytes = pl->blob.size() * sizeof(int32_t);
+  if (pl->staged[k] && hipEventSynchronize(pl->staged[k]) != hipSuccess) return FORKKV_EHIP;
+  if (pl->staging_bytes[k] < bytes) {
+    if (pl->staging[k]) (void)hipHostFree(pl->staging[k]);
+    pl->staging[k] = nullptr;
+    pl->staging_bytes[k] = 0;
+    void* h = nullptr;
+    if (hipHostMalloc(&h, bytes, hipHostMallocDefault) != hipSuccess) return FORKKV_EHIP;
+    pl->staging[k] = h;
+    pl->staging_bytes[k] = bytes;
+  }
+  if (!pl->staged[k] &&
+      hipEventCreateWithFlags(&pl->staged[k], hipEventDisableTiming) != hipSuccess) {
+    pl->staged[k] = nullptr;
     return FORKKV_EHIP;
-  // the host blob must stay valid until the copy has run: wait for it
-  if (hipStreamSynchronize(stream) != hipSuccess) return FORKKV_EHIP;
+  }
+  std::memcpy(pl->staging[k], pl->blob.data(), bytes);
+  if (hipMemcpyAsync(dev, pl->staging[k], bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return FORKKV_EHIP;
+  if (hipEventRecord(pl->staged[k], stream) != hipSuccess) return FORKKV_EHIP;
+  pl->next_staging = 1 - k;
   pl->dev = dev;
   return FORKKV_OK;
 }
@@ -293,6 +468,7 @@ int forkkv_plan_destroy(forkkv_plan* pl) {
     (void)hipEventDestroy(t.e);
   }
   for (hipEvent_t e : pl->spare) (void)hipEventDestroy(e);
+  release_staging(pl);
   delete pl;
   return FORKKV_OK;
 }

@@ -184,6 +184,40 @@ int forkkv_seq_append(forkkv_pool* p, forkkv_seq h, int32_t n, int32_t* bslots,
   return FORKKV_OK;
 }
 
+int forkkv_seq_append_batch(forkkv_pool* p, const forkkv_seq* seqs, int32_t n, int32_t rows,
+                            int32_t* bslots, int32_t* rslots, forkkv_cow_op* cows,
+                            int32_t* new_pages) {
+  if (!p || n < 0 || rows < 0 || (n > 0 && !seqs)) return FORKKV_EINVAL;
+  // validate everything and count the pages the whole batch needs before changing anything
+  int64_t need_b = 0, need_r = 0;
+  std::vector<char> seen(p->seqs.size(), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get_seq(const_cast<const forkkv_pool*>(p), seqs[i]);
+    if (!s || seen[seqs[i]]) return FORKKV_EINVAL;
+    seen[seqs[i]] = 1;
+    if (s->missing_base()) return FORKKV_ESTATE;
+    if (int64_t(s->len) + rows > INT32_MAX / 2) return FORKKV_EINVAL;
+    const int32_t room = s->room();
+    const int32_t grow = ceil_div(std::max<int64_t>(0, int64_t(rows) - room), kPage);
+    const size_t last = s->bpages.empty() ? 0 : s->bpages.size() - 1;
+    const bool need_cow =
+        rows > 0 && room > 0 && s->rows(last) > 0 && p->ref_b[s->bpages[last]] > 1;
+    need_b += grow + (need_cow ? 1 : 0);
+    need_r += s->has_res ? grow : 0;
+  }
+  if (need_b > static_cast<int64_t>(p->free_b.size()) ||
+      need_r > static_cast<int64_t>(p->free_r.size()))
+    return FORKKV_ENOMEM;
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = forkkv_seq_append(p, seqs[i], rows, bslots ? bslots + size_t(i) * rows : nullptr,
+                                     rslots ? rslots + size_t(i) * rows : nullptr,
+                                     cows ? cows + i : nullptr);
+    if (rc != FORKKV_OK) return rc;  // (cannot happen after the checks above)
+  }
+  if (new_pages) *new_pages = static_cast<int32_t>(need_b);
+  return FORKKV_OK;
+}
+
 int forkkv_fork(forkkv_pool* p, forkkv_seq parent, int32_t alias_len, forkkv_seq* child,
                 forkkv_cow_op* cow) {
   return forkkv_fork_ex(p, parent, alias_len, FORKKV_FORK_PACK, 0, child, cow);
@@ -282,7 +316,10 @@ int forkkv_evict_bpages(forkkv_pool* p, const int32_t* pages, int32_t n) {
   for (Seq& s : p->seqs) {
     if (!s.alive) continue;
     for (int32_t& pg : s.bpages)
-      if (pg >= 0 && gone[pg]) pg = -1;
+      if (pg >= 0 && gone[pg]) {
+        pg = -1;
+        ++s.missing;
+      }
   }
   for (int32_t i = 0; i < n; ++i) {
     p->ref_b[pages[i]] = 0;
@@ -314,7 +351,10 @@ int forkkv_refill_bpages(forkkv_pool* p, const forkkv_seq* seqs, int32_t n, int3
   for (int32_t j = lp0; j < lp1; ++j) {
     const int32_t pg = take(p->free_b, p->ref_b);
     p->ref_b[pg] = n;
-    for (Seq* s : ss) s->bpages[j] = pg;
+    for (Seq* s : ss) {
+      s->bpages[j] = pg;
+      --s->missing;
+    }
     if (new_pages) new_pages[j - lp0] = pg;
   }
   return FORKKV_OK;

@@ -44,13 +44,14 @@ class Stats(C.Structure):
 
 class PlanOpts(C.Structure):
     _fields_ = [("kernel", C.c_int32), ("max_agents_per_item", C.c_int32),
-                ("pages_per_item", C.c_int32)]
+                ("pages_per_item", C.c_int32), ("spare_items", C.c_int32)]
 
 
 class PlanInfo(C.Structure):
     _fields_ = [("n_agents", C.c_int32), ("n_items", C.c_int32), ("n_slots", C.c_int32),
                 ("kernel", C.c_int32), ("item_ints", C.c_int32), ("num_q_heads", C.c_int32),
-                ("plan_bytes", C.c_size_t), ("workspace_bytes", C.c_size_t)]
+                ("plan_bytes", C.c_size_t), ("workspace_bytes", C.c_size_t),
+                ("item_capacity", C.c_int32), ("slot_capacity", C.c_int32)]
 
 
 class DecodeArgs(C.Structure):
@@ -107,6 +108,8 @@ _SIGS = {
     "forkkv_refcounts": (C.c_int, [C.c_void_p, C.c_int32, _i32p]),
     "forkkv_cow_copy": (C.c_int, [C.c_void_p, C.POINTER(CowOp), C.c_int32, C.c_void_p]),
     "forkkv_plan_decode": (C.c_int, [C.c_void_p, _i32p, C.c_int32, C.c_int32, C.POINTER(PlanOpts), C.POINTER(C.c_void_p)]),
+    "forkkv_plan_rebuild": (C.c_int, [C.c_void_p, C.c_void_p, _i32p, C.c_int32, _i32p]),
+    "forkkv_seq_append_batch": (C.c_int, [C.c_void_p, _i32p, C.c_int32, C.c_int32, _i32p, _i32p, C.POINTER(CowOp), _i32p]),
     "forkkv_plan_get_info": (C.c_int, [C.c_void_p, C.POINTER(PlanInfo)]),
     "forkkv_plan_export": (C.c_int, [C.c_void_p, _i32p]),
     "forkkv_plan_upload": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
@@ -219,6 +222,21 @@ class Pool:
             return None, None, cow_t
         return list(bs)[:n], list(rs)[:n], cow_t
 
+    def append_batch(self, seqs, n, want_slots=False):
+        """Reserve n rows at the end of each sequence of `seqs` (distinct), all or nothing.
+        Returns (new base pages taken, [cow ops], bslots or None, rslots or None); a nonzero
+        page count means some sequence entered a new page (a decode plan needs a rebuild)."""
+        k = len(seqs)
+        bs = (C.c_int32 * max(k * n, 1))() if want_slots else None
+        rs = (C.c_int32 * max(k * n, 1))() if want_slots else None
+        cows = (CowOp * max(k, 1))()
+        pages = C.c_int32()
+        _check(lib().forkkv_seq_append_batch(self.handle, _i32_array(seqs), k, n, bs, rs, cows,
+                                             C.byref(pages)), "forkkv_seq_append_batch")
+        cow_list = [(c.src_bpage, c.dst_bpage, c.n_rows) for c in cows[:k] if c.n_rows]
+        return (pages.value, cow_list, list(bs)[:k * n] if want_slots else None,
+                list(rs)[:k * n] if want_slots else None)
+
     def fork(self, parent, alias_len, mode=None, suffix_hint=0):
         """Fork (mode None: forkkv_fork, i.e. pack; else forkkv_fork_ex with FORK_*)."""
         child, cow = C.c_int32(), CowOp()
@@ -320,8 +338,8 @@ class Pool:
 
 class Plan:
     def __init__(self, pool: Pool, seqs, num_q_heads, kernel=KERNEL_AUTO, max_agents_per_item=0,
-                 pages_per_item=0):
-        opts = PlanOpts(kernel, max_agents_per_item, pages_per_item)
+                 pages_per_item=0, spare_items=0):
+        opts = PlanOpts(kernel, max_agents_per_item, pages_per_item, spare_items)
         h = C.c_void_p()
         _check(lib().forkkv_plan_decode(pool.handle, _i32_array(seqs), len(seqs), num_q_heads,
                                         C.byref(opts), C.byref(h)), "forkkv_plan_decode")
@@ -332,6 +350,17 @@ class Plan:
         self.info = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
         self.dev = None
 
+    def rebuild(self, seqs):
+        """Rebuild in place from the pool's current state; returns True when a decode launch
+        captured before stays valid once the plan is uploaded to the same buffer."""
+        same = C.c_int32()
+        _check(lib().forkkv_plan_rebuild(self.handle, self.pool.handle, _i32_array(seqs),
+                                         len(seqs), C.byref(same)), "forkkv_plan_rebuild")
+        info = PlanInfo()
+        _check(lib().forkkv_plan_get_info(self.handle, C.byref(info)), "forkkv_plan_get_info")
+        self.info = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+        return bool(same.value)
+
     def blob(self):
         n = self.info["plan_bytes"] // 4
         out = (C.c_int32 * n)()
@@ -339,9 +368,12 @@ class Plan:
         return list(out)
 
     def upload(self, stream=None):
+        """Copy the blob to the device (asynchronously on the stream).  The device buffer is
+        kept while it is large enough, so a captured launch keeps its address."""
         import torch
         n = self.info["plan_bytes"] // 4
-        self.dev = torch.empty(n, dtype=torch.int32, device="cuda")
+        if self.dev is None or self.dev.numel() < n:
+            self.dev = torch.empty(n, dtype=torch.int32, device="cuda")
         _check(lib().forkkv_plan_upload(self.handle, _ptr(self.dev), _stream(stream)),
                "forkkv_plan_upload")
         return self

@@ -58,24 +58,82 @@ class DeviceBatch:
         if plan:
             self.make_plan(kernel, pages_per_item, max_agents_per_item, stream)
 
-    def refresh_tables(self, extra_pages=0):
+    def refresh_tables(self, extra_pages=0, inplace=False):
         """Upload the block tables and, when a sequence holds a frozen tail, the page start
-        table (the slot map; ``pstart`` is None for aligned batches)."""
+        table (the slot map; ``pstart`` is None for aligned batches).  ``extra_pages`` leaves
+        room for later pages; ``inplace`` writes into the device tables already there (same
+        width, so that a captured launch keeps their addresses)."""
+        self._st = None  # next_step's view of the last pages is recomputed
         pages = [self.pool.pages(h) for h in self.handles]
-        self.max_pages = max(1, max(pages, default=1) + extra_pages)
+        width = max(1, max(pages, default=1) + extra_pages)
+        if inplace:
+            assert width <= self.max_pages, "the tables have no room for the new pages"
+            width = self.max_pages
+        self.max_pages = width
         bt, rt, self.lens = self.pool.tables(self.handles, self.max_pages)
         self.btab_host = np.array(bt, dtype=np.int32).reshape(len(self.handles), self.max_pages)
         self.rtab_host = np.array(rt, dtype=np.int32).reshape(len(self.handles), self.max_pages)
-        self.btab = torch.from_numpy(self.btab_host).to(self.device)
-        self.rtab = torch.from_numpy(self.rtab_host).to(self.device)
         st, aligned = self.pool.starts(self.handles, self.max_pages)
         self.pstart_host = np.array(st, dtype=np.int32).reshape(len(self.handles), self.max_pages)
+        if inplace:
+            self.btab.copy_(torch.from_numpy(self.btab_host))
+            self.rtab.copy_(torch.from_numpy(self.rtab_host))
+            if self.pstart is not None:
+                self.pstart.copy_(torch.from_numpy(self.pstart_host))
+            return
+        self.btab = torch.from_numpy(self.btab_host).to(self.device)
+        self.rtab = torch.from_numpy(self.rtab_host).to(self.device)
         self.pstart = None if aligned else torch.from_numpy(self.pstart_host).to(self.device)
 
+    def next_step(self, stream=None):
+        """Decode with append, between two steps: reserve each agent's next token on the host
+        (one batched call) and, when that took an agent into a new page or needed a
+        copy-on-write, run the copies, update the device tables in place and rebuild and
+        re-upload the plan (asynchronously).  Returns (same, cows): ``same`` is True when a
+        launch captured earlier stays valid (always, within the plan's capacities and the
+        tables' room); ``cows`` the row copies that were run."""
+        st = self._step_state()
+        rc = fk.lib().forkkv_seq_append_batch(self.pool.handle, st["seqs"], st["n"], 1,
+                                              st["bslots"], st["rslots"], st["cows"],
+                                              fk.C.byref(st["pages"]))
+        if rc != fk.OK:
+            raise fk.ForkKVError(rc, "forkkv_seq_append_batch")
+        cows = [(c.src_bpage, c.dst_bpage, c.n_rows) for c in st["cows"] if c.n_rows]
+        if cows:
+            self.pool.cow_copy(cows, stream)
+        self.lens = [n + 1 for n in self.lens]
+        if not st["pages"].value and not cows:
+            return True, cows
+        # patch the host tables where a token opened a page (row 0) or the last page was
+        # copied, then copy them to the device tables in place
+        for a in range(st["n"]):
+            page, row = divmod(st["bslots"][a], fk.PAGE)
+            lp = st["last"][a]
+            if row == 0 or lp < 0:
+                lp += 1
+                st["last"][a] = lp
+                if self.pstart is not None:
+                    self.pstart_host[a, lp] = self.lens[a] - 1
+            assert lp < self.max_pages, "the tables have no room for the new pages"
+            self.btab_host[a, lp] = page
+            self.rtab_host[a, lp] = st["rslots"][a] // fk.PAGE
+        self.btab.copy_(torch.from_numpy(self.btab_host))
+        self.rtab.copy_(torch.from_numpy(self.rtab_host))
+        if self.pstart is not None:
+            self.pstart.copy_(torch.from_numpy(self.pstart_host))
+        same = self.plan.rebuild(self.handles)
+        dev = self.plan.dev.data_ptr()
+        self.plan.upload(stream)
+        same = same and self.plan.dev.data_ptr() == dev
+        if self.plan.info["workspace_bytes"] > self.workspace.numel():
+            self.workspace = self.plan.workspace()
+            same = False
+        return same, cows
+
     def make_plan(self, kernel=fk.KERNEL_AUTO, pages_per_item=0, max_agents_per_item=0,
-                  stream=None):
+                  stream=None, spare_items=0):
         self.plan = fk.Plan(self.pool, self.handles, self.g["num_q_heads"], kernel,
-                            max_agents_per_item, pages_per_item).upload(stream)
+                            max_agents_per_item, pages_per_item, spare_items).upload(stream)
         self.workspace = self.plan.workspace()
         return self.plan
 
@@ -95,6 +153,18 @@ class DeviceBatch:
                                        rope_theta, rows["k_new"], rows["v_new"], rows["rk_new"],
                                        rows["rv_new"], stream, pstart=self.pstart)
         return out
+
+    def _step_state(self):
+        """ctypes buffers of next_step, made once per batch (and the agents' last pages)."""
+        st = getattr(self, "_st", None)
+        if st is None or st["n"] != len(self.handles):
+            n = len(self.handles)
+            last = [int((self.btab_host[a] >= 0).sum()) - 1 for a in range(n)]
+            st = dict(n=n, seqs=fk._i32_array(self.handles), bslots=(fk.C.c_int32 * n)(),
+                      rslots=(fk.C.c_int32 * n)(), cows=(fk.CowOp * n)(),
+                      pages=fk.C.c_int32(), last=last)
+            self._st = st
+        return st
 
     # ---- chunked prefill ---------------------------------------------------------------
     def reserve_chunk(self, chunk_len):

@@ -192,23 +192,20 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
         items_of.setdefault(page, set()).add(i)
     for page, hs_ in holders.items():
         assert len(items_of[page]) == -(-len(hs_) // cap), (page, len(hs_), cap)
-    # decode with append: item bit j marks agent j's last page; the append section holds the
-    # base and residual slot (page * 16 + row) of every agent's last row
-    off_app = blob[12]
+    # decode with append: the last-page section holds each agent's last logical page (the
+    # kernels store the new token there, at row length - 1 - page start); word 3 of an item
+    # is reserved
+    off_last = blob[12]
     for i in range(n_items):
         it = blob[off_items + i * ITEM_INTS: off_items + (i + 1) * ITEM_INTS]
-        lp0, npg, na = it[:3]
-        for j, a in enumerate(it[4:4 + na]):
-            last = -(-lens[a] // 16) - 1
-            assert bool((it[3] >> j) & 1) == (lens[a] > 0 and lp0 <= last < lp0 + npg)
-        assert it[3] >> na == 0
+        assert it[3] == 0
     for a in range(n_agents):
-        bs, rs = blob[off_app + 2 * a], blob[off_app + 2 * a + 1]
-        if lens[a] == 0:
-            assert bs == rs == -1
-        else:
-            t = lens[a] - 1
-            assert bs == bt[a][t // 16] * 16 + t % 16 and rs == rt[a][t // 16] * 16 + t % 16
+        assert blob[off_last + a] == (-(-lens[a] // 16) - 1 if lens[a] > 0 else -1)
+    # capacities: the items section has room for item_capacity items, zero past n_items
+    item_cap, slot_cap = blob[13], blob[14]
+    assert item_cap >= n_items and slot_cap >= n_slots
+    assert off_lens == off_items + item_cap * ITEM_INTS
+    assert all(v == 0 for v in blob[off_items + n_items * ITEM_INTS:off_lens])
     # the partial slots of each agent are exactly the range slot_ptr[a] .. slot_ptr[a+1]
     assert blob[off_ptr] == 0 and off_list == off_ptr + n_agents + 1
     for a in range(n_agents):
@@ -400,3 +397,84 @@ def test_plan_rejects_partial_hit_and_flags_frozen_tail():
     new = lp.refill_base(hs + [names["t"]], 1, 2)
     assert lp.tables(hs, 5)[0][0][1] == new[0]
     fk.Plan(lp, hs, 2, kernel=fk.KERNEL_GENERIC)
+
+
+# ---- step-stable plans: batched append, in-place rebuild ---------------------------------
+
+def _state(lp, hs, max_pages=64):
+    bt, rt, lens = lp.tables(hs, max_pages)
+    return bt, rt, lens, lp.free_list(0), lp.free_list(1), lp.refcounts(0), lp.refcounts(1)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_append_batch_equals_one_by_one(seed):
+    """forkkv_seq_append_batch reserves what forkkv_seq_append would, sequence by sequence,
+    with the same copy-on-write reports, and counts the base pages it took."""
+    from tests.cases import freeze_ops, random_ops, resolve_ops
+    rng = np.random.default_rng(3100 + seed)
+    if seed % 2:
+        ops, agents = freeze_ops(rng, 4, 16, 70, 40)
+        ops = resolve_ops(ops)
+    else:
+        ops, agents = random_ops(rng, 5, max_prefix=70, max_suffix=40)
+    pb, pr = rng.permutation(128), rng.permutation(128)
+    one, many = (fk.Pool(128, 128, 2, 16, 4, "f32", pb, pr) for _ in range(2))
+    n1, _ = one.replay(ops)
+    n2, _ = many.replay(ops)
+    h1, h2 = [n1[a] for a in agents], [n2[a] for a in agents]
+    for rows in (1, 1, 3, 16, 1, 17):
+        live = many.stats()["live_bpages"]
+        cows1, slots1 = [], []
+        for h in h1:
+            bs, rs, cow = one.append(h, rows)
+            slots1 += bs
+            cows1 += [cow] if cow else []
+        pages, cows2, slots2, _ = many.append_batch(h2, rows, want_slots=True)
+        assert cows2 == cows1 and slots2 == slots1
+        assert pages == many.stats()["live_bpages"] - live
+        assert _state(one, h1) == _state(many, h2)
+
+
+def test_append_batch_is_all_or_nothing():
+    lp = fk.Pool(8, 16, 1, 16, 4, "f32")
+    root = lp.create(False)
+    lp.append(root, 16)
+    a, _ = lp.fork(root, 16)
+    b, _ = lp.fork(root, 16)
+    before = _state(lp, [a, b])
+    with pytest.raises(fk.ForkKVError) as e:  # 2 x 4 fresh pages > 7 free
+        lp.append_batch([a, b], 64)
+    assert e.value.code == fk.ENOMEM and _state(lp, [a, b]) == before
+    with pytest.raises(fk.ForkKVError) as e:  # a sequence listed twice
+        lp.append_batch([a, a], 1)
+    assert e.value.code == fk.EINVAL and _state(lp, [a, b]) == before
+
+
+@pytest.mark.parametrize("kernel", [fk.KERNEL_GENERIC, fk.KERNEL_MFMA])
+def test_plan_rebuild_equals_fresh_plan(kernel):
+    """After decode steps that cross pages, a rebuilt plan has exactly the items, lengths,
+    slots and last pages of a plan built afresh, keeps its capacities (so a captured launch
+    stays valid) and passes the validity checks."""
+    cfg = config_by_name("llama3_8b_react_decode")
+    lp = fk.Pool(cfg.num_bpages, cfg.num_rpages, cfg.num_kv_heads, cfg.head_dim, cfg.rank,
+                 cfg.dtype)
+    ops, agents = pool_ops(cfg)
+    names, _ = lp.replay(ops)
+    hs = [names[a] for a in agents]
+    lp.append_batch(hs, 1)
+    plan = fk.Plan(lp, hs, cfg.num_q_heads, kernel=kernel)
+    cap0 = plan.info["item_capacity"], plan.info["slot_capacity"], plan.info["plan_bytes"]
+    for step in range(40):
+        pages, _, _, _ = lp.append_batch(hs, 1)
+        if not pages:
+            continue
+        same = plan.rebuild(hs)
+        fresh = fk.Plan(lp, hs, cfg.num_q_heads, kernel=kernel)
+        b1, b2 = plan.blob(), fresh.blob()
+        assert b1[2] == b2[2] and b1[3] == b2[3]  # items, slots
+        n = len(hs)
+        for off_word, size in ((6, b1[2] * ITEM_INTS), (7, n), (8, n + 1), (12, n)):
+            assert b1[b1[off_word]:b1[off_word] + size] == b2[b2[off_word]:b2[off_word] + size]
+        assert same and (plan.info["item_capacity"], plan.info["slot_capacity"],
+                         plan.info["plan_bytes"]) == cap0
+        _check_plan(lp, lp.tables(hs, -(-lp.length(hs[0]) // 16)), hs, plan, 8)

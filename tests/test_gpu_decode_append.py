@@ -125,19 +125,28 @@ def test_decode_append_tiny(seed, dtype, kernel, d, r, Hq, Hkv):
     assert_close(g, ref, f"append seed={seed} {dtype} kernel={kernel}", scale_abs=True)
 
 
-STEP_CASES = [(fk.KERNEL_MFMA, False), (fk.KERNEL_MFMA, True), (fk.KERNEL_GENERIC, True)]
+STEP_CASES = [(fk.KERNEL_MFMA, False, False), (fk.KERNEL_MFMA, True, False),
+              (fk.KERNEL_GENERIC, True, False), (fk.KERNEL_MFMA, False, True),
+              (fk.KERNEL_MFMA, True, True), (fk.KERNEL_GENERIC, False, True)]
 
 
-@pytest.mark.parametrize("kernel,freeze", STEP_CASES)
-def test_decode_append_steps(kernel, freeze):
-    """A serving loop: 20 decode-with-append steps in a row, so the new tokens cross page
-    boundaries and open fresh pages; with ``freeze`` the agents share the root's frozen
-    unaligned tail (the slot map is in use).  Every step's output, and the pools at the end,
-    are checked against the oracle replaying the same writes."""
+@pytest.mark.parametrize("kernel,freeze,graph", STEP_CASES)
+def test_decode_append_steps(kernel, freeze, graph):
+    """A serving loop: 40 decode-with-append steps in a row on one plan, so the new tokens
+    cross page boundaries (and, after unaligned packed forks, first fill the packed tail
+    pages); with ``freeze`` the agents share the root's frozen unaligned tail (the slot map
+    is in use).  The plan's device lengths advance inside each call; between steps the host
+    reserves the next tokens in one batched call and only at a page crossing updates the
+    tables in place and rebuilds and re-uploads the plan.  With ``graph`` one captured call
+    is replayed for every step (with new query and row values copied in), which must stay
+    valid across the rebuilds.  Every step's output, and the pools at the end, are checked
+    against the oracle replaying the same writes."""
     from oracle.attention import apply_rows_write
-    rng = np.random.default_rng(4321 + int(freeze))
+    rng = np.random.default_rng(4321 + int(freeze) + 2 * int(graph))
     dtype, d, r, Hq, Hkv = "bf16", 128, 16, 8, 2
-    n_agents, num_pages, L0, steps = 3, 64, 37, 20
+    if kernel == fk.KERNEL_GENERIC:
+        dtype, d, r = "f32", 32, 8
+    n_agents, num_pages, L0, steps = 3, 96, 37, 40
     ops = [("create", "root", 0), ("append", "root", L0)]
     points = [L0, 32, 21]
     for j in range(n_agents):
@@ -159,39 +168,75 @@ def test_decode_append_steps(kernel, freeze):
                    dtype=dtype)
     host_b, host_r = apply_cows_host(bpool, b.cows, Hkv, d), rpool.copy()
     lora_scale, theta, sm = 2.0, 5e5, 1.0 / np.sqrt(d)
+    # the first token: reserved, tables with room for the loop's pages, one plan
+    _, cows, _, _ = b.pool.append_batch(b.handles, 1)
+    if cows:
+        b.pool.cow_copy(cows)
+        host_b = apply_cows_host(host_b, cows, Hkv, d)
+    b.refresh_tables(extra_pages=steps // 16 + 2)
+    b.make_plan(kernel)
+    assert b.plan.info["kernel"] == kernel and (b.pstart is not None) == freeze
+    dev_rows = {k: to_device(np.zeros(shape, dtype=np.float32 if dtype == "f32" else np.uint16))
+                for k, shape in (("k_new", (n_agents, Hkv, d)), ("v_new", (n_agents, Hkv, d)),
+                                 ("rk_new", (n_agents, r)), ("rv_new", (n_agents, r)))}
+    g = None
+    rebuilds = 0
     for step in range(steps):
-        start = [b.pool.length(h) for h in b.handles]
-        for h in b.handles:
-            _, _, cow = b.pool.append(h, 1, want_slots=False)
-            if cow:
-                b.pool.cow_copy([cow])
-                host_b = apply_cows_host(host_b, [cow], Hkv, d)
-        b.refresh_tables()
-        b.make_plan(kernel)
-        assert b.plan.info["kernel"] == kernel
-        assert (b.pstart is not None) == freeze
+        if step > 0:
+            before = [b.pool.length(h) for h in b.handles]
+            n_bpages = b.pool.stats()["live_bpages"]
+            same, cows = b.next_step()
+            if cows:
+                host_b = apply_cows_host(host_b, cows, Hkv, d)
+            rebuilds += int(b.pool.stats()["live_bpages"] != n_bpages)
+            assert [b.pool.length(h) for h in b.handles] == [n + 1 for n in before]
+            # the tables next_step patched equal a fresh export, and so do the device tables
+            bt, rt, lens = b.pool.tables(b.handles, b.max_pages)
+            assert np.array_equal(np.array(bt).reshape(b.btab_host.shape), b.btab_host)
+            assert np.array_equal(np.array(rt).reshape(b.rtab_host.shape), b.rtab_host)
+            assert list(lens) == list(b.lens)
+            assert np.array_equal(b.btab.cpu().numpy(), b.btab_host)
+            if freeze:
+                st, _ = b.pool.starts(b.handles, b.max_pages)
+                assert np.array_equal(np.array(st).reshape(b.pstart_host.shape), b.pstart_host)
+                assert np.array_equal(b.pstart.cpu().numpy(), b.pstart_host)
+            assert same or not graph
         q = encode(rng.standard_normal((n_agents, Hq, d)), dtype)
         rows = dict(k_new=encode(rng.standard_normal((n_agents, Hkv, d)), dtype),
                     v_new=encode(rng.standard_normal((n_agents, Hkv, d)), dtype),
                     rk_new=encode(rng.standard_normal((n_agents, r)), dtype),
                     rv_new=encode(rng.standard_normal((n_agents, r)), dtype))
-        b.q = to_device(q)
-        b.out.fill_(0x7FC0)
-        out = b.decode_append({k: to_device(v) for k, v in rows.items()}, lora_scale, sm, theta)
+        b.q.copy_(to_device(q))
+        for k, v in rows.items():
+            dev_rows[k].copy_(to_device(v))
+        b.out.fill_(float("nan") if dtype == "f32" else 0x7FC0)
+        if graph and g is not None:
+            g.replay()
+        else:
+            b.decode_append(dev_rows, lora_scale, sm, theta)
+            if graph:  # capture the call once, after the eager first step
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    b.decode_append(dev_rows, lora_scale, sm, theta)
         torch.cuda.synchronize()
+        # the copy-on-write copies the library reported are mirrored on the oracle's pools
+        lens = [b.pool.length(h) for h in b.handles]
         starts = b.pstart_host if freeze else None
         host_b, host_r = apply_rows_write(geo, host_b, host_r, b.btab_host, b.rtab_host,
-                                          [[t] for t in start], rows["k_new"][:, None],
+                                          [[t - 1] for t in lens], rows["k_new"][:, None],
                                           rows["v_new"][:, None], rows["rk_new"][:, None],
                                           rows["rv_new"][:, None], starts=starts)
-        ref = decode_attention(geo, host_b, host_r, b.btab_host, b.rtab_host, np.array(b.lens),
+        ref = decode_attention(geo, host_b, host_r, b.btab_host, b.rtab_host, np.array(lens),
                                q, Bk, Bv, lora_scale, sm, theta, starts=starts)
-        assert_close(gpu_values(out, dtype), ref,
-                     f"append step {step} kernel={kernel} freeze={freeze}", scale_abs=True)
-    got_b = b.bcache.cpu().numpy().view(np.uint16)
-    got_r = b.rcache.cpu().numpy().view(np.uint16)
-    assert np.array_equal(got_b, host_b), "pool bytes (base) after the loop"
-    assert np.array_equal(got_r, host_r), "pool bytes (residual) after the loop"
+        assert_close(gpu_values(b.out, dtype), ref,
+                     f"append step {step} kernel={kernel} freeze={freeze} graph={graph}",
+                     scale_abs=True)
+    assert rebuilds >= 2  # the loop crossed pages
+    got_b = b.bcache.cpu().numpy().view(np.uint16 if dtype == "bf16" else np.float32)
+    got_r = b.rcache.cpu().numpy().view(np.uint16 if dtype == "bf16" else np.float32)
+    assert np.array_equal(got_b.view(np.uint8), host_b.view(np.uint8)), "pool bytes (base)"
+    assert np.array_equal(got_r.view(np.uint8), host_r.view(np.uint8)), "pool bytes (residual)"
 
 
 def test_decode_append_llama3_react_shape():
@@ -257,11 +302,13 @@ def test_decode_append_errors():
 @pytest.mark.parametrize("kernel,dtype,d,r", [(fk.KERNEL_GENERIC, "f32", 16, 4),
                                               (fk.KERNEL_MFMA, "bf16", 128, 16)])
 def test_decode_append_graph_replay_matches_eager(kernel, dtype, d, r):
-    """A decode-with-append call captured in a HIP graph (the rows stored, then attended)
-    gives the eager call's output and pool bytes on every replay (three replays, with eager
-    work on the output between them)."""
+    """Decode with append advances the plan's device lengths, so one captured call replayed
+    step after step is a serving loop.  Two identical batches run 20 steps: one calls eagerly
+    every step, the other replays a graph captured after its first eager step; between steps
+    both reserve the next tokens (rebuilding and re-uploading the plan at page crossings).
+    Outputs and pools agree bit for bit after every step."""
     rng = np.random.default_rng(990 + d)
-    n_agents, num_pages, Hq, Hkv = 5, 64, 8, 2
+    n_agents, num_pages, Hq, Hkv = 5, 96, 8, 2
     ops, agents = _fork_ops(rng, n_agents, int(rng.integers(20, 120)))
     perm_b = rng.permutation(num_pages).astype(np.int32)
     perm_r = rng.permutation(num_pages).astype(np.int32)
@@ -275,25 +322,37 @@ def test_decode_append_graph_replay_matches_eager(kernel, dtype, d, r):
              ("rk_new", (n_agents, r)), ("rv_new", (n_agents, r)))}
     geom = dict(num_bpages=num_pages, num_rpages=num_pages, num_kv_heads=Hkv, num_q_heads=Hq,
                 head_dim=d, rank=r, dtype=dtype)
-    b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
-    b.reserve_chunk(1)
-    b.make_plan(kernel)
-    assert b.plan.info["kernel"] == kernel
+    steps = 20
+    batches = []
+    for _ in range(2):
+        b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
+        b.reserve_chunk(1)
+        b.refresh_tables(extra_pages=3)
+        b.make_plan(kernel)
+        assert b.plan.info["kernel"] == kernel
+        batches.append(b)
+    eager_b, graph_b = batches
     args = (2.0, 1.0 / np.sqrt(d), 5e5)
-    b.decode_append(rows, *args)
-    torch.cuda.synchronize()
-    eager, pool_b, pool_r = b.out.clone(), b.bcache.clone(), b.rcache.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        b.decode_append(rows, *args)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        b.out.fill_(rep + 1)
+    graph = None
+    for step in range(steps):
+        if step > 0:
+            for b in batches:
+                same, _ = b.next_step()
+                assert same
+        eager_b.decode_append(rows, *args)
+        if graph is None:
+            graph_b.decode_append(rows, *args)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                graph_b.decode_append(rows, *args)
+        else:
+            graph_b.out.fill_(step + 1)
+            torch.cuda.synchronize()
+            graph.replay()
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        same = (torch.equal(b.out, eager) and torch.equal(b.bcache, pool_b)
-                and torch.equal(b.rcache, pool_r))
-        print(f"[parity] decode-append graph replay {rep} kernel={kernel}: bitwise equal={same}",
+        same = (torch.equal(eager_b.out, graph_b.out) and torch.equal(eager_b.bcache, graph_b.bcache)
+                and torch.equal(eager_b.rcache, graph_b.rcache))
+        print(f"[parity] decode-append graph step {step} kernel={kernel}: bitwise equal={same}",
               flush=True)
         assert same
