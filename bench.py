@@ -554,7 +554,8 @@ def serving_loop(cfg, x, ops, agents, steps):
     re-uploads the plan; then the step runs -- as an eager call, and in a second pass as a
     replay of one captured call (the plan's device lengths advance inside each call, so the
     same graph serves every step).  Reported per step: wall time with all host work, GPU
-    time, and the host's share."""
+    time, the host's share (Python included) and the part of it spent in the library's own
+    host calls (batched append, plan rebuild, upload)."""
     import numpy as np
     import torch
 
@@ -584,6 +585,7 @@ def serving_loop(cfg, x, ops, agents, steps):
                 call()
         torch.cuda.synchronize()
         host, rebuilds = 0.0, 0
+        b.lib_host_s = 0.0
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t_wall = time.perf_counter()
@@ -606,6 +608,7 @@ def serving_loop(cfg, x, ops, agents, steps):
                      "wall_us_per_step": wall / steps * 1e6,
                      "gpu_us_per_step": gpu_ms / steps * 1e3,
                      "host_us_per_step": host / steps * 1e6,
+                     "library_host_us_per_step": b.lib_host_s / steps * 1e6,
                      "agent_tokens_per_s": N * steps / wall}
         del b, g
         torch.cuda.empty_cache()

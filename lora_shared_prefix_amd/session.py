@@ -5,6 +5,8 @@ Marshalling only -- the attention itself and the fork bookkeeping run in libfork
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import torch
 
@@ -37,6 +39,7 @@ class DeviceBatch:
                  kernel=fk.KERNEL_AUTO, pages_per_item=0, max_agents_per_item=0, plan=True,
                  stream=None):
         self.g = dict(geom)
+        self.lib_host_s = 0.0  # time spent in the library's host calls of next_step
         self.dtype = self.g["dtype"]
         self.device = device
         self.bcache = to_device(arrays["bpool"], device)
@@ -93,9 +96,11 @@ class DeviceBatch:
         launch captured earlier stays valid (always, within the plan's capacities and the
         tables' room); ``cows`` the row copies that were run."""
         st = self._step_state()
+        t0 = time.perf_counter()
         rc = fk.lib().forkkv_seq_append_batch(self.pool.handle, st["seqs"], st["n"], 1,
                                               st["bslots"], st["rslots"], st["cows"],
                                               fk.C.byref(st["pages"]))
+        self.lib_host_s += time.perf_counter() - t0
         if rc != fk.OK:
             raise fk.ForkKVError(rc, "forkkv_seq_append_batch")
         cows = [(c.src_bpage, c.dst_bpage, c.n_rows) for c in st["cows"] if c.n_rows]
@@ -105,7 +110,10 @@ class DeviceBatch:
         if not st["pages"].value and not cows:
             return True, cows
         # patch the host tables where a token opened a page (row 0) or the last page was
-        # copied, then copy them to the device tables in place
+        # copied, then copy them to the device tables in place -- asynchronously, from pinned
+        # mirrors (the previous copy out of them has long finished; it is waited for)
+        if st["copied"] is not None:
+            st["copied"].synchronize()
         for a in range(st["n"]):
             page, row = divmod(st["bslots"][a], fk.PAGE)
             lp = st["last"][a]
@@ -117,13 +125,17 @@ class DeviceBatch:
             assert lp < self.max_pages, "the tables have no room for the new pages"
             self.btab_host[a, lp] = page
             self.rtab_host[a, lp] = st["rslots"][a] // fk.PAGE
-        self.btab.copy_(torch.from_numpy(self.btab_host))
-        self.rtab.copy_(torch.from_numpy(self.rtab_host))
+        self.btab.copy_(st["btab_pin"], non_blocking=True)
+        self.rtab.copy_(st["rtab_pin"], non_blocking=True)
         if self.pstart is not None:
-            self.pstart.copy_(torch.from_numpy(self.pstart_host))
+            self.pstart.copy_(st["pstart_pin"], non_blocking=True)
+        st["copied"] = torch.cuda.Event()
+        st["copied"].record()
+        t0 = time.perf_counter()
         same = self.plan.rebuild(self.handles)
         dev = self.plan.dev.data_ptr()
         self.plan.upload(stream)
+        self.lib_host_s += time.perf_counter() - t0
         same = same and self.plan.dev.data_ptr() == dev
         if self.plan.info["workspace_bytes"] > self.workspace.numel():
             self.workspace = self.plan.workspace()
@@ -162,7 +174,13 @@ class DeviceBatch:
             last = [int((self.btab_host[a] >= 0).sum()) - 1 for a in range(n)]
             st = dict(n=n, seqs=fk._i32_array(self.handles), bslots=(fk.C.c_int32 * n)(),
                       rslots=(fk.C.c_int32 * n)(), cows=(fk.CowOp * n)(),
-                      pages=fk.C.c_int32(), last=last)
+                      pages=fk.C.c_int32(), last=last, copied=None)
+            # pinned host mirrors of the tables (the host arrays become views of them)
+            for name in ("btab", "rtab", "pstart"):
+                host = getattr(self, name + "_host")
+                pin = torch.from_numpy(host.copy()).pin_memory()
+                st[name + "_pin"] = pin
+                setattr(self, name + "_host", pin.numpy())
             self._st = st
         return st
 
