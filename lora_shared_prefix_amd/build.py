@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libforkkv.so")
 MICROBENCH_LIB = os.path.join(PKG, "libforkkv_microbench.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-CPP_SOURCES = ["pool.cpp", "plan.cpp", "api.cpp"]
+CPP_SOURCES = ["pool.cpp", "plan.cpp", "api.cpp", "caps.cpp"]
 HIP_SOURCES = ["kernels_generic.hip", "kernels_mfma.hip", "scratch.hip"]
 ARCH = "gfx950"
 

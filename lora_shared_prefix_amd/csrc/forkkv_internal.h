@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <vector>
@@ -242,6 +243,43 @@ constexpr int kGenericThreads = 256;
 constexpr int kGenericAccPerThread = 32;   // rows * d <= 256 * 32
 constexpr int kGenericAccrPerThread = 8;   // rows * r <= 256 * 8
 constexpr int kGenericMaxRows = 64;
+// A gfx950 workgroup may use the CU's whole 160 KiB of LDS; launches above the default
+// 64 KiB of dynamic LDS raise the kernel's limit first.
+constexpr int kMaxLds = 160 * 1024;
+constexpr int kDefaultDynLds = 64 * 1024;
+
+// LDS plan of the generic kernel (byte offsets), shared by the kernel and the host code that
+// sizes its launches and items.
+struct GenLds {
+  int inv, cs, bk, bv, kq, rk, rv, s, alpha, m, l, accr, total;
+};
+__host__ __device__ inline GenLds gen_lds(int na, int rows, int d, int r) {
+  GenLds L{};
+  int o = 0;
+  auto take = [&](int bytes) { int at = o; o += (bytes + 15) & ~15; return at; };
+  L.inv = take(8 * (d / 2));
+  L.cs = take(4 * kPage * d);  // [P][d/2][2]
+  L.bk = take(4 * kPage * d);
+  L.bv = take(4 * kPage * d);
+  L.kq = take(4 * kPage * d);
+  L.rk = take(4 * na * kPage * r);
+  L.rv = take(4 * na * kPage * r);
+  L.s = take(4 * rows * kPage);
+  L.alpha = take(4 * rows);
+  L.m = take(4 * rows);
+  L.l = take(4 * rows);
+  L.accr = take(4 * rows * r);
+  L.total = o;
+  return L;
+}
+
+// The MFMA decode kernel: waves per workgroup, and agents per wave for a GQA group of
+// `group` query heads (the wave's 16 query columns hold whole groups, at most 4 agents).
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaHeadDim = 128, kMfmaRank = 16;  // the one shape the MFMA kernels take
+inline int mfma_agents_per_group(int group) {
+  return group >= 1 && group <= 16 ? (16 / group < 4 ? 16 / group : 4) : 0;
+}
 int generic_max_agents(int group, int head_dim, int rank);
 int generic_lds_bytes(int na, int rows, int d, int r);
 bool prefill_mfma_enabled();

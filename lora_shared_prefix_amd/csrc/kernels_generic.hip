@@ -43,34 +43,6 @@ template <> struct Elem<uint16_t> {  // bfloat16 bit patterns
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 // Dynamic LDS layout of the generic attention kernel.
-struct GenLds {
-  int inv, cs, bk, bv, kq, rk, rv, s, alpha, m, l, accr, total;  // byte offsets
-};
-
-__host__ __device__ inline GenLds gen_lds(int na, int rows, int d, int r) {
-  GenLds L{};
-  int o = 0;
-  auto take = [&](int bytes) { int at = o; o += (bytes + 15) & ~15; return at; };
-  L.inv = take(8 * (d / 2));
-  L.cs = take(4 * kPage * d);  // [P][d/2][2]
-  L.bk = take(4 * kPage * d);
-  L.bv = take(4 * kPage * d);
-  L.kq = take(4 * kPage * d);
-  L.rk = take(4 * na * kPage * r);
-  L.rv = take(4 * na * kPage * r);
-  L.s = take(4 * rows * kPage);
-  L.alpha = take(4 * rows);
-  L.m = take(4 * rows);
-  L.l = take(4 * rows);
-  L.accr = take(4 * rows * r);
-  L.total = o;
-  return L;
-}
-
-// A gfx950 workgroup may use the CU's whole 160 KiB of LDS; launches above the default
-// 64 KiB of dynamic LDS raise the kernel's limit first (see launch_generic).
-constexpr int kMaxLds = 160 * 1024;
-constexpr int kDefaultDynLds = 64 * 1024;
 
 // Rows of the workgroup: decode = (agent j of the item, q head within the group);
 // prefill = (query of the block, q head within the group), one agent.
@@ -667,21 +639,6 @@ int prefill_rows(int G, int d, int r) {
 }
 
 }  // namespace
-
-int generic_lds_bytes(int na, int rows, int d, int r) { return gen_lds(na, rows, d, r).total; }
-
-int generic_max_agents(int group, int head_dim, int rank) {
-  int best = 0;
-  for (int na = 1; na <= kItemAgents; ++na) {
-    const int rows = na * group;
-    if (rows > kGenericMaxRows) break;
-    if (rows * head_dim > kGenericThreads * kGenericAccPerThread) break;
-    if (rows * rank > kGenericThreads * kGenericAccrPerThread) break;
-    if (gen_lds(na, rows, head_dim, rank).total > kMaxLds) break;
-    best = na;
-  }
-  return best;
-}
 
 // Launch one instantiation of the generic kernel with lds bytes of dynamic LDS.
 template <typename T, bool kPrefill>

@@ -1062,26 +1062,14 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   }
 }
 
-int agents_per_group(int group) { return group >= 1 && group <= 16 ? min(4, 16 / group) : 0; }
-
 }  // namespace
 
-bool mfma_supported(int dtype, int head_dim, int rank, int group) {
-  return dtype == FORKKV_DTYPE_BF16 && head_dim == kD && rank == kR &&
-         agents_per_group(group) >= 1;
-}
-
-int mfma_agents_per_wave(int group) { return agents_per_group(group); }
-
-// Agents per plan item: up to four groups of agents_per_group(G) each, at most 8.
-int mfma_group_agents(int group) {
-  const int A = agents_per_group(group);
-  return A > 0 ? min(kItemAgents, kWaves * A) : 0;
-}
+static_assert(kWaves == kMfmaWaves, "the planner sizes items for this many waves");
+static_assert(kD == kMfmaHeadDim && kR == kMfmaRank, "the shape the planner routes here");
 
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
-  const int A = agents_per_group(p.group);
+  const int A = mfma_agents_per_group(p.group);
   const int n_items = p.n_items;
   const int blocks = 8 * p.num_kv_heads * ((n_items + 7) / 8);
 #define FORKKV_DECODE_LAUNCH(NA, MAP) \
@@ -1101,8 +1089,6 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
 #undef FORKKV_DECODE_LAUNCH
   return hipGetLastError();
 }
-
-bool prefill_mfma_enabled() { return true; }
 
 hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t*, hipStream_t s) {
   const int n_rblocks = (p.chunk_len * p.group + kPfRows - 1) / kPfRows;
