@@ -320,9 +320,9 @@ int forkkv_residual_attn_prefill(const forkkv_prefill_args* a, hipStream_t strea
   if (p.group > forkkv::kGenericMaxRows || forkkv::generic_max_agents(p.group, p.head_dim, p.rank) < 1)
     return FORKKV_EUNSUPPORTED;
 
-  // (the MFMA prefill kernel assumes pages at multiples of P: a slot map runs the generic one)
+  // (the MFMA prefill kernel has an instantiation for the slot map, like the decode kernel)
   const bool mfma_ok = forkkv::mfma_supported(g.dtype, g.head_dim, g.rank, p.group) &&
-                       forkkv::prefill_mfma_enabled() && !a->pstart;
+                       forkkv::prefill_mfma_enabled();
   if (a->kernel == FORKKV_KERNEL_MFMA && !mfma_ok) return FORKKV_EUNSUPPORTED;
   const bool mfma = mfma_ok && a->kernel != FORKKV_KERNEL_GENERIC;
   (void)hipGetLastError();

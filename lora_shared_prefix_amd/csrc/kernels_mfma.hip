@@ -744,6 +744,10 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // rows per workgroup
 
+// kMap: the agents hold frozen tails, so pages start where the page start table says (the
+// slot map) and a page may hold fewer than 16 rows; without it page lp starts at lp * P and
+// none of that bookkeeping is compiled in.
+template <bool kMap>
 __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __shared__ __align__(16) uint4 s_k[2][2][4 * 64];   // [buf][page][chunk * 64 + lane]
@@ -752,6 +756,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __shared__ __align__(16) uint4 s_v[2][8 * 64];
   __shared__ __align__(16) uint4 s_rv[2][64];         // [buf][lane], same page halves
   __shared__ int s_miss[2][2];                          // [buf][page]: base page missing
+  __shared__ int s_pos[2][2], s_vrows[2][2];            // [buf][page]: start, valid rows
   const int Hkv = p.num_kv_heads, G = p.group, Hq = p.num_q_heads, C = p.chunk_len;
   // the workgroups of one KV head share an XCD (block ids are dealt round robin over the
   // 8 XCDs), so the shared prefix of that head streams through one L2
@@ -771,7 +776,8 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   const int first_pos = row_position(p, a, row0 / G);
   const int last_pos = row_position(p, a, last_row / G);
   const int end_pos = row_position(p, a, C - 1) + 1;  // rows at or past end_pos: unwritten
-  const int lp_end = last_pos / kPage + 1;  // pages any row of the block sees
+  // pages any row of the block sees
+  const int lp_end = page_of(kMap ? p.pstart : nullptr, p.max_pages, a, last_pos) + 1;
   const int n_it = (lp_end + 1) / 2;
   const int n = Hkv * kD;
   const uint16_t* bcache = static_cast<const uint16_t*>(p.bcache);
@@ -820,10 +826,12 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     sts[i] = static_cast<float>(sv);
   }
   float rc[4], rs[4];
-  auto anchor = [&](int it) {
+  int next_base = pg * kPage;  // the page start the recurrence stands at
+  // exact cos/sin (fp64-reduced angle) of this lane's key position base + col
+  auto anchor_at = [&](int base) {
     for (int i = 0; i < 4; ++i) {
       const double om = exp2(-2.0 * perm_dim(tp, 4 * g4 + i) / kD * log2_theta);
-      double ang = static_cast<double>((2 * it + pg) * kPage + col) * om;
+      double ang = static_cast<double>(base + col) * om;
       ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
       double sv, cv;
       sincos(ang, &sv, &cv);
@@ -839,24 +847,35 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     uint4 v;      // quarter tp of page pg's value tile (operand pieces of lanes 2l, 2l+1)
     uint2 rv;     // value-residual operand of page pg (staged by the tp == 0 waves)
     bool miss;    // page pg's base page is missing (evicted): its keys take no part
+    int pos, nx;  // with the slot map: the page's start and the next page's (-1: none)
   };
   // Page ids: lane i holds the ids of this wave's page at iteration 64 k + i (block k),
   // checked against the pools once here (a missing or out-of-pool page is -1); a page's ids
   // then come from a readlane.  A missing base page is read from page 0 (any in-pool page)
   // and then masked; a missing residual page reads the zero page.
   int ids_b = -1, ids_r = -1;
+  int ids_st = 0, ids_nx = 0;  // with the slot map: start of the page and of the next one
   auto fetch_ids = [&](int blk) {
     const int lp = min(2 * (64 * blk + lane) + pg, lp_end - 1);
     const int bp = p.btab[size_t(a) * p.max_pages + lp];
     const int rp = p.rtab[size_t(a) * p.max_pages + lp];
     ids_b = (bp >= 0 && bp < p.num_bpages) ? bp : -1;
     ids_r = (rp >= 0 && rp < p.num_rpages) ? rp : -1;
+    if constexpr (kMap) {
+      const int32_t* row = p.pstart + size_t(a) * p.max_pages;
+      ids_st = row[lp];
+      ids_nx = lp + 1 < p.max_pages ? row[lp + 1] : -1;
+    }
   };
   auto load = [&](int it, PfBuf& B) {
     if ((it & 63) == 0) fetch_ids(it >> 6);  // wave-uniform
     const int ib = __builtin_amdgcn_readlane(ids_b, it & 63);
     const int ir = __builtin_amdgcn_readlane(ids_r, it & 63);
     B.miss = ib < 0;
+    if constexpr (kMap) {
+      B.pos = __builtin_amdgcn_readlane(ids_st, it & 63);
+      B.nx = __builtin_amdgcn_readlane(ids_nx, it & 63);
+    }
     const size_t pb = max(ib, 0);
     const uint16_t* kt = bcache + (pb * 2 * Hkv + h) * tile;
     const uint16_t* vt = bcache + (pb * 2 * Hkv + Hkv + h) * tile;
@@ -891,7 +910,12 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   auto stage = [&](int it, const PfBuf& B) {
     const int buf = it & 1;
     const int lp = 2 * it + pg;
-    if ((it & 31) == 0 && it) anchor(it);
+    // the page's first position; the recurrence below stands at next_base, and is re-anchored
+    // (fp64) every 32 iterations and wherever a page does not start where it stands (a frozen
+    // tail in between)
+    const int base = kMap ? B.pos : lp * kPage;
+    if (((it & 31) == 0 && it) || (kMap && base != next_base)) anchor_at(base);
+    next_base = base + 2 * kPage;
     // rebuild this wave's two key tiles of page pg: K = bK + RoPE(s * rK B_k)
     U2 rk;
     rk.u = B.rk;
@@ -921,7 +945,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // arbitrary bytes (even NaN); a zero probability times NaN is NaN, so they are zeroed.
     // The 16 bytes this lane stages are the operand pieces of reader lanes 2l and 2l+1
     // (tokens 4 g .. 4 g + 3, g = ((2l) mod 64) / 16); its value-residual piece is its own.
-    const int last = (lp < lp_end && !B.miss) ? end_pos - lp * kPage : 0;
+    // rows of the page that hold keys: up to the next page's start (a frozen tail holds fewer
+    // than 16) and up to the last stored position
+    int last = (lp < lp_end && !B.miss) ? end_pos - base : 0;
+    if (kMap && B.nx >= 0) last = min(last, B.nx - base);
     uint4 v = B.v;
     uint2 rv = B.rv;
     if (last < kPage) {  // wave-uniform: the pages at the end of the sequence, missing pages
@@ -940,7 +967,11 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     }
     if (tp == 0) {
       reinterpret_cast<uint2*>(&s_rv[buf][0])[2 * lane + pg] = rv;
-      if (lane == 0) s_miss[buf][pg] = B.miss;
+      if (lane == 0) {
+        s_miss[buf][pg] = B.miss;
+        s_pos[buf][pg] = base;
+        s_vrows[buf][pg] = min(max(last, 0), kPage);
+      }
     }
   };
 
@@ -966,8 +997,17 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     // no mask at all.  Rows past the chunk have zero q and are never written, so they need
     // none either.  (Wave-uniform.)
     const bool miss[2] = {s_miss[buf][0] != 0, s_miss[buf][1] != 0};  // wave-uniform
-    const bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < first_pos &&
-                          !miss[0] && !miss[1];
+    bool unmasked = 2 * it + 1 < lp_end && (2 * it + 1) * kPage + kPage - 1 < first_pos &&
+                    !miss[0] && !miss[1];
+    int pbase[2] = {2 * it * kPage, (2 * it + 1) * kPage}, pvr[2] = {kPage, kPage};
+    if constexpr (kMap) {  // starts and valid rows of the pair, as staged
+      for (int pgi = 0; pgi < 2; ++pgi) {
+        pbase[pgi] = s_pos[buf][pgi];
+        pvr[pgi] = s_vrows[buf][pgi];
+      }
+      unmasked = 2 * it + 1 < lp_end && pvr[0] == kPage && pvr[1] == kPage &&
+                 pbase[1] + kPage - 1 < first_pos && !miss[0] && !miss[1];
+    }
     for (int rt = 0; rt < 2; ++rt) {
       // raw scores (q.k); the softmax scale (> 0, log2 units) is applied inside the exp
       float sc[8], pmax = -INFINITY;
@@ -977,7 +1017,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       } else {
         for (int pgi = 0; pgi < 2; ++pgi) {
           const int lp = 2 * it + pgi;
-          const int lim = (lp < lp_end && !miss[pgi]) ? qpos[rt] - lp * kPage - 4 * g4 : -1;
+          // keys i <= lim of this lane's four: causal (key position <= query position), and
+          // with the slot map only the page's valid rows
+          int lim = (lp < lp_end && !miss[pgi]) ? qpos[rt] - pbase[pgi] - 4 * g4 : -1;
+          if constexpr (kMap) lim = min(lim, pvr[pgi] - 1 - 4 * g4);
           for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[rt][pgi][i] : -INFINITY;
         }
       }
@@ -1016,7 +1059,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // the other buffer, and iteration it + 2 waits behind the next barrier.
   PfBuf pb_;
   load(0, pb_);
-  anchor(0);
+  anchor_at(pg * kPage);  // (re-anchored at the first page's start where the slot map says)
   for (int it = 0; it < n_it; ++it) {
     stage(it, pb_);
     load(min(it + 1, n_it - 1), pb_);
@@ -1093,7 +1136,12 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_prefill_mfma(const PrefillParams& p, const int32_t*, hipStream_t s) {
   const int n_rblocks = (p.chunk_len * p.group + kPfRows - 1) / kPfRows;
   const int blocks = p.num_kv_heads * n_rblocks * p.n_agents;
-  hipLaunchKernelGGL(prefill_mfma_kernel, dim3(blocks), dim3(kPfThreads), 0, s, p, n_rblocks);
+  if (p.pstart)
+    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(blocks), dim3(kPfThreads), 0, s, p,
+                       n_rblocks);
+  else
+    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(blocks), dim3(kPfThreads), 0, s, p,
+                       n_rblocks);
   return hipGetLastError();
 }
 

@@ -201,3 +201,59 @@ def test_freeze_decode_needs_the_slot_map():
         fk.residual_attn_decode(b.pool, b.plan, b.q, b.Bk, b.Bv, b.btab, b.rtab, b.out,
                                 b.workspace, 1.0, 0.25, 1e4)
     assert e.value.code == fk.EINVAL
+
+
+@pytest.mark.parametrize("L0,nested", [(16 * 40 + 7, False), (7, False), (16 * 70 + 11, True)])
+def test_freeze_prefill_both_kernels(L0, nested):
+    """Chunk prefill over frozen tails on both kernels (the MFMA kernel's slot-map
+    instantiation and the generic kernel), each against the oracle on every row, with a
+    material adapter: a trunk frozen at an unaligned end (at 7 rows: the first page itself is
+    the frozen tail), agents whose chunks start fresh pages there, and with ``nested`` a
+    grandchild frozen again at its parent's unaligned end (two frozen tails in its history).
+    The stored rows are compared bit for bit."""
+    rng = np.random.default_rng(L0)
+    Hq, Hkv, d, r, C = 8, 2, 128, 16, 70
+    agents = ["a0", "a1"]
+    ops = [("create", "t", 0), ("append", "t", L0)]
+    ops += [("fork", "t", L0, a, fk.FORK_FREEZE, 0) for a in agents]
+    if nested:
+        ops += [("append", "a0", 21), ("fork", "a0", L0 + 21, "g", fk.FORK_FREEZE, 0)]
+        agents = ["a1", "g"]
+    npg = (L0 + 16 * 8 + 2 * C) // 16 + 24
+    perm_b = rng.permutation(npg).astype(np.int32)
+    perm_r = rng.permutation(3 * npg).astype(np.int32)
+    N = len(agents)
+    arrays = dict(bpool=encode(rng.standard_normal((npg, 2, Hkv, 16 * d)), "bf16"),
+                  rpool=encode(rng.standard_normal((3 * npg, 2, 16 * r)), "bf16"),
+                  Bk=encode(0.3 * rng.standard_normal((N, r, Hkv * d)), "bf16"),
+                  Bv=encode(0.3 * rng.standard_normal((N, r, Hkv * d)), "bf16"),
+                  q=encode(rng.standard_normal((N, Hq, d)), "bf16"))
+    chunk = {k: encode(rng.standard_normal(s), "bf16") for k, s in
+             (("q", (N, C, Hq, d)), ("k_new", (N, C, Hkv, d)), ("v_new", (N, C, Hkv, d)),
+              ("rk_new", (N, C, r)), ("rv_new", (N, C, r)))}
+    geom = dict(num_bpages=npg, num_rpages=3 * npg, num_kv_heads=Hkv, num_q_heads=Hq,
+                head_dim=d, rank=r, dtype="bf16")
+    geo = Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, rank=r,
+                   dtype="bf16")
+    outs = {}
+    for kernel in (fk.KERNEL_MFMA, fk.KERNEL_GENERIC):
+        print(f"[gpu-freeze] prefill L0={L0} nested={nested} kernel={kernel}", flush=True)
+        b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, plan=False)
+        start = b.reserve_chunk(C)
+        assert b.pstart is not None
+        pos = np.array([[s0 + i for i in range(C)] for s0 in start])
+        dev = {k: to_device(v) for k, v in chunk.items()}
+        out = b.prefill(dev, 2.0, 1.0 / np.sqrt(d), 1e6, kernel=kernel)
+        torch.cuda.synchronize()
+        exp_b, exp_r = apply_rows_write(geo, arrays["bpool"], arrays["rpool"], b.btab_host,
+                                        b.rtab_host, pos, chunk["k_new"], chunk["v_new"],
+                                        chunk["rk_new"], chunk["rv_new"], starts=b.pstart_host)
+        assert np.array_equal(b.bcache.cpu().numpy().view(np.uint16), exp_b)
+        assert np.array_equal(b.rcache.cpu().numpy().view(np.uint16), exp_r)
+        ref = prefill_attention_at(geo, arrays["bpool"], arrays["rpool"], b.btab_host,
+                                   b.rtab_host, pos, chunk["q"], chunk["k_new"], chunk["v_new"],
+                                   chunk["rk_new"], chunk["rv_new"], arrays["Bk"], arrays["Bv"],
+                                   2.0, 1.0 / np.sqrt(d), 1e6, starts=b.pstart_host)
+        outs[kernel] = gpu_values(out, "bf16")
+        assert_close(outs[kernel], ref, f"freeze prefill L0={L0} nested={nested} k={kernel}",
+                     scale_abs=True)
