@@ -187,6 +187,39 @@ def bench_prefill(steps, warmup):
         "rows_per_agent": f"{half} refilled at {h0}..{h0 + half - 1} + {half} appended",
         "ms_per_call": ms_r, "dense_flops_per_call": fl_r,
         "tflops": fl_r / (ms_r * 1e-3) / 1e12}
+    del b
+
+    # Frozen tail, same shape: the prefix ends 7 rows into a page that every agent shares
+    # read-only (fork mode freeze), so each agent's chunk starts on a fresh page and the
+    # page start table (the slot map) is in use; both prefill kernels are timed.
+    L0 = cfg.prefix_len + 7
+    fops = [("create", "root", 0), ("append", "root", L0)]
+    for a in agents:
+        fops += [("fork", "root", L0, a, fk.FORK_FREEZE, 0)]
+    fb = DeviceBatch(workload_geom(cfg), x, fops, agents, x["perm_b"], x["perm_r"],
+                     plan=False)
+    assert fb.pstart is not None
+    fb.reserve_chunk(cfg.chunk_len)
+    fl_f = cfg.n_agents * cfg.num_q_heads * per_key * sum(
+        L0 + i + 1 for i in range(cfg.chunk_len))
+    frozen = {"prefix": f"{L0} tokens, the last 7 in a shared read-only page",
+              "dense_flops_per_call": fl_f}
+    for name, kern in (("mfma", fk.KERNEL_MFMA), ("generic", fk.KERNEL_GENERIC)):
+        run = lambda: fb.prefill(chunk, cfg.lora_scale, sm, cfg.rope_theta, out=out,
+                                 kernel=kern)
+        run()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(n):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_f = t0.elapsed_time(t1) / n
+        log(f"frozen-tail prefill ({name}) {ms_f:.3f} ms per call, "
+            f"{fl_f / (ms_f * 1e-3) / 1e12:.1f} TFLOP/s")
+        frozen[name] = {"ms_per_call": ms_f, "tflops": fl_f / (ms_f * 1e-3) / 1e12}
+    res["frozen_tail"] = frozen
+    del fb
     return res
 
 
