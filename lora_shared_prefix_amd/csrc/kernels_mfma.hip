@@ -166,15 +166,31 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int xcd = b & 7, s = b >> 3;
   const int h = s % Hkv;
   const int item = xcd + 8 * (s / Hkv);
-  // the grid covers the plan's item capacity; items past the live count are empty
-  if (item >= n_items || item >= p.plan[kHdrItems]) return;
+  // The grid covers the plan's item capacity and the items section has room for that many
+  // records, zero past the live count (the whole section is uploaded): a record with no
+  // agents is an empty item, so the live count itself is never read.  The agent and slot
+  // entries are read with constant indices (a few wide scalar loads instead of a chain of
+  // dependent ones) and picked later by wave-uniform selects.
+  if (item >= n_items) return;
+  const int32_t* it = p.plan + p.off_items + item * kItemInts;
+  int ia[kItemAgents], is[kItemAgents];
+#pragma unroll
+  for (int k = 0; k < kItemAgents; ++k) {
+    ia[k] = it[4 + k];
+    is[k] = it[4 + kItemAgents + k];
+  }
+  const int lp0 = it[0], np = it[1], na = it[2];
+  // (the empty statements take the record's values as operands, so that all of its loads are
+  // issued before the test below -- one memory round trip -- rather than sunk past it)
+  asm volatile("" : : "s"(lp0), "s"(np), "s"(na));
+#pragma unroll
+  for (int k = 0; k < kItemAgents; ++k) asm volatile("" : : "s"(ia[k]), "s"(is[k]));
+  if (na <= 0) return;  // past the live count
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int col = lane & 15, g4 = lane >> 4;
   const int G = p.group, Hq = p.num_q_heads;
-  const int32_t* it = p.plan + p.off_items + item * kItemInts;
-  const int lp0 = it[0], np = it[1], na = it[2];
   const int n_groups = (na + A - 1) / A;
   const int n_sub = kWaves / n_groups;  // >= 1 (the plan keeps na <= 4A)
   const int gi = w % n_groups, si = w / n_groups;
@@ -206,14 +222,6 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
 
   // ---- this wave's agents and query columns ------------------------------------------------
-  // the item's agent and slot entries, read with constant indices (a few wide scalar loads
-  // instead of a chain of dependent ones), then picked by wave-uniform selects
-  int ia[kItemAgents], is[kItemAgents];
-#pragma unroll
-  for (int k = 0; k < kItemAgents; ++k) {
-    ia[k] = it[4 + k];
-    is[k] = it[4 + kItemAgents + k];
-  }
   int agent[A], slot[A], rlen[A];  // wave-uniform
 #pragma unroll
   for (int j = 0; j < A; ++j) {
@@ -332,22 +340,30 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   };
   // The page routines take the group's agent count NA as a compile-time constant, so the
   // per-agent work is straight-line code.
-  auto load_k = [&](int lp, KBuf& B, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
+  // key tiles and residual key rows of page lp, in two halves: the page loop refills one
+  // buffer in place, each half as soon as the previous page's copy has been consumed
+  auto load_kt = [&](int lp, KBuf& B) {
     B.bp = __builtin_amdgcn_readlane(vb, lp - id_base);
     const uint16_t* kt_base = bcache + (size_t(max(B.bp, 0)) * 2 * Hkv + h) * tile;
     // tiles are stored in operand order: lane l's piece is the l-th 16 B (K) / 8 B (V)
     for (int c = 0; c < 4; ++c)
       B.kt[c].u = *reinterpret_cast<const uint4*>(kt_base + 512 * c + 8 * lane);
+  };
+  auto load_rk = [&](int lp, KBuf& B, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       B.rb[j] = res_page(lp, j);
       B.rk[j].u = *reinterpret_cast<const uint2*>(B.rb[j] + 4 * lane);
     }
   };
+  auto load_k = [&](int lp, KBuf& B, auto na_c) {
+    load_kt(lp, B);
+    load_rk(lp, B, na_c);
+  };
   auto load_v = [&](const KBuf& B, VBuf& V, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    const uint16_t* vt_base = bcache + (size_t(B.bp) * 2 * Hkv + Hkv + h) * tile;
+    const uint16_t* vt_base = bcache + (size_t(max(B.bp, 0)) * 2 * Hkv + Hkv + h) * tile;
     for (int t = 0; t < 8; ++t)
       V.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
 #pragma unroll
@@ -355,28 +371,23 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       V.rv[j].u = *reinterpret_cast<const uint2*>(B.rb[j] + kPage * kR + 4 * lane);
   };
 
-  auto compute_page = [&](int lp, KBuf& B, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
-    if (B.bp < 0) return;  // wave-uniform
-    VBuf V;
-    load_v(B, V, na_c);
-    // rows of this page held by each agent (the page's start is common to them all)
-    int vrows = 0, minrows = kPage;
-    int prow[NA];
-    int pos0 = 0, pend = 0;
+  // A page's work is split into trig_for (RoPE angles), scores (key tiles and rotated
+  // residual keys against the queries) and softmax_acc (online softmax, P V).  The angles of
+  // page lp + 1 are formed right after the scores of page lp, where their LDS round trip
+  // overlaps the softmax's cross-lane maximum instead of opening the next page.
+
+  // s * cos / s * sin of (t0 + c) * w_j for the page scores() forms next, for
+  // j = 32*half + 8*g4 + e (c = this lane's key row), as fp16 pairs (e, e + 1)
+  h2 ct[2][4], st[2][4];
+  // Angles of page lp (every page of the sub-range passes through here once, in order,
+  // skipped pages included): lane j holds cos/sin(t0 * w_j) of the recurrence, which then
+  // advances by one page; with the slot map a page whose start differs from the
+  // recurrence's position re-anchors it first.  Past the sub-range's end (lp >= lpb) the
+  // values are computed and never used.
+  auto trig_for = [&](int lp) {
     if constexpr (kMap) {
-      pos0 = __builtin_amdgcn_readlane(vst, lp - id_base);
-      pend = __builtin_amdgcn_readlane(vend, lp - id_base);
-    }
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      prow[j] = kMap ? min(min(rlen[j], pend) - pos0, kPage)
-                     : page_rows(nullptr, p.max_pages, agent[j], lp, rlen[j]);
-      vrows = max(vrows, prow[j]);
-      minrows = min(minrows, prow[j]);
-    }
-    if constexpr (kMap) {
-      if (pos0 != next_pos) {  // wave-uniform: re-anchor the rotation at this page's start
+      const int pos0 = __builtin_amdgcn_readlane(vst, min(lp, lpb - 1) - id_base);
+      if (pos0 != next_pos) {  // wave-uniform
         float sv, cv;
         sincosf(static_cast<float>(pos0 - next_pos) * omega_f, &sv, &cv);
         const float c = mul_sub(pc, cv, ps, sv);
@@ -385,15 +396,6 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       }
       next_pos = pos0 + kPage;
     }
-    // Rows no column may read are zeroed: their bytes are arbitrary (even NaN).
-    const bool row_ok = col < vrows;  // this lane's key row (tok = col) in the A operands
-    const int tv = vrows - 4 * g4;    // valid tokens among this lane's 4 (B / V operands)
-    if (vrows < kPage && !row_ok) {   // (vrows < 16 only on a sequence's last page)
-      for (int c = 0; c < 4; ++c) B.kt[c].u = make_uint4(0, 0, 0, 0);
-      for (int j = 0; j < NA; ++j) B.rk[j].u = make_uint2(0, 0);
-    }
-
-    // -- RoPE angles of this page: lane j holds cos/sin(t0 * w_j) (see the recurrence) --
     ptrig[lane] = static_cast<_Float16>(pc);
     ptrig[64 + lane] = static_cast<_Float16>(ps);
     {  // advance to the next page: rotate by 16 * w_j
@@ -401,12 +403,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       ps = mul_add(ps, step_c, pc, step_s);
       pc = c;
     }
+    // (LDS operations of one wave execute in order: the reads below see the writes above)
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes above have landed
-
-    // s * cos / s * sin of (t0 + c) * w_j for j = 32*half + 8*g4 + e (c = this lane's key
-    // row), as fp16 pairs (e, e + 1)
-    h2 ct[2][4], st[2][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int jb = 32 * half + 8 * g4;
@@ -420,35 +418,44 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         st[half][e] = mul_add2(s0.p[e], cc.p[e], c0.p[e], ss.p[e]);
       }
     }
+  };
 
-    // -- scores: shared base tile, plus for each agent its rotated residual key --
+  // Scores of the page whose key-side operands B holds (angles from trig_for of that page):
+  // the shared base tile, plus for each agent its rotated residual key; this lane's column's
+  // agent is selected.  The page's value-side operands are loaded into V first, and B is
+  // refilled with page lp_next's key-side operands as its own are consumed.  Rows past a page's valid rows give arbitrary scores
+  // (their bytes may even be NaN); softmax_acc masks them out before any arithmetic.
+  auto scores = [&](KBuf& B, VBuf& V, int lp_next, auto na_c) -> f4 {
+    constexpr int NA = decltype(na_c)::value;
+    load_v(B, V, na_c);
     f4 sb = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < 4; ++c) {
       U4 qb;
       qb.u = qb_lds[c * 64 + lane];
       sb = mfma32(B.kt[c].b, qb.b, sb);
     }
-    // Work units u = (half, agent): half h covers score chunks h and h + 2, i.e. the
-    // reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.  The units are
+    load_kt(lp_next, B);  // the key tiles have been read: refill them with page lp_next's
+    // Work units u = (agent, half), agent-major: half h covers score chunks h and h + 2, i.e.
+    // the reconstruction tiles T = 2h, 2h+1 and their RoPE partners T + 4.  The units are
     // software-pipelined: the reconstruction MFMAs of unit u + 1 are issued before the
     // rotation arithmetic of unit u, so the matrix core and the vector ALU work together.
+    // An agent's residual score is complete after its second unit and is then selected
+    // for the columns it owns.
     constexpr int NU = 2 * NA;
-    f4 sj[NA];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) sj[j] = f4{0.f, 0.f, 0.f, 0.f};
+    f4 ssel = f4{0.f, 0.f, 0.f, 0.f}, sj = f4{0.f, 0.f, 0.f, 0.f};
     // B_k operands of a unit (four 8-byte LDS reads), fetched one unit before their use
     auto bk_ops = [&](int u, U2 (&a)[4]) {
-      const int half = u / NA, j = u % NA;
+      const int j = u / 2, half = u % 2;
       const uint2* bkj = bkl + (j0 + j) * 8 * 64 + lane;
       const int Ts[4] = {2 * half, 2 * half + 1, 2 * half + 4, 2 * half + 5};
       for (int k = 0; k < 4; ++k) a[k].u = bkj[Ts[k] * 64];
     };
     auto recon = [&](int u, const U2 (&a)[4], f4 (&d)[4]) {
-      const int j = u % NA;
+      const int j = u / 2;
       for (int k = 0; k < 4; ++k) d[k] = mfma16(a[k].s, B.rk[j].s, f4{0.f, 0.f, 0.f, 0.f});
     };
     auto rotate_score = [&](int u, const f4 (&d)[4]) {
-      const int half = u / NA, j = u % NA;
+      const int j = u / 2, half = u % 2;
       // rotate the partner pairs (tile k, tile k + 2) on packed fp16 values
       H8 k0, k2;
       for (int k = 0; k < 2; ++k) {
@@ -460,8 +467,10 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
           k2.p[2 * k + q2] = mul_add2(y, c, x, sn);
         }
       }
-      sj[j] = mfma32h(k0.v, qhr[half].v, sj[j]);
-      sj[j] = mfma32h(k2.v, qhr[half + 2].v, sj[j]);
+      if (half == 0) sj = f4{0.f, 0.f, 0.f, 0.f};
+      sj = mfma32h(k0.v, qhr[half].v, sj);
+      sj = mfma32h(k2.v, qhr[half + 2].v, sj);
+      if (half == 1) ssel = (j == 0 || jc == j) ? sj : ssel;
     };
     f4 dA[4], dB[4];
     U2 oA[4], oB[4];
@@ -480,16 +489,47 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         rotate_score(u, dB);
       }
     }
-    f4 ssel = sj[0];
+    load_rk(lp_next, B, na_c);  // likewise the residual key rows, after the last reconstruction
+    return ssel + sb;
+  };
+
+  // Rows of page lp held by the group's agents (the page's start is common to them all):
+  // the most and the fewest, and those of this lane's column's agent.
+  struct Rows {
+    int vrows, minrows, rows_col;
+  };
+  auto page_rows_of = [&](int lp, auto na_c) -> Rows {
+    constexpr int NA = decltype(na_c)::value;
+    int pos0 = 0, pend = 0;
+    if constexpr (kMap) {
+      pos0 = __builtin_amdgcn_readlane(vst, lp - id_base);
+      pend = __builtin_amdgcn_readlane(vend, lp - id_base);
+    }
+    Rows R{0, kPage, 0};
+    int prow[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      prow[j] = kMap ? min(min(rlen[j], pend) - pos0, kPage)
+                     : page_rows(nullptr, p.max_pages, agent[j], lp, rlen[j]);
+      R.vrows = max(R.vrows, prow[j]);
+      R.minrows = min(R.minrows, prow[j]);
+    }
+    R.rows_col = prow[0];
 #pragma unroll
     for (int j = 1; j < NA; ++j)
-      if (jc == j) ssel = sj[j];
-    ssel += sb;
+      if (jc == j) R.rows_col = prow[j];
+    return R;
+  };
 
-    // -- online softmax over this page's 16 keys, per column (log2 domain) --
+  // Online softmax over a page's 16 keys, per column (log2 domain), then acc += P bV and
+  // acc_r += P_a rV_a.  kFull: every agent of the group holds all 16 rows of the page, so
+  // nothing is masked (R is not read).
+  auto softmax_acc = [&](f4 ssel, VBuf& V, auto na_c, auto full_c, const Rows& R) {
+    constexpr int NA = decltype(na_c)::value;
+    constexpr bool kFull = decltype(full_c)::value;
     float sc[4];
     float pmax = -INFINITY;
-    if (minrows >= kPage) {
+    if (kFull || R.minrows >= kPage) {
       // every agent of the group has all 16 keys of the page; columns without an agent
       // (zero q) only ever touch their own, unwritten, state
       for (int i = 0; i < 4; ++i) {
@@ -497,12 +537,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
         pmax = fmaxf(pmax, sc[i]);
       }
     } else {
-      int rows_col = prow[0];  // rows of the page held by this lane's column's agent
-#pragma unroll
-      for (int j = 1; j < NA; ++j)
-        if (jc == j) rows_col = prow[j];
       for (int i = 0; i < 4; ++i) {
-        sc[i] = (col_ok && 4 * g4 + i < rows_col) ? ssel[i] * qscale : -INFINITY;
+        sc[i] = (col_ok && 4 * g4 + i < R.rows_col) ? ssel[i] * qscale : -INFINITY;
         pmax = fmaxf(pmax, sc[i]);
       }
     }
@@ -528,16 +564,21 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
     U2 pb;
     pb.u = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
-    if (tv < 4) {  // (only on a sequence's last page)
-      auto mask4 = [&](uint2 v) {
-        if (tv <= 0) v.x = 0;
-        else if (tv == 1) v.x &= 0xffffu;
-        if (tv <= 2) v.y = 0;
-        else if (tv == 3) v.y &= 0xffffu;
-        return v;
-      };
-      for (int t = 0; t < 8; ++t) V.vt[t].u = mask4(V.vt[t].u);
-      for (int j = 0; j < NA; ++j) V.rv[j].u = mask4(V.rv[j].u);
+    if constexpr (!kFull) {
+      // value rows past the page's valid rows are zeroed: P is 0 there, but their bytes
+      // are arbitrary (even NaN)
+      const int tv = R.vrows - 4 * g4;  // valid tokens among this lane's 4 (V operands)
+      if (tv < 4) {
+        auto mask4 = [&](uint2 v) {
+          if (tv <= 0) v.x = 0;
+          else if (tv == 1) v.x &= 0xffffu;
+          if (tv <= 2) v.y = 0;
+          else if (tv == 3) v.y &= 0xffffu;
+          return v;
+        };
+        for (int t = 0; t < 8; ++t) V.vt[t].u = mask4(V.vt[t].u);
+        for (int j = 0; j < NA; ++j) V.rv[j].u = mask4(V.rv[j].u);
+      }
     }
     for (int t = 0; t < 8; ++t) acc[t] = mfma16(V.vt[t].s, pb.s, acc[t]);
 #pragma unroll
@@ -673,19 +714,49 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     sincosf(static_cast<float>(kPage * omega), &step_s, &step_c);
   }
 
-  auto run_pages = [&](auto na_c) __attribute__((always_inline)) {
-    // The prefetch is issued unconditionally (past the end it re-reads the last page, an
-    // L2 hit) so that every wait below only covers the older buffer's loads.
-    KBuf buf0 = first, buf1;
-    for (int lp = lpa; lp < lpb; lp += 2) {
-      load_k(min(lp + 1, lpb - 1), buf1, na_c);
-      compute_page(lp, buf0, na_c);
-      if (lp + 1 >= lpb) break;
-      load_k(min(lp + 2, lpb - 1), buf0, na_c);
-      compute_page(lp + 1, buf1, na_c);
+  using Full = std::true_type;
+  using Masked = std::false_type;
+  // Key-side prefetches are issued unconditionally (past the end they re-read the last page,
+  // an L2 hit).  One key-side buffer B serves both loops (refilled in place by scores).
+  //
+  // General loop (the slot map, or a sub-range holding a page id outside the pool): every
+  // page is masked by its agents' rows, and a page without a base id is skipped.
+  auto run_general = [&](auto na_c) __attribute__((always_inline)) {
+    KBuf B = first;
+    VBuf v;
+    trig_for(lpa);
+    for (int lp = lpa; lp < lpb; ++lp) {
+      const bool have = B.bp >= 0;
+      const f4 s = scores(B, v, min(lp + 1, lpb - 1), na_c);
+      trig_for(lp + 1);
+      if (have) softmax_acc(s, v, na_c, Masked{}, page_rows_of(lp, na_c));
     }
   };
-  if (lpa < lpb) with_na(run_pages);
+  // Loop over full pages (pages start at lp * P and every id is in the pool).  Every page of
+  // the sub-range but its last is full for every agent of the group: a page with fewer rows
+  // is an agent's last and no other agent maps it (a fork copies a partial tail), so it ends
+  // its item.  Only the last page is masked.
+  auto run_fast = [&](auto na_c) __attribute__((always_inline)) {
+    KBuf B = first;
+    VBuf v;
+    trig_for(lpa);
+    for (int lp = lpa; lp + 1 < lpb; ++lp) {
+      const f4 s = scores(B, v, lp + 1, na_c);
+      trig_for(lp + 1);
+      softmax_acc(s, v, na_c, Full{}, Rows{});
+    }
+    const f4 s = scores(B, v, lpb - 1, na_c);
+    softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
+  };
+  if (lpa < lpb) {
+    if constexpr (kMap) {
+      with_na(run_general);
+    } else {
+      const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
+      if (__builtin_amdgcn_ballot_w64(bad) == 0) with_na(run_fast);
+      else with_na(run_general);
+    }
+  }
 
   // ---- merge the sub-range partials of each group (LSE rule), write split-K partials ----
   l_run += shfl_xor(l_run, 16);
