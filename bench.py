@@ -37,9 +37,11 @@ DECODE_WORKLOAD = "llama3_8b_mapreduce_decode"
 OTHER_DECODE_WORKLOADS = ("llama3_8b_react_decode", "qwen25_14b_batched_decode")
 PREFILL_WORKLOAD = "qwen3_8b_chunked_prefill"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_pmc_llama3_8b_mapreduce.json")
+# the sources of each split kernel (its counters are valid while these are unchanged)
 KERNEL_SOURCES = {
-    "generic": "lora_shared_prefix_amd/csrc/kernels_generic.hip",
-    "mfma": "lora_shared_prefix_amd/csrc/kernels_mfma.hip",
+    "generic": ("lora_shared_prefix_amd/csrc/kernels_generic.hip",),
+    "mfma": ("lora_shared_prefix_amd/csrc/kernels_mfma_decode.hip",
+             "lora_shared_prefix_amd/csrc/kernels_mfma_common.h"),
 }
 
 
@@ -62,8 +64,11 @@ def algorithmic_bytes(cfg, n_unique_tokens):
 
 
 def source_sha(kernel):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel):
@@ -198,8 +203,8 @@ def bench_prefill(steps, warmup):
         fops += [("fork", "root", L0, a, fk.FORK_FREEZE, 0)]
     fb = DeviceBatch(workload_geom(cfg), x, fops, agents, x["perm_b"], x["perm_r"],
                      plan=False)
+    fb.reserve_chunk(cfg.chunk_len)  # the chunk's first page starts 7 rows past a page edge
     assert fb.pstart is not None
-    fb.reserve_chunk(cfg.chunk_len)
     fl_f = cfg.n_agents * cfg.num_q_heads * per_key * sum(
         L0 + i + 1 for i in range(cfg.chunk_len))
     frozen = {"prefix": f"{L0} tokens, the last 7 in a shared read-only page",

@@ -19,7 +19,8 @@ MICROBENCH_LIB = os.path.join(PKG, "libforkkv_microbench.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 CPP_SOURCES = ["pool.cpp", "plan.cpp", "api.cpp", "caps.cpp"]
-HIP_SOURCES = ["kernels_generic.hip", "kernels_mfma.hip", "scratch.hip"]
+HIP_SOURCES = ["kernels_generic.hip", "kernels_mfma_decode.hip", "kernels_mfma_prefill.hip",
+               "scratch.hip"]
 ARCH = "gfx950"
 
 CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
