@@ -204,8 +204,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       const float x = d0[i], y = d1[i];
       const float b0 = __uint_as_float((i & 1) ? (bw0[i >> 1] & 0xffff0000u) : (bw0[i >> 1] << 16));
       const float b1 = __uint_as_float((i & 1) ? (bw1[i >> 1] & 0xffff0000u) : (bw1[i >> 1] << 16));
-      k0[i] = b0 + (x * rc[i] - y * rs[i]);
-      k1[i] = b1 + (y * rc[i] + x * rs[i]);
+      // two fused steps each: bK + x c - y s and bK + y c + x s
+      k0[i] = __builtin_fmaf(x, rc[i], __builtin_fmaf(-y, rs[i], b0));
+      k1[i] = __builtin_fmaf(y, rc[i], __builtin_fmaf(x, rs[i], b1));
     }
     for (int i = 0; i < 4; ++i) {  // advance to the next iteration (two pages on)
       const float c = rc[i] * stc[i] - rs[i] * sts[i];
