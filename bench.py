@@ -196,7 +196,7 @@ def bench_prefill(steps, warmup):
 
     # Frozen tail, same shape: the prefix ends 7 rows into a page that every agent shares
     # read-only (fork mode freeze), so each agent's chunk starts on a fresh page and the
-    # page start table (the slot map) is in use; both prefill kernels are timed.
+    # page start table (the slot map) is in use.
     L0 = cfg.prefix_len + 7
     fops = [("create", "root", 0), ("append", "root", L0)]
     for a in agents:
@@ -209,7 +209,7 @@ def bench_prefill(steps, warmup):
         L0 + i + 1 for i in range(cfg.chunk_len))
     frozen = {"prefix": f"{L0} tokens, the last 7 in a shared read-only page",
               "dense_flops_per_call": fl_f}
-    for name, kern in (("mfma", fk.KERNEL_MFMA), ("generic", fk.KERNEL_GENERIC)):
+    for name, kern in (("mfma", fk.KERNEL_MFMA),):
         run = lambda: fb.prefill(chunk, cfg.lora_scale, sm, cfg.rope_theta, out=out,
                                  kernel=kern)
         run()
