@@ -586,7 +586,7 @@ def measured_ceilings():
 
 def serving_loop(cfg, x, ops, agents, steps):
     """A serving loop of decode with append at the decode workload's shape (one input copy):
-    `steps` steps in a row on one plan.  Each step the host reserves every agent's next
+    three rounds of `steps` steps in a row on one plan (the median round is reported).  Each step the host reserves every agent's next
     token (one batched call); at a page crossing (every 16 steps here: the agents' lengths
     are multiples of 16) it also updates the device tables in place and rebuilds and
     re-uploads the plan; then the step runs -- as an eager call, and in a second pass as a
@@ -608,10 +608,11 @@ def serving_loop(cfg, x, ops, agents, steps):
             "rk_new": torch.randn(N, r, dtype=bf, device="cuda"),
             "rv_new": torch.randn(N, r, dtype=bf, device="cuda")}
     res = {}
+    rounds = 3  # the host share is noisy on a shared host: the median round is reported
     for mode in ("eager", "graph"):
         b = DeviceBatch(geom, x, ops, agents, x["perm_b"], x["perm_r"], plan=False)
         b.pool.append_batch(b.handles, 1)
-        b.refresh_tables(extra_pages=steps // 16 + 2)
+        b.refresh_tables(extra_pages=rounds * steps // 16 + 2)
         b.make_plan()
         call = lambda: b.decode_append(rows, cfg.lora_scale, sm, cfg.rope_theta)
         call()  # first step (untimed): compiles nothing, warms the device
@@ -622,32 +623,43 @@ def serving_loop(cfg, x, ops, agents, steps):
             with torch.cuda.graph(g):
                 call()
         torch.cuda.synchronize()
-        host, rebuilds = 0.0, 0
-        b.lib_host_s = 0.0
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t_wall = time.perf_counter()
-        t0.record()
-        for _ in range(steps):
-            th = time.perf_counter()
-            same, _ = b.next_step()
-            rebuilds += int(b.lens[0] % 16 == 1)
-            assert same, "the captured step outlived the plan's capacities"
-            host += time.perf_counter() - th
-            if g is not None:
-                g.replay()
-            else:
-                call()
-        t1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_wall
-        gpu_ms = t0.elapsed_time(t1)
-        res[mode] = {"steps": steps, "page_crossings": rebuilds,
-                     "wall_us_per_step": wall / steps * 1e6,
-                     "gpu_us_per_step": gpu_ms / steps * 1e3,
-                     "host_us_per_step": host / steps * 1e6,
-                     "library_host_us_per_step": b.lib_host_s / steps * 1e6,
-                     "agent_tokens_per_s": N * steps / wall}
+        per_round = []
+        for _ in range(rounds):
+            host, rebuilds, recaptures = 0.0, 0, 0
+            b.lib_host_s = 0.0
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t_wall = time.perf_counter()
+            t0.record()
+            for _ in range(steps):
+                th = time.perf_counter()
+                same, _ = b.next_step()
+                rebuilds += int(b.lens[0] % 16 == 1)
+                host += time.perf_counter() - th
+                if g is not None and not same:  # the plan outgrew its capacities: capture anew
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        call()  # (recorded, not run)
+                    recaptures += 1
+                if g is not None:
+                    g.replay()
+                else:
+                    call()
+            t1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_wall
+            gpu_ms = t0.elapsed_time(t1)
+            per_round.append({"steps": steps, "page_crossings": rebuilds, "recaptures": recaptures,
+                              "wall_us_per_step": wall / steps * 1e6,
+                              "gpu_us_per_step": gpu_ms / steps * 1e3,
+                              "host_us_per_step": host / steps * 1e6,
+                              "library_host_us_per_step": b.lib_host_s / steps * 1e6,
+                              "agent_tokens_per_s": N * steps / wall})
+        med = sorted(per_round, key=lambda r: r["wall_us_per_step"])[rounds // 2]
+        res[mode] = dict(med, rounds=rounds,
+                         wall_us_per_step_rounds=[r["wall_us_per_step"] for r in per_round],
+                         library_host_us_per_step_rounds=[r["library_host_us_per_step"]
+                                                          for r in per_round])
         del b, g
         torch.cuda.empty_cache()
     log("serving loop: " + json.dumps(res))
