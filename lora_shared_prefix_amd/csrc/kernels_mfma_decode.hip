@@ -199,9 +199,10 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   f4 accr = f4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Page buffers.  The key-side operands of page lp + 1 (base key tile, residual keys) are
-  // loaded while page lp is computed (two register buffers, used alternately); the
-  // value-side operands of page lp are loaded when its computation starts and used last.
+  // Page buffers.  One key-side buffer (base key tile, residual keys) holds page lp while
+  // its scores are formed and is refilled with page lp + 1 in place, each half as soon as
+  // it has been read; the value-side operands of page lp are loaded when its scores start
+  // and used last.
   struct KBuf {
     U4 kt[4];
     U2 rk[A];
