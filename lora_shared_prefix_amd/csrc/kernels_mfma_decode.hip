@@ -650,28 +650,58 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   }
 
   // ---- merge the sub-range partials of each group (LSE rule), write split-K partials ----
+  // Every wave of a group takes part: the n_sub partials' (m, l) give one set of weights, and
+  // wave si merges and stores the accumulator tiles [si * 8 / n_sub, (si + 1) * 8 / n_sub)
+  // (wave 0 also acc_r and (m, l)).  With one sub-range there is nothing to merge.
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  __syncthreads();  // LDS is reused for the merge
-  float* mb = reinterpret_cast<float*>(lds) + (w * 64 + lane) * kMergeFloats;
-  mb[0] = m_run;
-  mb[1] = l_run;
-  for (int t = 0; t < 8; ++t)
-    for (int i = 0; i < 4; ++i) mb[4 + 4 * t + i] = acc[t][i];
-  for (int i = 0; i < 4; ++i) mb[36 + i] = accr[i];
-  __syncthreads();
-  if (!active || si != 0) return;
-  for (int o = 1; o < n_sub; ++o) {
-    const float* ob = reinterpret_cast<float*>(lds) + ((gi + o * n_groups) * 64 + lane) * kMergeFloats;
-    const float m2 = ob[0];
-    const float M = fmaxf(m_run, m2);
-    if (M == -INFINITY) continue;
-    const float w1 = exp2f(m_run - M), w2 = exp2f(m2 - M);
-    l_run = l_run * w1 + ob[1] * w2;
+  const int per = 8 / n_sub, t0 = si * per;  // this wave's accumulator tiles
+  if (n_sub > 1) {  // uniform over the workgroup
+    __syncthreads();  // LDS is reused for the merge
+    float* mb = reinterpret_cast<float*>(lds) + (w * 64 + lane) * kMergeFloats;
+    mb[0] = m_run;
+    mb[1] = l_run;
     for (int t = 0; t < 8; ++t)
-      for (int i = 0; i < 4; ++i) acc[t][i] = acc[t][i] * w1 + ob[4 + 4 * t + i] * w2;
-    for (int i = 0; i < 4; ++i) accr[i] = accr[i] * w1 + ob[36 + i] * w2;
+      for (int i = 0; i < 4; ++i) mb[4 + 4 * t + i] = acc[t][i];
+    for (int i = 0; i < 4; ++i) mb[36 + i] = accr[i];
+    __syncthreads();
+    if (!active) return;
+    const float* ob[kWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int o = 0; o < kWaves; ++o) {
+      const int oo = o < n_sub ? o : 0;  // (partners past n_sub are never read)
+      ob[o] = reinterpret_cast<float*>(lds) + ((gi + oo * n_groups) * 64 + lane) * kMergeFloats;
+      if (o < n_sub) M = fmaxf(M, ob[o][0]);
+    }
+    float wo[kWaves], L = 0.f;
+#pragma unroll
+    for (int o = 0; o < kWaves; ++o) {
+      wo[o] = (o < n_sub && M != -INFINITY) ? exp2f(ob[o][0] - M) : 0.f;
+      if (o < n_sub) L += wo[o] * ob[o][1];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < t0 || t >= t0 + per) continue;
+      f4 v = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int o = 0; o < kWaves; ++o)
+        if (o < n_sub)
+          for (int i = 0; i < 4; ++i) v[i] += wo[o] * ob[o][4 + 4 * t + i];
+      acc[t] = v;
+    }
+    if (si == 0) {
+      f4 v = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int o = 0; o < kWaves; ++o)
+        if (o < n_sub)
+          for (int i = 0; i < 4; ++i) v[i] += wo[o] * ob[o][36 + i];
+      accr = v;
+    }
     m_run = M;
+    l_run = L;
+  } else if (!active) {
+    return;
   }
   if (!col_ok) return;
   int s_col = slot[0];
@@ -679,9 +709,13 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   for (int j = 1; j < A; ++j)
     if (jc == j) s_col = slot[j];
   const size_t row = size_t(s_col) * Hq + h * G + col % G;
-  for (int t = 0; t < 8; ++t)
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t < t0 || t >= t0 + per) continue;
     *reinterpret_cast<float4*>(p.ws_acc + row * kD + 16 * t + 4 * g4) =
         make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  }
+  if (si != 0) return;
   *reinterpret_cast<float4*>(p.ws_accr + row * kR + 4 * g4) =
       make_float4(accr[0], accr[1], accr[2], accr[3]);
   if (g4 == 0) {
