@@ -106,7 +106,8 @@ def cpu_baseline(cfg, x, ops, agents, n_sample):
     return {"value": n_sample / dt, "unit": "agent-tokens/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"{n_sample} of {cfg.n_agents} agents, all {cfg.num_q_heads} q heads, "
-                      f"fp64 numpy, {dt:.1f} s; host cpus={len(os.sched_getaffinity(0))}"}
+                      f"fp64 numpy, {dt:.1f} s; host cpus={len(os.sched_getaffinity(0))} "
+                      f"(os.cpu_count()={os.cpu_count()}), BLAS threads={blas_threads}"}
 
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 (spec)
