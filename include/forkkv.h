@@ -327,7 +327,13 @@ typedef struct {
                                "Design vs APC": the fork-aware slot map) */
 } forkkv_decode_args;
 
-/* Errors: FORKKV_EINVAL (null pointers, a plan of another geometry, max_pages below the
+/* Page ids are read from btab / rtab at launch; the plan fixes only which agents share
+ * which logical pages.  The plan refuses missing base pages, but an entry changed after
+ * the build to -1 or to an id outside its pool is taken as a missing page (the rule under
+ * "Missing pages" below); for a base page that several batch sequences share, the change
+ * must be made in every holder's row.
+ *
+ * Errors: FORKKV_EINVAL (null pointers, a plan of another geometry, max_pages below the
  * plan's, a small workspace, non-finite scales, sm_scale <= 0, theta <= 0, no pstart
  * for a plan over a frozen tail);
  * FORKKV_ESTATE (pool without device storage, plan not uploaded); FORKKV_EHIP. */
@@ -442,7 +448,7 @@ typedef struct {
  * on it are not stored.  A residual table entry of -1 (a sequence without residual pages,
  * such as a base-only snapshot) reads as zero residual rows (the key and value are the base
  * rows alone), and chunk residual rows that fall on it are not stored.  Both kernels follow
- * this rule.
+ * this rule, here and in decode.
  *
  * Errors: FORKKV_EINVAL for null pointers, C < 1, a head count that is not a multiple of
  * Hkv, rows outside the tables, positions that do not strictly increase, scales out of

@@ -190,3 +190,78 @@ def test_prefill_over_missing_pages(kernel):
                                      arrays["v_new"], arrays["rk_new"], arrays["rv_new"])
     assert np.array_equal(b.bcache.cpu().numpy().view(np.uint16), exp_b)
     assert np.array_equal(b.rcache.cpu().numpy().view(np.uint16), exp_r)
+
+
+@pytest.mark.parametrize("kernel,dtype,d,r,Hq,Hkv", [
+    (fk.KERNEL_MFMA, "bf16", 128, 16, 16, 4),
+    (fk.KERNEL_GENERIC, "f32", 32, 8, 4, 2),
+])
+def test_decode_reads_tables_at_launch(kernel, dtype, d, r, Hq, Hkv):
+    """Decode takes page ids from the tables at launch, not from the plan: entries changed
+    after the plan was built -- a page evicted from every holder, an id outside its pool, a
+    residual page dropped -- follow the missing-page rule of the ForkKV study note ("Error /
+    eviction recovery"): no key on a missing base page, a zero residual without a residual
+    page.  Against the oracle on the same tables with those entries -1; with every base entry
+    gone each output is zero (no keys); the original tables give the original output again,
+    bit for bit.  On the MFMA kernel this is the masked page loop without a slot map."""
+    rng = np.random.default_rng(83)
+    L0, n_agents, npg, nrp = 16 * 40, 4, 160, 256
+    agents = [f"a{j}" for j in range(n_agents)]
+    ops = [("create", "t", 0), ("append", "t", L0)]
+    ops += [("fork", "t", L0, a) for a in agents]
+    ops += [("append", a, int(rng.integers(20, 90))) for a in agents]
+    perm_b = rng.permutation(npg).astype(np.int32)
+    perm_r = rng.permutation(nrp).astype(np.int32)
+    arrays = dict(bpool=encode(rng.standard_normal((npg, 2, Hkv, 16 * d)), dtype),
+                  rpool=encode(rng.standard_normal((nrp, 2, 16 * r)), dtype),
+                  Bk=encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype),
+                  Bv=encode(0.3 * rng.standard_normal((n_agents, r, Hkv * d)), dtype),
+                  q=encode(rng.standard_normal((n_agents, Hq, d)), dtype))
+    geom = dict(num_bpages=npg, num_rpages=nrp, num_kv_heads=Hkv, num_q_heads=Hq,
+                head_dim=d, rank=r, dtype=dtype)
+    print(f"[gpu-evict] tables at launch kernel={kernel} {dtype} d={d}", flush=True)
+    b = DeviceBatch(geom, arrays, ops, agents, perm_b, perm_r, kernel=kernel)
+    sm = 1.0 / np.sqrt(d)
+    as_int = torch.int32 if dtype == "f32" else torch.int16
+    before = b.decode(2.0, sm, 5e5).clone()
+    torch.cuda.synchronize()
+    bt0, rt0 = b.btab_host.copy(), b.rtab_host.copy()
+    # oracle side: pool bytes from the inputs and the model's fork packing, not the device
+    _, _, cows = model_replay(npg, nrp, perm_b, perm_r, ops)
+    host_b = apply_cows_host(arrays["bpool"], cows, Hkv, d)
+    geo = Geometry(page_size=16, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, rank=r,
+                   dtype=dtype)
+
+    bt, rt = bt0.copy(), rt0.copy()
+    assert (bt0[:, 9] == bt0[0, 9]).all() and (bt0[:, 22] == bt0[0, 22]).all()
+    assert (bt0[:, 41] >= 0).all() and (rt0[:, 40] >= 0).all() and rt0[2, 3] >= 0
+    bt[:, 9] = npg + 5   # a trunk page, outside the pool in every holder's table
+    bt[:, 22] = -1       # a trunk page evicted from every holder
+    bt[1, 41] = -1       # a private page
+    rt[2, 3] = nrp + 1   # a residual page outside the pool
+    rt[3, 40] = -1       # a residual page dropped
+    b.btab.copy_(torch.from_numpy(bt))
+    b.rtab.copy_(torch.from_numpy(rt))
+    got = b.decode(2.0, sm, 5e5).clone()
+    torch.cuda.synchronize()
+    bt_ref, rt_ref = bt.copy(), rt.copy()
+    bt_ref[bt_ref >= npg] = -1
+    rt_ref[rt_ref >= nrp] = -1
+    ref = decode_attention(geo, host_b, arrays["rpool"], bt_ref, rt_ref, np.array(b.lens),
+                           arrays["q"], arrays["Bk"], arrays["Bv"], 2.0, sm, 5e5)
+    assert_close(gpu_values(got, dtype), ref, f"decode over changed tables k={kernel}",
+                 scale_abs=True)
+    full = decode_attention(geo, host_b, arrays["rpool"], bt0, rt0, np.array(b.lens),
+                            arrays["q"], arrays["Bk"], arrays["Bv"], 2.0, sm, 5e5)
+    assert np.abs(ref - full).max() > 1e-2, "the changed entries must change the output"
+
+    b.btab.fill_(-1)  # every base page gone: no keys anywhere
+    none = b.decode(2.0, sm, 5e5).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(none.view(as_int), torch.zeros_like(none).view(as_int))
+
+    b.btab.copy_(torch.from_numpy(bt0))
+    b.rtab.copy_(torch.from_numpy(rt0))
+    again = b.decode(2.0, sm, 5e5)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(as_int), before.view(as_int))
