@@ -21,6 +21,39 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // rows per workgroup
 
+// cos and sin (fp64) of an angle in [0, 2 pi]: a reduction by quarter turns leaves
+// t = x - q pi/2 in [-pi/4, pi/4] (pi/2 in two parts, so t is exact to rounding), where the
+// Taylor series of sin t through t^15 and of cos t through t^16 are exact to below 1e-16.
+// Far lighter in registers than the general library routine, which must also reduce huge
+// arguments.
+__device__ __forceinline__ void sincos_turn(double x, double& s, double& c) {
+  constexpr double kHalfPiHi = 1.5707963267948966192;
+  constexpr double kHalfPiLo = 6.123233995736766036e-17;
+  const double q = rint(x * 0.63661977236758134308);  // x / (pi/2), rounded
+  const double t = fma(-q, kHalfPiLo, fma(-q, kHalfPiHi, x));
+  const double u = t * t;
+  double ps = -1.0 / 1307674368000.0;  // -1/15!
+  ps = fma(ps, u, 1.0 / 6227020800.0);
+  ps = fma(ps, u, -1.0 / 39916800.0);
+  ps = fma(ps, u, 1.0 / 362880.0);
+  ps = fma(ps, u, -1.0 / 5040.0);
+  ps = fma(ps, u, 1.0 / 120.0);
+  ps = fma(ps, u, -1.0 / 6.0);
+  const double st = fma(ps * u, t, t);
+  double pc = 1.0 / 20922789888000.0;  // 1/16!
+  pc = fma(pc, u, -1.0 / 87178291200.0);
+  pc = fma(pc, u, 1.0 / 479001600.0);
+  pc = fma(pc, u, -1.0 / 3628800.0);
+  pc = fma(pc, u, 1.0 / 40320.0);
+  pc = fma(pc, u, -1.0 / 720.0);
+  pc = fma(pc, u, 1.0 / 24.0);
+  pc = fma(pc, u, -0.5);
+  const double ct = fma(pc, u, 1.0);
+  const int k = static_cast<int>(q) & 3;  // sin and cos of t + k pi/2
+  s = k == 0 ? st : k == 1 ? ct : k == 2 ? -st : -ct;
+  c = k == 0 ? ct : k == 1 ? -st : k == 2 ? -ct : st;
+}
+
 // kMap: the agents hold frozen tails, so pages start where the page start table says (the
 // slot map) and a page may hold fewer than 16 rows; without it page lp starts at lp * P and
 // none of that bookkeeping is compiled in.
@@ -34,6 +67,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __shared__ __align__(16) uint4 s_rv[2][64];         // [buf][lane], same page halves
   __shared__ int s_miss[2][2];                          // [buf][page]: base page missing
   __shared__ int s_pos[2][2], s_vrows[2][2];            // [buf][page]: start, valid rows
+  __shared__ double s_om[kD / 2];                        // RoPE frequencies w_j (fp64)
   const int Hkv = p.num_kv_heads, G = p.group, Hq = p.num_q_heads, C = p.chunk_len;
   // the workgroups of one KV head share an XCD (block ids are dealt round robin over the
   // 8 XCDs), so the shared prefix of that head streams through one L2
@@ -93,12 +127,13 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // RoPE of this lane's 4 frequencies j_i = perm_dim(tp, 4 g4 + i) at position
   // t = 16 (2 it + pg) + col: exact (fp64-reduced) every 32 iterations, a rotation by
   // 32 w_j per iteration in between.
-  const double log2_theta = log2(static_cast<double>(p.rope_theta));
+  if (tid < kD / 2)
+    s_om[tid] = exp2(-2.0 * tid / kD * log2(static_cast<double>(p.rope_theta)));
+  __syncthreads();
   float stc[4], sts[4];
   for (int i = 0; i < 4; ++i) {
-    const double om = exp2(-2.0 * perm_dim(tp, 4 * g4 + i) / kD * log2_theta);
     double sv, cv;
-    sincos(2 * kPage * om, &sv, &cv);
+    sincos_turn(2 * kPage * s_om[perm_dim(tp, 4 * g4 + i)], sv, cv);  // 32 w_j <= 32 < 2 pi
     stc[i] = static_cast<float>(cv);
     sts[i] = static_cast<float>(sv);
   }
@@ -107,11 +142,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // exact cos/sin (fp64-reduced angle) of this lane's key position base + col
   auto anchor_at = [&](int base) {
     for (int i = 0; i < 4; ++i) {
-      const double om = exp2(-2.0 * perm_dim(tp, 4 * g4 + i) / kD * log2_theta);
-      double ang = static_cast<double>(base + col) * om;
+      double ang = static_cast<double>(base + col) * s_om[perm_dim(tp, 4 * g4 + i)];
       ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
       double sv, cv;
-      sincos(ang, &sv, &cv);
+      sincos_turn(ang, sv, cv);
       rc[i] = static_cast<float>(cv) * p.lora_scale;
       rs[i] = static_cast<float>(sv) * p.lora_scale;
     }
@@ -170,6 +204,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   f4 acc[2][8];
   f4 accr[2];
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // m_run + 8 (the rescale threshold) and the reference the exponents are taken against
+  // (-1e30 while a row has no key yet: no -inf - -inf), both updated only on a rescale
+  float m_thr[2] = {-INFINITY, -INFINITY}, m_ref[2] = {-1e30f, -1e30f};
   for (int rt = 0; rt < 2; ++rt) {
     for (int t = 0; t < 8; ++t) acc[rt][t] = f4{0.f, 0.f, 0.f, 0.f};
     accr[rt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -188,10 +225,10 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     const int buf = it & 1;
     const int lp = 2 * it + pg;
     // the page's first position; the recurrence below stands at next_base, and is re-anchored
-    // (fp64) every 32 iterations and wherever a page does not start where it stands (a frozen
-    // tail in between)
+    // (fp64) every 32 iterations (by the loop below) and wherever a page does not start where
+    // it stands (a frozen tail in between)
     const int base = kMap ? B.pos : lp * kPage;
-    if (((it & 31) == 0 && it) || (kMap && base != next_base)) anchor_at(base);
+    if (kMap && base != next_base) anchor_at(base);
     next_base = base + 2 * kPage;
     // rebuild this wave's two key tiles of page pg: K = bK + RoPE(s * rK B_k)
     U2 rk;
@@ -288,7 +325,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     }
     for (int rt = 0; rt < 2; ++rt) {
       // raw scores (q.k); the softmax scale (> 0, log2 units) is applied inside the exp
-      float sc[8], pmax = -INFINITY;
+      float sc[8];
       if (unmasked) {
         for (int pgi = 0; pgi < 2; ++pgi)
           for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = sc4[rt][pgi][i];
@@ -302,20 +339,26 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
           for (int i = 0; i < 4; ++i) sc[4 * pgi + i] = i <= lim ? sc4[rt][pgi][i] : -INFINITY;
         }
       }
-      for (int e = 0; e < 8; ++e) pmax = fmaxf(pmax, sc[e]);
-      pmax = max_over_rows(pmax) * qscale;
-      const bool grow = pmax > m_run[rt] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // Lazy rescale: the running maximum moves only when a row's maximum passes it by more
+      // than 8 (a factor 256 of headroom in the fp32 sums).  A row's maximum passes the
+      // threshold exactly when one of its four lanes' own maxima does, so the cross-lane
+      // reduction is needed only then.
+      float lmax = -INFINITY;
+      for (int e = 0; e < 8; ++e) lmax = fmaxf(lmax, sc[e]);
+      if (__builtin_amdgcn_ballot_w64(lmax * qscale > m_thr[rt]) != 0) {
+        const float pmax = max_over_rows(lmax) * qscale;
+        const bool grow = pmax > m_thr[rt];
         const float m_new = grow ? pmax : m_run[rt];
         const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
         l_run[rt] *= alpha;
         for (int t = 0; t < 8; ++t) acc[rt][t] *= alpha;
         accr[rt] *= alpha;
         m_run[rt] = m_new;
+        m_thr[rt] = m_new + 8.f;
+        m_ref[rt] = max2(m_new, -1e30f);
       }
-      const float m_ref = max2(m_run[rt], -1e30f);
       float pr[8];
-      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref));
+      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref[rt]));
       l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       U4 pb;  // P^T operand, K = 32 keys: elements 0..3 page 0, 4..7 page 1
       pb.u = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
@@ -335,14 +378,20 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // staged, so those loads fly during the whole compute phase.  Two LDS
   // buffers alternate, so one barrier per iteration suffices: iteration it + 1 stages into
   // the other buffer, and iteration it + 2 waits behind the next barrier.
+  // The iterations run in blocks of 32, each starting from an exact (fp64) anchor, so the
+  // page loop itself carries only the recurrence.
   PfBuf pb_;
   load(0, pb_);
-  anchor_at(pg * kPage);  // (re-anchored at the first page's start where the slot map says)
-  for (int it = 0; it < n_it; ++it) {
-    stage(it, pb_);
-    load(min(it + 1, n_it - 1), pb_);
-    __syncthreads();
-    compute(it);
+  for (int it0 = 0; it0 < n_it; it0 += 32) {
+    next_base = kMap ? pb_.pos : (2 * it0 + pg) * kPage;
+    anchor_at(next_base);
+    const int it1 = min(it0 + 32, n_it);
+    for (int it = it0; it < it1; ++it) {
+      stage(it, pb_);
+      load(min(it + 1, n_it - 1), pb_);
+      __syncthreads();
+      compute(it);
+    }
   }
 
   // ---- epilogue: o = (acc + s * acc_r B_v) / l, B_v applied once ------------------------
