@@ -203,7 +203,12 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
 
   f4 acc[2][8];
   f4 accr[2];
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  // softmax denominators: a matrix product of the bf16 probabilities with a ones operand,
+  // so every lane of a row holds that row's sum (the same rounded weights as acc)
+  f4 l_acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  bf8 ones;
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
   // m_run + 8 (the rescale threshold) and the reference the exponents are taken against
   // (-1e30 while a row has no key yet: no -inf - -inf), both updated only on a rescale
   float m_thr[2] = {-INFINITY, -INFINITY}, m_ref[2] = {-1e30f, -1e30f};
@@ -350,7 +355,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
         const bool grow = pmax > m_thr[rt];
         const float m_new = grow ? pmax : m_run[rt];
         const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-        l_run[rt] *= alpha;
+        l_acc[rt] *= alpha;
         for (int t = 0; t < 8; ++t) acc[rt][t] *= alpha;
         accr[rt] *= alpha;
         m_run[rt] = m_new;
@@ -359,7 +364,6 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       }
       float pr[8];
       for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_ref[rt]));
-      l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       U4 pb;  // P^T operand, K = 32 keys: elements 0..3 page 0, 4..7 page 1
       pb.u = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
@@ -371,6 +375,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       U4 rvop;
       rvop.u = s_rv[buf][lane];
       accr[rt] = mfma32(rvop.b, pb.b, accr[rt]);
+      l_acc[rt] = mfma32(ones, pb.b, l_acc[rt]);
     }
   };
 
@@ -408,9 +413,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __syncthreads();
   uint16_t* out = static_cast<uint16_t*>(p.out);
   for (int rt = 0; rt < 2; ++rt) {
-    float l = l_run[rt];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    const float l = l_acc[rt][0];
     if (!rok[rt]) continue;
     const int row = row0 + kPfRowsPerWave * w + 16 * rt + col;
     const int qi = row / G, g = row % G;
