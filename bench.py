@@ -527,7 +527,40 @@ def _microbench_lib():
                                  C.c_void_p]
     L.mb_mfma_bf16.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_void_p]
     L.mb_mfma_chains.restype = C.c_int
+    L.mb_pipe_probe.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                C.c_int, C.c_void_p]
     return L
+
+
+def pipe_probes():
+    """How the matrix cores of a SIMD share it with another wave's work: 256 workgroups of
+    512 threads (one per compute unit; waves w and w + 4 share a SIMD), waves 0-3 running 16
+    bf16 16x16x32 MFMAs per trip, waves 4-7 64 FMAs, 64 exp2 or 16 ds_read_b128 per trip
+    (or both waves that same work).  Returns ns per trip for each combination."""
+    import torch
+    L = _microbench_lib()
+    sp = torch.cuda.current_stream().cuda_stream
+    ops = torch.tensor([0x3F80] * 8 + [0x3D00] * 8, dtype=torch.int16, device="cuda")
+    blocks, iters = 256, 5000
+    out = torch.zeros(blocks * 8, dtype=torch.float32, device="cuda")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def ns(mode, mfma, chains):
+        assert L.mb_pipe_probe(mode, mfma, chains, ops.data_ptr(), iters, out.data_ptr(),
+                               blocks, sp) == 0
+        t0.record()
+        L.mb_pipe_probe(mode, mfma, chains, ops.data_ptr(), iters, out.data_ptr(), blocks, sp)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e6 / iters
+
+    res = {f"16 MFMA, {c} chain(s), other wave idle": ns(0, 1, c) for c in (1, 2, 4, 16)}
+    for mode, what in ((1, "64 FMA"), (2, "64 exp2"), (3, "16 ds_read_b128")):
+        res[f"{what} alone"] = ns(mode, 0, 4)
+        res[f"{what} beside 16 MFMA (4 chains)"] = ns(mode, 1, 4)
+        res[f"{what} on both waves of each SIMD"] = ns(mode, 2, 4)
+    return {"ns_per_trip": res, "setup": f"{blocks} workgroups x 512 threads, {iters} trips"}
 
 
 def measured_ceilings():
@@ -706,6 +739,8 @@ def main():
                     help="skip decode-with-append, frozen-tail decode and eviction/refill timing")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing chunked prefill on the Qwen3-8B 131072-prefix workload")
+    ap.add_argument("--pipe-probes", action="store_true",
+                    help="time the SIMD pipe-sharing probes and exit")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many MiB (PMC scaling)")
     args = ap.parse_args()
@@ -721,6 +756,9 @@ def main():
     from lora_shared_prefix_amd import forkkv as fk
     from lora_shared_prefix_amd.session import DeviceBatch, workload_geom
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.pipe_probes:
+        print(json.dumps(pipe_probes()))
+        return
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * 2 ** 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
