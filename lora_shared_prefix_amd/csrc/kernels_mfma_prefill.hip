@@ -21,8 +21,9 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // rows per workgroup
 
-// cos and sin (fp64) of an angle in [0, 2 pi]: a reduction by quarter turns leaves
-// t = x - q pi/2 in [-pi/4, pi/4] (pi/2 in two parts, so t is exact to rounding), where the
+// cos and sin (fp64) of a moderate angle (here at most 2 pi, or 32 for the per-iteration
+// step): a reduction by a small number q of quarter turns leaves t = x - q pi/2 in
+// [-pi/4, pi/4] (pi/2 in two parts, a fused step each, so t is exact to rounding), where the
 // Taylor series of sin t through t^15 and of cos t through t^16 are exact to below 1e-16.
 // Far lighter in registers than the general library routine, which must also reduce huge
 // arguments.
@@ -133,7 +134,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   float stc[4], sts[4];
   for (int i = 0; i < 4; ++i) {
     double sv, cv;
-    sincos_turn(2 * kPage * s_om[perm_dim(tp, 4 * g4 + i)], sv, cv);  // 32 w_j <= 32 < 2 pi
+    sincos_turn(2 * kPage * s_om[perm_dim(tp, 4 * g4 + i)], sv, cv);  // 32 w_j <= 32
     stc[i] = static_cast<float>(cv);
     sts[i] = static_cast<float>(sv);
   }
