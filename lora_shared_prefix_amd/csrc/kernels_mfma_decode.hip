@@ -313,12 +313,14 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
   // Scores of the page whose key-side operands B holds (angles from trig_for of that page):
   // the shared base tile, plus for each agent its rotated residual key; this lane's column's
-  // agent is selected.  The page's value-side operands are loaded into V first, and B is
-  // refilled with page lp_next's key-side operands as its own are consumed.  Rows past a page's valid rows give arbitrary scores
-  // (their bytes may even be NaN); softmax_acc masks them out before any arithmetic.
-  auto scores = [&](KBuf& B, VBuf& V, int lp_next, auto na_c) -> f4 {
+  // agent is selected.  The page's value-side operands are loaded into V first (unless
+  // pre_c: then they are there already, loaded a page ahead), and B is refilled with page
+  // lp_next's key-side operands as its own are consumed.  Rows past a page's valid rows give
+  // arbitrary scores (their bytes may even be NaN); softmax_acc masks them out before any
+  // arithmetic.
+  auto scores = [&](KBuf& B, VBuf& V, int lp_next, auto na_c, auto pre_c) -> f4 {
     constexpr int NA = decltype(na_c)::value;
-    load_v(B, V, na_c);
+    if constexpr (!decltype(pre_c)::value) load_v(B, V, na_c);
     f4 sb = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < 4; ++c) {
       U4 qb;
@@ -618,25 +620,55 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     trig_for(lpa);
     for (int lp = lpa; lp < lpb; ++lp) {
       const bool have = B.bp >= 0;
-      const f4 s = scores(B, v, min(lp + 1, lpb - 1), na_c);
+      const f4 s = scores(B, v, min(lp + 1, lpb - 1), na_c, std::false_type{});
       trig_for(lp + 1);
       if (have) softmax_acc(s, v, na_c, Masked{}, page_rows_of(lp, na_c));
     }
   };
-  // Loop over full pages (pages start at lp * P and every id is in the pool).  Every page of
-  // the sub-range but its last is full for every agent of the group: a page with fewer rows
-  // is an agent's last and no other agent maps it (a fork copies a partial tail), so it ends
-  // its item.  Only the last page is masked.
+  // Loops over full pages (pages start at lp * P and every id is in the pool).  Every page
+  // of the sub-range but its last is full for every agent of the group: a page with fewer
+  // rows is an agent's last and no other agent maps it (a fork copies a partial tail), so it
+  // ends its item.  Only the last page is masked.  Long sub-ranges take run_fast_ahead, which
+  // loads each page's value tiles a page before their use (two value buffers, the loop
+  // taken two pages at a time); short ones, where that set-up does not pay, run_fast, which
+  // loads them when the page's scores start.
+  auto run_fast_ahead = [&](auto na_c) __attribute__((always_inline)) {
+    KBuf B = first;
+    VBuf va, vb;
+    load_v(B, va, na_c);
+    trig_for(lpa);
+    // page lp's scores refill B with page lp + 1's key side; that page's values are loaded
+    // right after, a page ahead of their use, into the other buffer
+    auto page = [&](int lp, VBuf& cur, VBuf& nxt) __attribute__((always_inline)) {
+      const f4 s = scores(B, cur, lp + 1, na_c, std::true_type{});
+      load_v(B, nxt, na_c);
+      trig_for(lp + 1);
+      softmax_acc(s, cur, na_c, Full{}, Rows{});
+    };
+    int lp = lpa;
+    for (; lp + 2 < lpb; lp += 2) {
+      page(lp, va, vb);
+      page(lp + 1, vb, va);
+    }
+    if (lp + 1 < lpb) {
+      page(lp, va, vb);
+      const f4 s = scores(B, vb, lpb - 1, na_c, std::true_type{});
+      softmax_acc(s, vb, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
+    } else {
+      const f4 s = scores(B, va, lpb - 1, na_c, std::true_type{});
+      softmax_acc(s, va, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
+    }
+  };
   auto run_fast = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;
     VBuf v;
     trig_for(lpa);
     for (int lp = lpa; lp + 1 < lpb; ++lp) {
-      const f4 s = scores(B, v, lp + 1, na_c);
+      const f4 s = scores(B, v, lp + 1, na_c, std::false_type{});
       trig_for(lp + 1);
       softmax_acc(s, v, na_c, Full{}, Rows{});
     }
-    const f4 s = scores(B, v, lpb - 1, na_c);
+    const f4 s = scores(B, v, lpb - 1, na_c, std::false_type{});
     softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
   };
   if (lpa < lpb) {
@@ -644,7 +676,10 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       with_na(run_general);
     } else {
       const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
-      if (__builtin_amdgcn_ballot_w64(bad) == 0) with_na(run_fast);
+      if (__builtin_amdgcn_ballot_w64(bad) == 0) {
+        if (lpb - lpa >= 8) with_na(run_fast_ahead);
+        else with_na(run_fast);
+      }
       else with_na(run_general);
     }
   }
