@@ -252,14 +252,20 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     load_kt(lp, B);
     load_rk(lp, B, na_c);
   };
-  auto load_v = [&](const KBuf& B, VBuf& V, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
+  auto load_vt = [&](const KBuf& B, U2 (&vt)[8]) {
     const uint16_t* vt_base = bcache + (size_t(max(B.bp, 0)) * 2 * Hkv + Hkv + h) * tile;
     for (int t = 0; t < 8; ++t)
-      V.vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
+      vt[t].u = *reinterpret_cast<const uint2*>(vt_base + 256 * t + 4 * lane);
+  };
+  auto load_rv = [&](const KBuf& B, VBuf& V, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
     for (int j = 0; j < NA; ++j)
       V.rv[j].u = *reinterpret_cast<const uint2*>(B.rb[j] + kPage * kR + 4 * lane);
+  };
+  auto load_v = [&](const KBuf& B, VBuf& V, auto na_c) {
+    load_vt(B, V.vt);
+    load_rv(B, V, na_c);
   };
 
   // A page's work is split into trig_for (RoPE angles), scores (key tiles and rotated
@@ -313,14 +319,16 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
 
   // Scores of the page whose key-side operands B holds (angles from trig_for of that page):
   // the shared base tile, plus for each agent its rotated residual key; this lane's column's
-  // agent is selected.  The page's value-side operands are loaded into V first (unless
-  // pre_c: then they are there already, loaded a page ahead), and B is refilled with page
-  // lp_next's key-side operands as its own are consumed.  Rows past a page's valid rows give
+  // agent is selected.  The page's value-side operands are loaded into V first, except what
+  // the caller has already loaded a page ahead: pre_c is 0 (nothing), 1 (the base value
+  // tiles) or 2 (all of them).  B is refilled with page lp_next's key-side operands as its
+  // own are consumed.  Rows past a page's valid rows give
   // arbitrary scores (their bytes may even be NaN); softmax_acc masks them out before any
   // arithmetic.
   auto scores = [&](KBuf& B, VBuf& V, int lp_next, auto na_c, auto pre_c) -> f4 {
     constexpr int NA = decltype(na_c)::value;
-    if constexpr (!decltype(pre_c)::value) load_v(B, V, na_c);
+    if constexpr (decltype(pre_c)::value == 0) load_v(B, V, na_c);
+    else if constexpr (decltype(pre_c)::value == 1) load_rv(B, V, na_c);
     f4 sb = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < 4; ++c) {
       U4 qb;
@@ -620,7 +628,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     trig_for(lpa);
     for (int lp = lpa; lp < lpb; ++lp) {
       const bool have = B.bp >= 0;
-      const f4 s = scores(B, v, min(lp + 1, lpb - 1), na_c, std::false_type{});
+      const f4 s = scores(B, v, min(lp + 1, lpb - 1), na_c, std::integral_constant<int, 0>{});
       trig_for(lp + 1);
       if (have) softmax_acc(s, v, na_c, Masked{}, page_rows_of(lp, na_c));
     }
@@ -628,10 +636,12 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   // Loops over full pages (pages start at lp * P and every id is in the pool).  Every page
   // of the sub-range but its last is full for every agent of the group: a page with fewer
   // rows is an agent's last and no other agent maps it (a fork copies a partial tail), so it
-  // ends its item.  Only the last page is masked.  Long sub-ranges take run_fast_ahead, which
-  // loads each page's value tiles a page before their use (two value buffers, the loop
-  // taken two pages at a time); short ones, where that set-up does not pay, run_fast, which
-  // loads them when the page's scores start.
+  // ends its item.  Only the last page is masked.  Long sub-ranges load a page's value
+  // operands a page before their use: run_fast_ahead all of them (two value buffers, the
+  // loop taken two pages at a time), run_fast_ahead_vt only the base value tiles, for the
+  // four-agent group, whose registers do not hold a second full buffer without spilling.
+  // Short sub-ranges, where that set-up does not pay, take run_fast, which loads them when
+  // the page's scores start.
   auto run_fast_ahead = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;
     VBuf va, vb;
@@ -640,7 +650,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     // page lp's scores refill B with page lp + 1's key side; that page's values are loaded
     // right after, a page ahead of their use, into the other buffer
     auto page = [&](int lp, VBuf& cur, VBuf& nxt) __attribute__((always_inline)) {
-      const f4 s = scores(B, cur, lp + 1, na_c, std::true_type{});
+      const f4 s = scores(B, cur, lp + 1, na_c, std::integral_constant<int, 2>{});
       load_v(B, nxt, na_c);
       trig_for(lp + 1);
       softmax_acc(s, cur, na_c, Full{}, Rows{});
@@ -652,23 +662,39 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     }
     if (lp + 1 < lpb) {
       page(lp, va, vb);
-      const f4 s = scores(B, vb, lpb - 1, na_c, std::true_type{});
+      const f4 s = scores(B, vb, lpb - 1, na_c, std::integral_constant<int, 2>{});
       softmax_acc(s, vb, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
     } else {
-      const f4 s = scores(B, va, lpb - 1, na_c, std::true_type{});
+      const f4 s = scores(B, va, lpb - 1, na_c, std::integral_constant<int, 2>{});
       softmax_acc(s, va, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
     }
+  };
+  auto run_fast_ahead_vt = [&](auto na_c) __attribute__((always_inline)) {
+    KBuf B = first;
+    VBuf v;
+    U2 vn[8];
+    load_vt(B, v.vt);
+    trig_for(lpa);
+    for (int lp = lpa; lp + 1 < lpb; ++lp) {
+      const f4 s = scores(B, v, lp + 1, na_c, std::integral_constant<int, 1>{});
+      load_vt(B, vn);
+      trig_for(lp + 1);
+      softmax_acc(s, v, na_c, Full{}, Rows{});
+      for (int t = 0; t < 8; ++t) v.vt[t] = vn[t];
+    }
+    const f4 s = scores(B, v, lpb - 1, na_c, std::integral_constant<int, 1>{});
+    softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
   };
   auto run_fast = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;
     VBuf v;
     trig_for(lpa);
     for (int lp = lpa; lp + 1 < lpb; ++lp) {
-      const f4 s = scores(B, v, lp + 1, na_c, std::false_type{});
+      const f4 s = scores(B, v, lp + 1, na_c, std::integral_constant<int, 0>{});
       trig_for(lp + 1);
       softmax_acc(s, v, na_c, Full{}, Rows{});
     }
-    const f4 s = scores(B, v, lpb - 1, na_c, std::false_type{});
+    const f4 s = scores(B, v, lpb - 1, na_c, std::integral_constant<int, 0>{});
     softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
   };
   if (lpa < lpb) {
@@ -677,7 +703,10 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     } else {
       const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
       if (__builtin_amdgcn_ballot_w64(bad) == 0) {
-        if (lpb - lpa >= 8) with_na(run_fast_ahead);
+        if (lpb - lpa >= 8) {
+          if constexpr (A >= 4) with_na(run_fast_ahead_vt);
+          else with_na(run_fast_ahead);
+        }
         else with_na(run_fast);
       }
       else with_na(run_general);
