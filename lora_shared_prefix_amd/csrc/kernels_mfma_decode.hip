@@ -36,8 +36,8 @@ constexpr int kBkBytes = kItemAgents * 8 * 64 * 8;      // [agent][tile][lane][4
 constexpr int kTrigBytes = 2 * kPage * kTrigPad * 2;    // cos, sin: [c][j] (scaled by s)
 constexpr int kPageTrigBytes = kWaves * 2 * 64 * 2;     // per wave: cos[64], sin[64]
 constexpr int kQhBytes = kWaves * 4 * 64 * 16;          // per wave: bf16 q, [chunk][lane]
-constexpr int kMergeFloats = 4 + 32 + 4;                // m, l, pad, pad | acc[32] | accr[4]
-constexpr int kMergeBytes = kWaves * 64 * kMergeFloats * 4;
+constexpr int kMergeVecs = 1 + 8 + 1;                   // (m, l, -, -) | acc[8] | accr (float4)
+constexpr int kMergeBytes = kMergeVecs * kWaves * 64 * 16;
 constexpr int kLdsMain = kBkBytes + kTrigBytes + kPageTrigBytes + kQhBytes;
 constexpr int kLdsBytes = kLdsMain > kMergeBytes ? kLdsMain : kMergeBytes;
 
@@ -636,12 +636,13 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   // Loops over full pages (pages start at lp * P and every id is in the pool).  Every page
   // of the sub-range but its last is full for every agent of the group: a page with fewer
   // rows is an agent's last and no other agent maps it (a fork copies a partial tail), so it
-  // ends its item.  Only the last page is masked.  Long sub-ranges load a page's value
-  // operands a page before their use: run_fast_ahead all of them (two value buffers, the
-  // loop taken two pages at a time), run_fast_ahead_vt only the base value tiles, for the
-  // four-agent group, whose registers do not hold a second full buffer without spilling.
-  // Short sub-ranges, where that set-up does not pay, take run_fast, which loads them when
-  // the page's scores start.
+  // ends its item.  Only the last page is masked.  Value operands loaded a page before their
+  // use: the four-agent kernel (whose registers do not hold a second full value buffer
+  // without spilling) takes run_fast_ahead_vt on every sub-range -- the base value tiles of
+  // page lp + 1 are loaded into the one buffer right after page lp's value products have
+  // read it; the other kernels take run_fast_ahead on sub-ranges of 8 pages or more (all
+  // value operands, two buffers, the loop taken two pages at a time) and run_fast, which
+  // loads them when the page's scores start, on shorter ones, where that set-up does not pay.
   auto run_fast_ahead = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;
     VBuf va, vb;
@@ -672,15 +673,18 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   auto run_fast_ahead_vt = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;
     VBuf v;
-    U2 vn[8];
     load_vt(B, v.vt);
     trig_for(lpa);
+    // page lp + 1's base value tiles are loaded as soon as page lp's value products have
+    // read the buffer, a whole page before their own use; no memory read may be scheduled
+    // above those products (a read hoisted there would need a second buffer and a register
+    // copy at the loop's end, which waits for every load issued in the page)
     for (int lp = lpa; lp + 1 < lpb; ++lp) {
       const f4 s = scores(B, v, lp + 1, na_c, std::integral_constant<int, 1>{});
-      load_vt(B, vn);
       trig_for(lp + 1);
       softmax_acc(s, v, na_c, Full{}, Rows{});
-      for (int t = 0; t < 8; ++t) v.vt[t] = vn[t];
+      __builtin_amdgcn_sched_barrier(0x078F);
+      load_vt(B, v.vt);
     }
     const f4 s = scores(B, v, lpb - 1, na_c, std::integral_constant<int, 1>{});
     softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
@@ -703,10 +707,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     } else {
       const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
       if (__builtin_amdgcn_ballot_w64(bad) == 0) {
-        if (lpb - lpa >= 8) {
-          if constexpr (A >= 4) with_na(run_fast_ahead_vt);
-          else with_na(run_fast_ahead);
-        }
+        if constexpr (A >= 4) with_na(run_fast_ahead_vt);
+        else if (lpb - lpa >= 8) with_na(run_fast_ahead);
         else with_na(run_fast);
       }
       else with_na(run_general);
@@ -722,27 +724,31 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const int per = 8 / n_sub, t0 = si * per;  // this wave's accumulator tiles
   if (n_sub > 1) {  // uniform over the workgroup
     __syncthreads();  // LDS is reused for the merge
-    float* mb = reinterpret_cast<float*>(lds) + (w * 64 + lane) * kMergeFloats;
-    mb[0] = m_run;
-    mb[1] = l_run;
-    for (int t = 0; t < 8; ++t)
-      for (int i = 0; i < 4; ++i) mb[4 + 4 * t + i] = acc[t][i];
-    for (int i = 0; i < 4; ++i) mb[36 + i] = accr[i];
+    // [vector][wave][lane] of float4: (m, l, -, -), acc[0..7], acc_r -- each wave's row of a
+    // vector is 1 KiB of consecutive lanes (no bank conflicts)
+    float4* mb = reinterpret_cast<float4*>(lds);
+    auto mslot = [&](int v, int wv) { return (v * kWaves + wv) * 64 + lane; };
+    mb[mslot(0, w)] = make_float4(m_run, l_run, 0.f, 0.f);
+    for (int t = 0; t < 8; ++t) mb[mslot(1 + t, w)] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    mb[mslot(9, w)] = make_float4(accr[0], accr[1], accr[2], accr[3]);
     __syncthreads();
     if (!active) return;
-    const float* ob[kWaves];
+    int ow[kWaves];
+    float om[kWaves], ol[kWaves];
     float M = -INFINITY;
 #pragma unroll
     for (int o = 0; o < kWaves; ++o) {
-      const int oo = o < n_sub ? o : 0;  // (partners past n_sub are never read)
-      ob[o] = reinterpret_cast<float*>(lds) + ((gi + oo * n_groups) * 64 + lane) * kMergeFloats;
-      if (o < n_sub) M = fmaxf(M, ob[o][0]);
+      ow[o] = gi + (o < n_sub ? o : 0) * n_groups;  // (partners past n_sub are never read)
+      const float4 ml = mb[mslot(0, ow[o])];
+      om[o] = ml.x;
+      ol[o] = ml.y;
+      if (o < n_sub) M = fmaxf(M, om[o]);
     }
     float wo[kWaves], L = 0.f;
 #pragma unroll
     for (int o = 0; o < kWaves; ++o) {
-      wo[o] = (o < n_sub && M != -INFINITY) ? exp2f(ob[o][0] - M) : 0.f;
-      if (o < n_sub) L += wo[o] * ob[o][1];
+      wo[o] = (o < n_sub && M != -INFINITY) ? exp2f(om[o] - M) : 0.f;
+      if (o < n_sub) L += wo[o] * ol[o];
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -750,16 +756,26 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       f4 v = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int o = 0; o < kWaves; ++o)
-        if (o < n_sub)
-          for (int i = 0; i < 4; ++i) v[i] += wo[o] * ob[o][4 + 4 * t + i];
+        if (o < n_sub) {
+          const float4 x = mb[mslot(1 + t, ow[o])];
+          v[0] += wo[o] * x.x;
+          v[1] += wo[o] * x.y;
+          v[2] += wo[o] * x.z;
+          v[3] += wo[o] * x.w;
+        }
       acc[t] = v;
     }
     if (si == 0) {
       f4 v = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int o = 0; o < kWaves; ++o)
-        if (o < n_sub)
-          for (int i = 0; i < 4; ++i) v[i] += wo[o] * ob[o][36 + i];
+        if (o < n_sub) {
+          const float4 x = mb[mslot(9, ow[o])];
+          v[0] += wo[o] * x.x;
+          v[1] += wo[o] * x.y;
+          v[2] += wo[o] * x.z;
+          v[3] += wo[o] * x.w;
+        }
       accr = v;
     }
     m_run = M;
