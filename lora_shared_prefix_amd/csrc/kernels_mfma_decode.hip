@@ -368,7 +368,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
           k2.p[2 * k + q2] = mul_add2(y, c, x, sn);
         }
       }
-      if (half == 0) sj = f4{0.f, 0.f, 0.f, 0.f};
+      if (half == 0) sj = sb;  // each agent's residual score accumulates onto the base score
       sj = mfma32h(k0.v, qhr[half].v, sj);
       sj = mfma32h(k2.v, qhr[half + 2].v, sj);
       if (half == 1) ssel = (j == 0 || jc == j) ? sj : ssel;
@@ -391,7 +391,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       }
     }
     load_rk(lp_next, B, na_c);  // likewise the residual key rows, after the last reconstruction
-    return ssel + sb;
+    return ssel;
   };
 
   // Rows of page lp held by the group's agents (the page's start is common to them all):
