@@ -112,7 +112,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   const size_t tile = size_t(kPage) * kD;  // elements per (page, plane, head) tile
 
   // ---- this wave's agents and query columns ------------------------------------------------
-  int agent[A], slot[A], rlen[A];  // wave-uniform
+  int agent[A], slot[A];  // wave-uniform
 #pragma unroll
   for (int j = 0; j < A; ++j) {
     int av = ia[0], sv = is[0];
@@ -125,7 +125,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     const bool ok = active && j < na_g;
     agent[j] = ok ? av : 0;
     slot[j] = ok ? sv : 0;
-    rlen[j] = ok ? p.plan[p.off_lens + agent[j]] : 0;
+
   }
   const int jc = col / G;                   // agent (within group) of this lane's column
   const bool col_ok = active && col < na_g * G;
@@ -158,19 +158,6 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
       if (vr[j] >= p.num_rpages) vr[j] = -1;
     }
   }
-  // With the slot map, lane i also holds page lpa + i's start and the position its rows end
-  // at, from the first agent's start table: a base page that several agents map holds the
-  // same rows for each of them (a shared page is full or a frozen tail), so only an agent's
-  // own length can cut it shorter.
-  int vst = 0, vend = 0;
-  if constexpr (kMap) {
-    const int lpi = id_base + lane;
-    const bool in = lpa < lpb && lpi < lpb;
-    const int32_t* row = p.pstart + size_t(agent[0]) * p.max_pages;
-    vst = in ? row[lpi] : 0;
-    const int nx = (in && lpi + 1 < p.max_pages) ? row[lpi + 1] : -1;
-    vend = nx >= 0 ? nx : rlen[0];
-  }
   // B_k,a[:, h*d:(h+1)*d] goes to LDS in MFMA A-operand order without a staging pass: a
   // work unit (agent jj, rank group g, dims 8pc .. 8pc+7) loads the four rank rows 4g .. 4g+3
   // of its eight dims (16 contiguous bytes each, coalesced over pc) and later packs, per
@@ -191,6 +178,32 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     for (int r = 0; r < 4; ++r)
       bkr[i][r] = *reinterpret_cast<const uint4*>(Bk + (size_t(a) * kR + 4 * g + r) * n + h * kD +
                                                   8 * pc);
+  }
+  // The agents' lengths (an agent's last page's valid rows): lane j holds group agent j's
+  // (0 for unused slots), loaded after every vector load above and read (readlane) only where
+  // needed -- the last page of the sub-range -- so no earlier step waits for it.
+  int vlen = 0;
+  {
+    int aj = agent[0];
+#pragma unroll
+    for (int j = 1; j < A; ++j)
+      if (lane == j) aj = agent[j];
+    const int l = p.plan[p.off_lens + aj];
+    vlen = l & -int(active && lane < na_g);  // (a mask, not a branch around the load)
+  }
+  auto rlen_of = [&](int j) { return __builtin_amdgcn_readlane(vlen, j); };
+  // With the slot map, lane i also holds page lpa + i's start and the position its rows end
+  // at, from the first agent's start table: a base page that several agents map holds the
+  // same rows for each of them (a shared page is full or a frozen tail), so only an agent's
+  // own length can cut it shorter.
+  int vst = 0, vend = 0;
+  if constexpr (kMap) {
+    const int lpi = id_base + lane;
+    const bool in = lpa < lpb && lpi < lpb;
+    const int32_t* row = p.pstart + size_t(agent[0]) * p.max_pages;
+    vst = in ? row[lpi] : 0;
+    const int nx = (in && lpi + 1 < p.max_pages) ? row[lpi + 1] : -1;
+    vend = nx >= 0 ? nx : rlen_of(0);
   }
   const float qscale = p.sm_scale_log2;
 
@@ -410,8 +423,8 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     int prow[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-      prow[j] = kMap ? min(min(rlen[j], pend) - pos0, kPage)
-                     : page_rows(nullptr, p.max_pages, agent[j], lp, rlen[j]);
+      prow[j] = kMap ? min(min(rlen_of(j), pend) - pos0, kPage)
+                     : page_rows(nullptr, p.max_pages, agent[j], lp, rlen_of(j));
       R.vrows = max(R.vrows, prow[j]);
       R.minrows = min(R.minrows, prow[j]);
     }
@@ -507,13 +520,22 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   if (p.k_new != nullptr) {  // uniform over the grid
     uint16_t* const bw = const_cast<uint16_t*>(bcache);
     uint16_t* const rw = const_cast<uint16_t*>(rcache);
+    // every item agent's last page and length in one round trip: lane j loads item agent
+    // j's (lanes past the item's agents its first agent's, not used)
+    int aj = ia[0];
+#pragma unroll
+    for (int k = 1; k < kItemAgents; ++k)
+      if (lane == k && k < na) aj = ia[k];
+    const int vlast = p.plan[p.off_lastpage + aj];
+    const int vlen_n = p.plan[p.off_lens + aj];
 #pragma unroll
     for (int j = 0; j < kItemAgents; ++j) {
       if (j >= na) continue;  // uniform
       const int a = ia[j];
-      const int lp_last = p.plan[p.off_lastpage + a];
+      const int lp_last = __builtin_amdgcn_readlane(vlast, j);
       if (lp_last < lp0 || lp_last >= lp0 + np) continue;  // uniform
-      const int row = p.plan[p.off_lens + a] - 1 - page_start(p.pstart, p.max_pages, a, lp_last);
+      const int row = __builtin_amdgcn_readlane(vlen_n, j) - 1 -
+                      page_start(p.pstart, p.max_pages, a, lp_last);
       // (a row past the page: the caller did not rebuild the plan after a page crossing)
       if (row < 0 || row >= kPage) continue;
       const int bpg = p.btab[size_t(a) * p.max_pages + lp_last];
