@@ -724,16 +724,26 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
   };
   if (lpa < lpb) {
+    const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
+    bool general = __builtin_amdgcn_ballot_w64(bad) != 0;
     if constexpr (kMap) {
-      with_na(run_general);
+      // With the slot map a page before the sub-range's last one can hold fewer than 16 rows
+      // (a frozen tail): such a sub-range takes the general loop.  Otherwise every page but
+      // the last is full for every agent of the group and starts where the previous one
+      // ends, exactly as without the slot map, and the loops below apply (the angles
+      // re-anchor at the first page if its start is not a multiple of 16).
+      const bool short_mid = lane < lpb - lpa - 1 && vend - vst != kPage;
+      general = general || __builtin_amdgcn_ballot_w64(short_mid) != 0;
+      // (the two-agent instantiation keeps the general loop only: with the fast loops beside
+      // it, its registers spill)
+      if constexpr (A == 2) general = true;
+    }
+    if (!general) {
+      if constexpr (A >= 4) with_na(run_fast_ahead_vt);
+      else if (lpb - lpa >= 8) with_na(run_fast_ahead);
+      else with_na(run_fast);
     } else {
-      const bool bad = lane < lpb - lpa && vb < 0;  // a page id outside the pool
-      if (__builtin_amdgcn_ballot_w64(bad) == 0) {
-        if constexpr (A >= 4) with_na(run_fast_ahead_vt);
-        else if (lpb - lpa >= 8) with_na(run_fast_ahead);
-        else with_na(run_fast);
-      }
-      else with_na(run_general);
+      with_na(run_general);
     }
   }
 
