@@ -18,7 +18,8 @@ constexpr int kPage = 16;
 // One decode work item: a run of logical pages that every listed agent maps to the same
 // physical base pages, processed by one workgroup per KV head.
 //   [0] first logical page   [1] number of pages   [2] number of agents
-//   [3] reserved (0)
+//   [3] 1 if the item holds the last logical page of one of its agents (decode with append
+//       stores that agent's new row there), else 0
 //   [4 .. 4+kItemAgents) agent indices
 //   [4+kItemAgents .. 4+2*kItemAgents) partial slot of each agent; the slots of one agent
 //   are consecutive (slot_ptr[a] .. slot_ptr[a+1]), so the combine needs no slot list

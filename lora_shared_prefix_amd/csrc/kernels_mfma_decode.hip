@@ -69,10 +69,10 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     ia[k] = it[4 + k];
     is[k] = it[4 + kItemAgents + k];
   }
-  const int lp0 = it[0], np = it[1], na = it[2];
+  const int lp0 = it[0], np = it[1], na = it[2], holds_last = it[3];
   // (the empty statements take the record's values as operands, so that all of its loads are
   // issued before the test below -- one memory round trip -- rather than sunk past it)
-  asm volatile("" : : "s"(lp0), "s"(np), "s"(na));
+  asm volatile("" : : "s"(lp0), "s"(np), "s"(na), "s"(holds_last));
 #pragma unroll
   for (int k = 0; k < kItemAgents; ++k) asm volatile("" : : "s"(ia[k]), "s"(is[k]));
   if (na <= 0) return;  // past the live count
@@ -517,7 +517,7 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
   // in a page private to its agent.  The token sits at position length - 1 (the length on
   // the device, which the previous call advanced), in the agent's last page.
   static_assert(kThreads == 2 * kD, "one thread per key and per value element of a row");
-  if (p.k_new != nullptr) {  // uniform over the grid
+  if (p.k_new != nullptr && holds_last != 0) {  // uniform over the workgroup
     uint16_t* const bw = const_cast<uint16_t*>(bcache);
     uint16_t* const rw = const_cast<uint16_t*>(rcache);
     // every item agent's last page and length in one round trip: lane j loads item agent

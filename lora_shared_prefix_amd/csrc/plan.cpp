@@ -257,11 +257,12 @@ int build(const forkkv_pool* p, const forkkv_seq* seqs, int32_t n, int32_t num_q
         it[0] = lp;
         it[1] = npg;
         it[2] = na;
-        it[3] = 0;  // reserved
+        it[3] = 0;  // set below when the item holds an agent's last page
         for (int32_t j = 0; j < na; ++j) {
           const int32_t a = r.agents[a0 + j];
           it[4 + j] = a;
           it[4 + kItemAgents + j] = per_agent[a]++;  // index within the agent, for now
+          if (np[a] - 1 >= lp && np[a] - 1 < lp + npg) it[3] = 1;
         }
         n_slots += na;
         items.insert(items.end(), it, it + kItemInts);

@@ -194,11 +194,13 @@ def _check_plan(lp: fk.Pool, pm_tables, handles, plan: fk.Plan, group_cap):
         assert len(items_of[page]) == -(-len(hs_) // cap), (page, len(hs_), cap)
     # decode with append: the last-page section holds each agent's last logical page (the
     # kernels store the new token there, at row length - 1 - page start); word 3 of an item
-    # is reserved
+    # flags the items that hold one of their agents' last pages (only those store)
     off_last = blob[12]
     for i in range(n_items):
         it = blob[off_items + i * ITEM_INTS: off_items + (i + 1) * ITEM_INTS]
-        assert it[3] == 0
+        lp0, npg, na = it[:3]
+        holds = any(lp0 <= -(-lens[a] // 16) - 1 < lp0 + npg for a in it[4:4 + na] if lens[a] > 0)
+        assert it[3] == int(holds), (i, it[:4])
     for a in range(n_agents):
         assert blob[off_last + a] == (-(-lens[a] // 16) - 1 if lens[a] > 0 else -1)
     # capacities: the items section has room for item_capacity items, zero past n_items
