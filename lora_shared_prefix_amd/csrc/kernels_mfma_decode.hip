@@ -701,15 +701,25 @@ decode_mfma_kernel(DecodeParams p, int n_items) {
     // read the buffer, a whole page before their own use; no memory read may be scheduled
     // above those products (a read hoisted there would need a second buffer and a register
     // copy at the loop's end, which waits for every load issued in the page)
+    // Wave priority falls by one level per quarter of the sub-range done: of the two waves
+    // that share a SIMD (one from each workgroup on the compute unit), the one further behind
+    // is issued first, instead of the older workgroup's running ahead and leaving the other's
+    // to finish alone.
+    __builtin_amdgcn_s_setprio(3);
     for (int lp = lpa; lp + 1 < lpb; ++lp) {
       const f4 s = scores(B, v, lp + 1, na_c, std::integral_constant<int, 1>{});
       trig_for(lp + 1);
       softmax_acc(s, v, na_c, Full{}, Rows{});
       __builtin_amdgcn_sched_barrier(0x078F);
       load_vt(B, v.vt);
+      const int done4 = 4 * (lp + 1 - lpa), tot = lpb - lpa;
+      if (done4 >= 3 * tot) __builtin_amdgcn_s_setprio(0);
+      else if (done4 >= 2 * tot) __builtin_amdgcn_s_setprio(1);
+      else if (done4 >= tot) __builtin_amdgcn_s_setprio(2);
     }
     const f4 s = scores(B, v, lpb - 1, na_c, std::integral_constant<int, 1>{});
     softmax_acc(s, v, na_c, Masked{}, page_rows_of(lpb - 1, na_c));
+    __builtin_amdgcn_s_setprio(0);
   };
   auto run_fast = [&](auto na_c) __attribute__((always_inline)) {
     KBuf B = first;

@@ -21,8 +21,8 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfRowsPerWave * kPfWaves;  // rows per workgroup
 
-// cos and sin (fp64) of a moderate angle (here at most 2 pi, or 32 for the per-iteration
-// step): a reduction by a small number q of quarter turns leaves t = x - q pi/2 in
+// cos and sin (fp64) of a moderate angle (here reduced to at most 2 pi before the call):
+// a reduction by a small number q of quarter turns leaves t = x - q pi/2 in
 // [-pi/4, pi/4] (pi/2 in two parts, a fused step each, so t is exact to rounding), where the
 // Taylor series of sin t through t^15 and of cos t through t^16 are exact to below 1e-16.
 // Far lighter in registers than the general library routine, which must also reduce huge
@@ -69,6 +69,11 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   __shared__ int s_miss[2][2];                          // [buf][page]: base page missing
   __shared__ int s_pos[2][2], s_vrows[2][2];            // [buf][page]: start, valid rows
   __shared__ double s_om[kD / 2];                        // RoPE frequencies w_j (fp64)
+  // the ones operand of the denominator product, read from here at each use: held in
+  // registers it would be rebuilt by copies wherever its registers serve as temporaries
+  __shared__ __align__(16) uint4 s_ones;
+  // cos and sin of k * 32 w_j (k < 32: the iterations since the last exact anchor)
+  __shared__ __align__(16) float s_ct[32][kD / 2], s_st[32][kD / 2];
   const int Hkv = p.num_kv_heads, G = p.group, Hq = p.num_q_heads, C = p.chunk_len;
   // the workgroups of one KV head share an XCD (block ids are dealt round robin over the
   // 8 XCDs), so the shared prefix of that head streams through one L2
@@ -125,31 +130,39 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     v.u.y = uint32_t(src[size_t(4 * g4 + 2) * n]) | (uint32_t(src[size_t(4 * g4 + 3) * n]) << 16);
     bkop[u] = v.s;
   }
-  // RoPE of this lane's 4 frequencies j_i = perm_dim(tp, 4 g4 + i) at position
-  // t = 16 (2 it + pg) + col: exact (fp64-reduced) every 32 iterations, a rotation by
-  // 32 w_j per iteration in between.
+  // RoPE of this lane's 4 frequencies j_i = perm_dim(tp, 4 g4 + i) = f0 + i at position
+  // t = 16 (2 it + pg) + col: exact (fp64-reduced) at an anchor every 32 iterations, and in
+  // between the anchor's angle plus k steps of 32 w_j (one angle addition with the table
+  // entry k, so no error accumulates between anchors).
   if (tid < kD / 2)
     s_om[tid] = exp2(-2.0 * tid / kD * log2(static_cast<double>(p.rope_theta)));
+  if (tid == 0) s_ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
   __syncthreads();
-  float stc[4], sts[4];
-  for (int i = 0; i < 4; ++i) {
+  for (int x = tid; x < 32 * (kD / 2); x += kPfThreads) {
+    const int k = x / (kD / 2), j = x % (kD / 2);
+    double ang = static_cast<double>(2 * kPage * k) * s_om[j];
+    ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
     double sv, cv;
-    sincos_turn(2 * kPage * s_om[perm_dim(tp, 4 * g4 + i)], sv, cv);  // 32 w_j <= 32
-    stc[i] = static_cast<float>(cv);
-    sts[i] = static_cast<float>(sv);
+    sincos_turn(ang, sv, cv);
+    s_ct[k][j] = static_cast<float>(cv);
+    s_st[k][j] = static_cast<float>(sv);
   }
-  float rc[4], rs[4];
-  int next_base = pg * kPage;  // the page start the recurrence stands at
+  __syncthreads();
+  const int f0 = perm_dim(tp, 4 * g4);
+  float rc[4], rs[4];  // the anchor's cos and sin, times the adapter scale s
+  int kk = 0;          // iterations since the anchor (wave-uniform, < 32)
+  int next_base = pg * kPage;  // the page start the angles stand at
   // exact cos/sin (fp64-reduced angle) of this lane's key position base + col
   auto anchor_at = [&](int base) {
     for (int i = 0; i < 4; ++i) {
-      double ang = static_cast<double>(base + col) * s_om[perm_dim(tp, 4 * g4 + i)];
+      double ang = static_cast<double>(base + col) * s_om[f0 + i];
       ang = fma(-kTwoPi, floor(ang * kInvTwoPi), ang);
       double sv, cv;
       sincos_turn(ang, sv, cv);
       rc[i] = static_cast<float>(cv) * p.lora_scale;
       rs[i] = static_cast<float>(sv) * p.lora_scale;
     }
+    kk = 0;
   };
 
   // global pieces of this wave's staging role, held in registers one iteration ahead
@@ -208,16 +221,17 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
   // softmax denominators: a matrix product of the bf16 probabilities with a ones operand,
   // so every lane of a row holds that row's sum (the same rounded weights as acc)
   f4 l_acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-  bf8 ones;
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
   // m_run + 8 (the rescale threshold) and the reference the exponents are taken against
-  // (-1e30 while a row has no key yet: no -inf - -inf), both updated only on a rescale
+  // (-1e30 while a row has no key yet: no -inf - -inf), both updated only on a rescale;
+  // m_raw is the threshold in raw-score units (m_thr / qscale, qscale > 0), so that a
+  // page's test costs no multiplication
   float m_thr[2] = {-INFINITY, -INFINITY}, m_ref[2] = {-1e30f, -1e30f};
+  float m_raw[2] = {-INFINITY, -INFINITY};
   for (int rt = 0; rt < 2; ++rt) {
     for (int t = 0; t < 8; ++t) acc[rt][t] = f4{0.f, 0.f, 0.f, 0.f};
     accr[rt] = f4{0.f, 0.f, 0.f, 0.f};
   }
-  const float qscale = p.sm_scale_log2;
+  const float qscale = p.sm_scale_log2, inv_qscale = 1.f / qscale;
   auto m2 = [](int tv, uint32_t& lo, uint32_t& hi) {
     if (tv < 4) {
       if (tv <= 0) lo = 0;
@@ -236,6 +250,16 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
     const int base = kMap ? B.pos : lp * kPage;
     if (kMap && base != next_base) anchor_at(base);
     next_base = base + 2 * kPage;
+    // this iteration's cos and sin: the anchor's angle plus kk steps
+    const float4 ct = *reinterpret_cast<const float4*>(&s_ct[kk][f0]);
+    const float4 st = *reinterpret_cast<const float4*>(&s_st[kk][f0]);
+    ++kk;
+    const float tc[4] = {ct.x, ct.y, ct.z, ct.w}, ts[4] = {st.x, st.y, st.z, st.w};
+    float cc[4], ss[4];
+    for (int i = 0; i < 4; ++i) {
+      cc[i] = __builtin_fmaf(rc[i], tc[i], -rs[i] * ts[i]);
+      ss[i] = __builtin_fmaf(rs[i], tc[i], rc[i] * ts[i]);
+    }
     // rebuild this wave's two key tiles of page pg: K = bK + RoPE(s * rK B_k)
     U2 rk;
     rk.u = B.rk;
@@ -248,13 +272,8 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       const float b0 = __uint_as_float((i & 1) ? (bw0[i >> 1] & 0xffff0000u) : (bw0[i >> 1] << 16));
       const float b1 = __uint_as_float((i & 1) ? (bw1[i >> 1] & 0xffff0000u) : (bw1[i >> 1] << 16));
       // two fused steps each: bK + x c - y s and bK + y c + x s
-      k0[i] = __builtin_fmaf(x, rc[i], __builtin_fmaf(-y, rs[i], b0));
-      k1[i] = __builtin_fmaf(y, rc[i], __builtin_fmaf(x, rs[i], b1));
-    }
-    for (int i = 0; i < 4; ++i) {  // advance to the next iteration (two pages on)
-      const float c = rc[i] * stc[i] - rs[i] * sts[i];
-      rs[i] = rs[i] * stc[i] + rc[i] * sts[i];
-      rc[i] = c;
+      k0[i] = __builtin_fmaf(x, cc[i], __builtin_fmaf(-y, ss[i], b0));
+      k1[i] = __builtin_fmaf(y, cc[i], __builtin_fmaf(x, ss[i], b1));
     }
     // tile T = tp lands in chunk tp/2, half (tp & 1); tile tp + 4 in chunk tp/2 + 2
     uint2* sk = reinterpret_cast<uint2*>(&s_k[buf][pg][0]);
@@ -351,7 +370,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       // reduction is needed only then.
       float lmax = -INFINITY;
       for (int e = 0; e < 8; ++e) lmax = fmaxf(lmax, sc[e]);
-      if (__builtin_amdgcn_ballot_w64(lmax * qscale > m_thr[rt]) != 0) {
+      // (an m_raw rounded low only adds a rescale that changes nothing; rounded high it lets
+      // an exponent reach 8 plus a rounding error, inside the headroom)
+      if (__builtin_amdgcn_ballot_w64(lmax > m_raw[rt]) != 0) {
         const float pmax = max_over_rows(lmax) * qscale;
         const bool grow = pmax > m_thr[rt];
         const float m_new = grow ? pmax : m_run[rt];
@@ -361,6 +382,7 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
         accr[rt] *= alpha;
         m_run[rt] = m_new;
         m_thr[rt] = m_new + 8.f;
+        m_raw[rt] = m_thr[rt] * inv_qscale;
         m_ref[rt] = max2(m_new, -1e30f);
       }
       float pr[8];
@@ -376,7 +398,9 @@ prefill_mfma_kernel(PrefillParams p, int n_rblocks) {
       U4 rvop;
       rvop.u = s_rv[buf][lane];
       accr[rt] = mfma32(rvop.b, pb.b, accr[rt]);
-      l_acc[rt] = mfma32(ones, pb.b, l_acc[rt]);
+      U4 ones;
+      ones.u = s_ones;
+      l_acc[rt] = mfma32(ones.b, pb.b, l_acc[rt]);
     }
   };
 
